@@ -1,0 +1,301 @@
+"""fp64 reference for the MoE layer forward (test infrastructure only).
+
+Each function is the plain definition of one step, in the pages' order:
+router scores -> softmax -> top-k -> renormalise -> group assignments by expert
+(counts, offsets, stable permutation, inverse map) -> per-expert SwiGLU FFN ->
+combine (unpermute, weight, sum) [+ shared expert].
+
+Inputs are the canonical stored values (f32 / bf16 numbers, or E4M3 codes with
+fp32 block scales); they are upcast exactly to float64 and every step runs in
+float64. Nothing here is blocked, fused or reordered beyond what each
+definition states.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+try:  # torch is only used as a container for the canonical inputs
+    import torch
+except ImportError:  # pragma: no cover
+    torch = None
+
+
+# ----------------------------------------------------------------------------
+# Canonical values
+# ----------------------------------------------------------------------------
+
+def to_f64(x) -> np.ndarray:
+    """Exact float64 copy of a float tensor/array (f32 and bf16 embed exactly)."""
+    if torch is not None and isinstance(x, torch.Tensor):
+        if x.dtype == torch.uint8:
+            raise TypeError("uint8 tensors are fp8 codes: use dequant_blocks")
+        return x.detach().to("cpu").to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP E4M3 ("e4m3fn") code -> float64, from the format definition.
+
+    Bit layout s|eeee|mmm, exponent bias 7. Exponent field 0 encodes subnormals
+    m * 2^-9; exponent field 15 with mantissa 7 is NaN (no infinities); every
+    other code is (-1)^s * (1 + m/8) * 2^(e-7). Largest finite value 448.
+    FP8 storage of expert weights is the format the page "MoE-推理部署" names in
+    its expert-quantisation section.
+    """
+    if torch is not None and isinstance(codes, torch.Tensor):
+        codes = codes.detach().to("cpu").numpy()
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    sign = np.where(s == 1, -1.0, 1.0)
+    sub = m.astype(np.float64) * 2.0 ** -9
+    nor = (1.0 + m.astype(np.float64) / 8.0) * np.exp2((e - 7).astype(np.float64))
+    val = sign * np.where(e == 0, sub, nor)
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+def dequant_blocks(codes, scales, block: int = 128) -> np.ndarray:
+    """W[r, c] = decode(code[r, c]) * scale[r // block, c // block], in float64.
+
+    Every E4M3 value times an fp32 scale is exact in float64 (4 + 24 significand
+    bits), so this is the exact value of the stored weight. The scales are per
+    expert and per 128x128 block, the per-expert granularity the page
+    "MoE-推理部署" asks for in its expert-quantisation section.
+    """
+    q = e4m3_decode(codes)
+    s = to_f64(scales)
+    return q * np.repeat(np.repeat(s, block, axis=0), block, axis=1)
+
+
+# ----------------------------------------------------------------------------
+# Router: page "MoE serving production quirks", memory-paradox section (linear
+# projection and softmax over all experts); page "MOE推理流程解析" §三 (top-k
+# keeps the selected indices and their weights) and §九 (kept weights are
+# renormalised).
+# ----------------------------------------------------------------------------
+
+def router_logits(X, Wg, gate_bias=None) -> np.ndarray:
+    """logits[t, e] = sum_h X[t, h] * Wg[h, e] (+ b[e]), float64."""
+    logits = to_f64(X) @ to_f64(Wg)
+    if gate_bias is not None:
+        logits = logits + to_f64(gate_bias)[None, :]
+    return logits
+
+
+def softmax(logits) -> np.ndarray:
+    """Row softmax with the row maximum subtracted, float64."""
+    z = np.asarray(logits, dtype=np.float64)
+    z = z - z.max(axis=1, keepdims=True)
+    ez = np.exp(z)
+    return ez / ez.sum(axis=1, keepdims=True)
+
+
+def select_topk(logits, k: int) -> np.ndarray:
+    """Indices of the k largest scores per token, best first; a tie goes to the
+    lower expert index. Comparisons happen in the dtype of `logits` (pass the
+    fp32 logits of another implementation to take the same decision it took).
+    Softmax is monotone, so the k largest logits are the k largest
+    probabilities.
+    """
+    L = np.asarray(logits)
+    T, E = L.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    idx = np.empty((T, k), dtype=np.int64)
+    experts = np.arange(E)
+    for t in range(T):
+        # primary key: score, descending; secondary key: expert index, ascending
+        order = np.lexsort((experts, -L[t].astype(np.float64)))
+        idx[t] = order[:k]
+    return idx
+
+
+def routing_weights(logits, idx) -> np.ndarray:
+    """w[t, j] = p[t, idx[t, j]] / sum_j' p[t, idx[t, j']] with p = softmax over
+    all E experts (float64)."""
+    p = softmax(logits)
+    sel = np.take_along_axis(p, np.asarray(idx), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def route(X, Wg, gate_bias, k: int):
+    """Returns (logits [T,E], idx [T,k], w [T,k]) in float64 / int64."""
+    logits = router_logits(X, Wg, gate_bias)
+    idx = select_topk(logits, k)
+    return logits, idx, routing_weights(logits, idx)
+
+
+# ----------------------------------------------------------------------------
+# Dispatch on one GPU: page "MOE推理流程解析" §二 (T*k assignments grouped into
+# per-expert matrices; the token id stays beside each row) and §三 (the
+# permutation writes rows in expert order and records an inverse map).
+# ----------------------------------------------------------------------------
+
+def permute(idx, E: int):
+    """Group the T*k assignments a = t*k + j by expert.
+
+    counts[e]     = number of assignments with expert e
+    offsets[e]    = sum of counts[:e]  (offsets[E] = T*k)
+    row_src[r]    = assignment held by row r; rows of expert e are
+                    offsets[e] .. offsets[e+1]-1, in ascending assignment order
+    assign_row[a] = row holding assignment a (inverse of row_src)
+    """
+    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
+    A = flat.size
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    row_src = np.argsort(flat, kind="stable").astype(np.int64)
+    assign_row = np.empty(A, dtype=np.int64)
+    assign_row[row_src] = np.arange(A)
+    return counts, offsets, row_src, assign_row
+
+
+# ----------------------------------------------------------------------------
+# Expert FFN: page "MOE推理流程解析" §三 (each expert applies its activation and
+# output projection). SwiGLU form: h = silu(x W1) * (x W3), y = h W2.
+# ----------------------------------------------------------------------------
+
+def silu(z):
+    """silu(z) = z / (1 + exp(-z)) (float64)."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(x, W1, W3, W2) -> np.ndarray:
+    """y = (silu(x @ W1) * (x @ W3)) @ W2 for rows x [n, H]."""
+    x = np.asarray(x, dtype=np.float64)
+    return (silu(x @ W1) * (x @ W3)) @ W2
+
+
+def grouped_ffn(Xrows, offsets, expert) -> np.ndarray:
+    """Yp[r] = FFN_e(Xrows[r]) for the rows r of each group e.
+
+    `expert(e)` returns (W1, W3, W2) as float64 arrays. Groups with no rows are
+    skipped (their weights are never touched).
+    """
+    Xrows = np.asarray(Xrows, dtype=np.float64)
+    offsets = np.asarray(offsets)
+    G = offsets.size - 1
+    Yp = None
+    for e in range(G):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi <= lo:
+            continue
+        W1, W3, W2 = expert(e)
+        y = swiglu_ffn(Xrows[lo:hi], W1, W3, W2)
+        if Yp is None:
+            Yp = np.zeros((Xrows.shape[0], y.shape[1]), dtype=np.float64)
+        Yp[lo:hi] = y
+    if Yp is None:
+        Yp = np.zeros((Xrows.shape[0], 0), dtype=np.float64)
+    return Yp
+
+
+# ----------------------------------------------------------------------------
+# Combine: page "MOE推理流程解析" §二 (each contribution times its routing
+# weight, summed per token) and §三 (the inverse map restores token order).
+# ----------------------------------------------------------------------------
+
+def combine(Yp, assign_row, w, T: int, k: int, S=None) -> np.ndarray:
+    """Y[t] = sum_{j<k} w[t,j] * Yp[assign_row[t*k+j]] (+ S[t]), j ascending."""
+    Yp = np.asarray(Yp, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64).reshape(T, k)
+    assign_row = np.asarray(assign_row).reshape(T, k)
+    Y = np.zeros((T, Yp.shape[1]), dtype=np.float64)
+    for j in range(k):
+        Y += w[:, j:j + 1] * Yp[assign_row[:, j]]
+    if S is not None:
+        Y = Y + np.asarray(S, dtype=np.float64)
+    return Y
+
+
+# ----------------------------------------------------------------------------
+# Whole layer
+# ----------------------------------------------------------------------------
+
+class Layer:
+    """Read-only view of one layer's canonical inputs, upcast on demand.
+
+    `d` holds torch tensors (any device) or numpy arrays under the keys X, Wg,
+    gate_bias, W1, W3, W2, S1, S3, S2 (scales only for fp8 codes) and,
+    optionally, the shared expert Ws1, Ws3, Ws2, Ss1, Ss3, Ss2. Experts are
+    converted one at a time so model-sized weights never sit in RAM as float64
+    all at once.
+    """
+
+    def __init__(self, d: dict, k: int):
+        self.d = d
+        self.k = int(k)
+        self.E = int(d["W1"].shape[0])
+        self.T, self.H = (int(s) for s in d["X"].shape)
+
+    def X(self):
+        return to_f64(self.d["X"])
+
+    def Wg(self):
+        return to_f64(self.d["Wg"])
+
+    def gate_bias(self):
+        b = self.d.get("gate_bias")
+        return None if b is None else to_f64(b)
+
+    def _mat(self, wkey, skey, e=None):
+        W = self.d[wkey] if e is None else self.d[wkey][e]
+        S = self.d.get(skey)
+        if S is not None:
+            return dequant_blocks(W, S if e is None else S[e])
+        return to_f64(W)
+
+    def expert(self, e: int):
+        return (self._mat("W1", "S1", e), self._mat("W3", "S3", e), self._mat("W2", "S2", e))
+
+    def has_shared(self) -> bool:
+        return self.d.get("Ws1") is not None
+
+    def shared(self):
+        return (self._mat("Ws1", "Ss1"), self._mat("Ws3", "Ss3"), self._mat("Ws2", "Ss2"))
+
+
+def forward(layer: Layer) -> dict:
+    """Full fp64 forward. Returns every intermediate of the pages' pipeline."""
+    X = layer.X()
+    T, k, E = layer.T, layer.k, layer.E
+    logits, idx, w = route(X, layer.Wg(), layer.gate_bias(), k)
+    counts, offsets, row_src, assign_row = permute(idx, E)
+    Xp = X[row_src // k]
+    Yp = grouped_ffn(Xp, offsets, layer.expert)
+    S = swiglu_ffn(X, *layer.shared()) if layer.has_shared() else None
+    Y = combine(Yp, assign_row, w, T, k, S)
+    return dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets,
+                row_src=row_src, assign_row=assign_row, Xp=Xp, Yp=Yp, S=S, Y=Y)
+
+
+def forward_tokens(layer: Layer, tokens, idx=None) -> dict:
+    """fp64 outputs for a subset of tokens only (the layer is per-token
+    independent: each token's output depends on its own row, its own routing
+    and the shared weights). `idx` optionally fixes the routing decision
+    (rows for the sampled tokens) instead of re-deriving it.
+    Returns logits, idx, w, per-token expert outputs y[t, j] and Y for the
+    sampled tokens, in the given order.
+    """
+    tokens = np.asarray(tokens, dtype=np.int64)
+    X = layer.X()[tokens]
+    logits = router_logits(X, layer.Wg(), layer.gate_bias())
+    if idx is None:
+        idx = select_topk(logits, layer.k)
+    idx = np.asarray(idx, dtype=np.int64).reshape(len(tokens), layer.k)
+    w = routing_weights(logits, idx)
+    n = len(tokens)
+    y = np.zeros((n, layer.k, layer.H), dtype=np.float64)
+    for e in np.unique(idx):
+        W1, W3, W2 = layer.expert(int(e))
+        ts, js = np.nonzero(idx == e)
+        y[ts, js] = swiglu_ffn(X[ts], W1, W3, W2)
+    Y = np.einsum("tj,tjh->th", w, y)
+    S = None
+    if layer.has_shared():
+        S = swiglu_ffn(X, *layer.shared())
+        Y = Y + S
+    return dict(tokens=tokens, logits=logits, idx=idx, w=w, y=y, S=S, Y=Y)

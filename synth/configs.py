@@ -1,0 +1,74 @@
+"""Layer shapes for the synthetic workloads.
+
+Names follow the pages' notation: T tokens, H hidden size, F per-expert FFN
+width, E routed experts, k experts chosen per token, Fs the width of the
+always-on shared expert (0 = none).
+
+Model shapes: Mixtral-8x7B (E=8, top-2), Qwen3-30B-A3B (E=128, top-8) and
+DeepSeek-V3 (E=256 routed + 1 shared, top-8), stated on the pages
+"MOE推理流程解析" (section 一, model card figures) and the ai-master page's
+expert-parallel paragraph; H and F are the published layer widths of those
+models.
+"""
+from dataclasses import dataclass, field, replace
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    T: int
+    H: int
+    F: int
+    E: int
+    k: int
+    Fs: int = 0            # shared-expert width; 0 = no shared expert
+    act: str = "bf16"      # activation / gate dtype: "f32" or "bf16"
+    w: str = "bf16"        # expert weight dtype: "f32", "bf16" or "fp8"
+    zipf_s: float = 0.0    # > 0: gate bias b[e] = -s*ln(e+1) (hot low experts)
+    x_std: float = 1.0
+    w_std: float = 0.02
+    seed: int = 0
+
+    @property
+    def A(self) -> int:
+        """Number of (token, expert) assignments, T*k."""
+        return self.T * self.k
+
+    def with_(self, **kw) -> "LayerConfig":
+        return replace(self, **kw)
+
+
+# Full-size workloads (one MoE layer each).
+CONFIGS = {
+    c.name: c for c in [
+        LayerConfig("toy_fp32", T=64, H=128, F=256, E=8, k=2, act="f32", w="f32"),
+        LayerConfig("mixtral_decode", T=16, H=4096, F=14336, E=8, k=2),
+        LayerConfig("mixtral_prefill", T=4096, H=4096, F=14336, E=8, k=2, zipf_s=1.1),
+        LayerConfig("qwen3_decode", T=32, H=2048, F=768, E=128, k=8),
+        LayerConfig("qwen3_prefill", T=8192, H=2048, F=768, E=128, k=8),
+        LayerConfig("dsv3_decode", T=64, H=7168, F=2048, E=256, k=8, Fs=2048, w="fp8"),
+        LayerConfig("dsv3_prefill", T=4096, H=7168, F=2048, E=256, k=8, Fs=2048, w="fp8"),
+    ]
+}
+
+# Reduced shapes with the same dtypes and routing structure, small enough for
+# the oracle to compute every output in seconds, with ragged tails (T, F and H
+# not multiples of the kernels' tiles where the format allows it).
+MINI_CONFIGS = {
+    c.name: c for c in [
+        LayerConfig("mini_f32", T=37, H=96, F=160, E=5, k=2, act="f32", w="f32", seed=1),
+        LayerConfig("mini_bf16_decode", T=13, H=512, F=640, E=8, k=2, seed=2),
+        LayerConfig("mini_bf16_prefill", T=700, H=512, F=384, E=8, k=2, zipf_s=1.1, seed=3),
+        LayerConfig("mini_bf16_wide", T=300, H=256, F=192, E=64, k=8, seed=4),
+        LayerConfig("mini_fp8_decode", T=20, H=384, F=256, E=16, k=4, Fs=256, w="fp8", seed=5),
+        LayerConfig("mini_fp8_prefill", T=520, H=512, F=384, E=16, k=4, Fs=384, w="fp8", seed=6),
+    ]
+}
+
+
+def get_config(name: str) -> LayerConfig:
+    if name in CONFIGS:
+        return CONFIGS[name]
+    if name in MINI_CONFIGS:
+        return MINI_CONFIGS[name]
+    raise KeyError(f"unknown layer config {name!r}")

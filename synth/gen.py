@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs for one MoE layer.
+
+Every tensor has its own seeded torch generator, so any expert's weights can be
+drawn on its own and on the device that will hold them. The values are drawn
+once, in float32, and then stored in the layer's storage dtype; the stored
+values (bf16 numbers, or fp8 codes plus fp32 block scales) are the canonical
+inputs that both the HIP path and the oracle consume.
+
+Distributions: token rows X ~ N(0, x_std^2); gate and expert weights
+~ N(0, w_std^2) (standard deviation w_std). For the hot-expert workload the gate
+carries the bias b[e] = -s*ln(e+1), which adds log-Zipf(s) offsets to the
+expert scores (the Zipf normaliser is a constant shift and cancels in softmax).
+
+The fp8 storage format is OCP E4M3 ("e4m3fn": bias 7, largest finite 448, no
+infinities) with one fp32 scale per 128x128 block: s = amax/448 (1 when the
+block is all zero) and code = round-to-nearest-even(w/s), saturated to +-448.
+This is the storage format of the synthetic weights, not a step of the layer.
+"""
+from __future__ import annotations
+
+import hashlib
+
+import torch
+
+from .configs import LayerConfig
+
+_E4M3_MAX = 448.0
+_BLOCK = 128
+
+_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def tensor_seed(cfg: LayerConfig, name: str, *idx: int) -> int:
+    """Stable 63-bit seed for one tensor (or one expert of a tensor)."""
+    key = "/".join([str(cfg.seed), cfg.name, name] + [str(i) for i in idx])
+    digest = hashlib.blake2b(key.encode(), digest_size=8).digest()
+    return int.from_bytes(digest, "little") & ((1 << 63) - 1)
+
+
+def _normal(cfg: LayerConfig, name: str, shape, std: float, device, *idx: int) -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(tensor_seed(cfg, name, *idx))
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x
+
+
+def quantize_e4m3_blocks(w: torch.Tensor):
+    """Store a float32 matrix [R, C] as E4M3 codes with 128x128 fp32 scales.
+
+    Returns (codes uint8 [R, C], scales float32 [R/128, C/128]).
+    """
+    R, C = w.shape
+    if R % _BLOCK or C % _BLOCK:
+        raise ValueError(f"fp8 block storage needs dims divisible by {_BLOCK}, got {R}x{C}")
+    w = w.to(torch.float32)
+    blk = w.reshape(R // _BLOCK, _BLOCK, C // _BLOCK, _BLOCK)
+    amax = blk.abs().amax(dim=(1, 3))
+    scale = amax / _E4M3_MAX
+    scale = torch.where(amax == 0, torch.ones_like(scale), scale)
+    q = blk / scale[:, None, :, None]
+    q = q.clamp(-_E4M3_MAX, _E4M3_MAX)
+    codes = q.to(torch.float8_e4m3fn).view(torch.uint8).reshape(R, C)
+    return codes.contiguous(), scale.contiguous()
+
+
+def _store(w32: torch.Tensor, wdt: str):
+    """Cast a float32 weight matrix to its storage format."""
+    if wdt == "fp8":
+        return quantize_e4m3_blocks(w32)
+    return w32.to(_DTYPES[wdt]).contiguous(), None
+
+
+def _expert_stack(cfg: LayerConfig, name: str, n: int, rows: int, cols: int, device):
+    """[n, rows, cols] expert weights (+ [n, rows/128, cols/128] scales for fp8)."""
+    if cfg.w == "fp8":
+        W = torch.empty((n, rows, cols), dtype=torch.uint8, device=device)
+        S = torch.empty((n, rows // _BLOCK, cols // _BLOCK), dtype=torch.float32, device=device)
+    else:
+        W = torch.empty((n, rows, cols), dtype=_DTYPES[cfg.w], device=device)
+        S = None
+    for e in range(n):
+        w32 = _normal(cfg, name, (rows, cols), cfg.w_std, device, e)
+        q, s = _store(w32, cfg.w)
+        W[e].copy_(q)
+        if S is not None:
+            S[e].copy_(s)
+        del w32, q, s
+    return W, S
+
+
+def gate_bias(cfg: LayerConfig, device="cpu"):
+    """Log-Zipf(s) per-expert offsets, or None when the workload has none."""
+    if cfg.zipf_s <= 0:
+        return None
+    e = torch.arange(cfg.E, dtype=torch.float64)
+    return (-cfg.zipf_s * torch.log1p(e)).to(torch.float32).to(device)
+
+
+def make_layer(cfg: LayerConfig, device="cpu", experts: bool = True) -> dict:
+    """Draw one layer's inputs on `device`.
+
+    Keys: X [T,H]; Wg [H,E]; gate_bias [E] or None; W1, W3 [E,H,F]; W2 [E,F,H];
+    S1, S3 [E,H/128,F/128], S2 [E,F/128,H/128] (fp8 only, else None); and for a
+    shared expert Ws1, Ws3 [H,Fs], Ws2 [Fs,H] with Ss1, Ss3, Ss2.
+    With experts=False only X, Wg and gate_bias are drawn.
+    """
+    act = _DTYPES[cfg.act]
+    out = {"cfg": cfg}
+    out["X"] = _normal(cfg, "X", (cfg.T, cfg.H), cfg.x_std, device).to(act).contiguous()
+    out["Wg"] = _normal(cfg, "Wg", (cfg.H, cfg.E), cfg.w_std, device).to(act).contiguous()
+    out["gate_bias"] = gate_bias(cfg, device)
+    if not experts:
+        return out
+    out["W1"], out["S1"] = _expert_stack(cfg, "W1", cfg.E, cfg.H, cfg.F, device)
+    out["W3"], out["S3"] = _expert_stack(cfg, "W3", cfg.E, cfg.H, cfg.F, device)
+    out["W2"], out["S2"] = _expert_stack(cfg, "W2", cfg.E, cfg.F, cfg.H, device)
+    if cfg.Fs > 0:
+        for name, r, c in (("Ws1", cfg.H, cfg.Fs), ("Ws3", cfg.H, cfg.Fs), ("Ws2", cfg.Fs, cfg.H)):
+            w, s = _store(_normal(cfg, name, (r, c), cfg.w_std, device), cfg.w)
+            out[name] = w
+            out["S" + name[1:]] = s
+    else:
+        for name in ("Ws1", "Ws3", "Ws2", "Ss1", "Ss3", "Ss2"):
+            out[name] = None
+    return out
+
+
+def redraw_rows(cfg: LayerConfig, X: torch.Tensor, rows, attempt: int) -> None:
+    """Replace token rows of X in place with fresh draws from per-row substreams."""
+    for t in rows:
+        t = int(t)
+        x = _normal(cfg, "X-redraw", (cfg.H,), cfg.x_std, X.device, t, attempt)
+        X[t].copy_(x.to(X.dtype))
