@@ -1,0 +1,182 @@
+/*
+ * moe.h - C ABI of libmoe: the forward pass of one Mixture-of-Experts layer on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the page "MOE推理流程解析" (ffner.com) describes it:
+ *   section 三: the router scores every expert and top-k keeps the chosen
+ *     indices and their weights; a permutation writes token rows in expert
+ *     order and records an inverse map; the grouped expert computation runs
+ *     all experts' row blocks in one launch; experts apply their activation
+ *     and output projection; the inverse map restores token order and the
+ *     weighted contributions are summed per token.
+ *   section 二: T*k assignments, each (token row, expert, weight), grouped
+ *     into per-expert matrices; the token id stays beside each row.
+ *   section 一: an optional shared expert processes every token with weight 1.
+ *   section 九: the kept top-k weights are renormalised.
+ * The page "MoE serving production quirks" (tianpan.co, memory-paradox
+ * section) states the gate as a linear projection plus a softmax over all
+ * experts; the page "MoE-推理部署" (zzmblog.top, expert-quantisation section)
+ * asks for per-expert FP8 scales.
+ *
+ * Expert FFN form (SwiGLU): h = silu(x W1) * (x W3), y = h W2, with
+ * silu(z) = z / (1 + exp(-z)).
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless stated; all buffers are owned by the
+ *    caller, including workspaces. The library never allocates or frees device
+ *    memory and keeps no pointer after a call returns.
+ *  - Calls are asynchronous on `stream` (NULL = the null stream). There is no
+ *    device-to-host synchronisation inside any call, so every call can be
+ *    captured into a HIP graph. Inputs must stay valid until the work ends.
+ *  - Matrices are row-major and densely packed.
+ *  - Shapes and pointers are validated on the host before anything is
+ *    launched; on error nothing is enqueued and a status is returned.
+ *    T == 0 returns MOE_OK without launching. Launch failures return
+ *    MOE_ERR_HIP. No call throws.
+ *  - Routing order: the k slots of a token hold its experts best score first;
+ *    equal scores go to the lower expert index. Rows of an expert block are in
+ *    ascending assignment order a = t*k + j (so ascending token order).
+ *  - dtype combinations (activation, expert weights): (F32, F32), (BF16,
+ *    BF16), (BF16, FP8_E4M3). The gate matrix has the activation dtype.
+ *    FP8 weights are OCP E4M3 codes with one fp32 scale per 128x128 block,
+ *    so their dimensions must be multiples of 128. H and F must be multiples
+ *    of 32 (BF16/F32); E <= 1024; 1 <= k <= min(E, 64).
+ *  - Thread safety: no mutable global state; concurrent calls on different
+ *    streams with disjoint outputs and workspaces are safe.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,         /* null pointer, bad size, k > E, ... */
+    MOE_ERR_UNSUPPORTED = 2,         /* valid but not implemented: dtype pair, alignment */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes below the *_workspace_bytes() value */
+    MOE_ERR_HIP = 4                  /* a HIP launch failed */
+} moe_status;
+
+typedef enum {
+    MOE_F32 = 0,
+    MOE_BF16 = 1,
+    MOE_FP8_E4M3 = 2 /* OCP E4M3 ("e4m3fn"), 1 byte per value, weights only */
+} moe_dtype;
+
+/* Expert-FFN kernel choice. AUTO picks the row-streaming (batched GEMV) path
+ * when the average rows per expert is small (decode) and the LDS-tiled
+ * grouped GEMM otherwise (prefill). Both give results within the same
+ * tolerance of the exact layer; the forced values exist for testing. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_TILED = 2 } moe_ffn_path;
+
+/* Static string for a status code (host memory, never NULL). */
+const char *moe_status_string(moe_status s);
+
+/* ---------------------------------------------------------------------------
+ * Router: logits, softmax, top-k, renormalised weights.
+ *   logits[t,e] = sum_h X[t,h] * Wg[h,e] + gate_bias[e]   (fp32 accumulate)
+ *   topk_idx[t,:] = the k experts with the largest logits (softmax is
+ *     monotone), best first, ties to the lower index
+ *   topk_w[t,j]   = p[t,topk_idx[t,j]] / sum_j' p[t,topk_idx[t,j']], p the
+ *     softmax over all E logits; computed as the identical softmax over the
+ *     k kept logits, in fp32.
+ * X [T,H] and Wg [H,E] in x_dt (F32 or BF16); gate_bias [E] fp32 or NULL.
+ * Outputs: logits [T,E] fp32, topk_idx [T,k] int32, topk_w [T,k] fp32.
+ * NaN logits are never selected while a non-NaN logit is left.
+ * ------------------------------------------------------------------------- */
+moe_status moe_route(const void *X, moe_dtype x_dt, const void *Wg, const float *gate_bias,
+                     int T, int H, int E, int k,
+                     float *logits, int32_t *topk_idx, float *topk_w, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Dispatch on one GPU: group the A = T*k assignments by expert.
+ *   counts[e]     = #{a : topk_idx[a] == e}                  [E]
+ *   offsets[e]    = sum_{e' < e} counts[e'], offsets[E] = A  [E+1]
+ *   row_src[r]    = assignment a held by row r (stable: ascending a within
+ *                   each expert block)                        [A]
+ *   assign_row[a] = row r with row_src[r] == a (inverse map)  [A]
+ *   Xp[r, :]      = X[row_src[r] / k, :] if Xp != NULL        [A, H] (x_dt)
+ * topk_idx entries must lie in [0, E) (the kernel skips others, leaving their
+ * rows unset). Bit-exact and deterministic (no atomics decide any order).
+ * Workspace: moe_permute_workspace_bytes(T, k, E) bytes (device, any
+ * contents, 256-byte aligned).
+ * ------------------------------------------------------------------------- */
+size_t moe_permute_workspace_bytes(int T, int k, int E);
+moe_status moe_permute(const int32_t *topk_idx, int T, int k, int E,
+                       int32_t *counts, int32_t *offsets, int32_t *row_src, int32_t *assign_row,
+                       const void *X, moe_dtype x_dt, int H, void *Xp,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Grouped expert FFN over G row blocks (one per expert):
+ *   for each group g and row r in [offsets[g], offsets[g+1]):
+ *     x  = row r of the input (see below)
+ *     h  = silu(x W1[g]) * (x W3[g])
+ *     Yp[r, :] = h W2[g]
+ * Input rows: if row_src == NULL, Xin is [M, H] already permuted and row r is
+ * Xin[r]; otherwise Xin is the token matrix [T, H] and row r is
+ * Xin[row_src[r] / k] (the permutation is fused into the load).
+ * offsets [G+1] int32 on the device with offsets[0] = 0 and offsets[G] = M.
+ * W1, W3 [G, H, F]; W2 [G, F, H] in w_dt. For FP8 weights, S1, S3
+ * [G, H/128, F/128] and S2 [G, F/128, H/128] are fp32 block scales
+ * (weight = decode(code) * scale); they must be NULL otherwise.
+ * Yp [M, H] in act_dt. Accumulation is fp32; h is rounded to act_dt.
+ * Workspace: moe_grouped_ffn_workspace_bytes(...) bytes.
+ * ------------------------------------------------------------------------- */
+size_t moe_grouped_ffn_workspace_bytes(int M, int G, int H, int F, moe_dtype act_dt,
+                                       moe_dtype w_dt, moe_ffn_path path);
+moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M,
+                           const int32_t *offsets, int G, int H, int F,
+                           const void *W1, const void *W3, const void *W2, moe_dtype w_dt,
+                           const float *S1, const float *S3, const float *S2,
+                           moe_dtype act_dt, void *Yp, moe_ffn_path path,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Combine / unpermute:
+ *   Y[t, :] = sum_{j<k} topk_w[t,j] * Yp[assign_row[t*k+j], :]  (+ S[t, :])
+ * summed in fp32 in ascending j, then S added with weight 1, then rounded to
+ * act_dt. Yp [A, H], S [T, H] (or NULL), Y [T, H] in act_dt.
+ * ------------------------------------------------------------------------- */
+moe_status moe_combine(const void *Yp, const int32_t *assign_row, const float *topk_w,
+                       int T, int k, int H, const void *S, moe_dtype act_dt, void *Y,
+                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Whole layer: route -> permute -> grouped FFN (+ shared expert) -> combine.
+ * Weights are borrowed device pointers described by moe_layer_desc. The
+ * shared expert (Fs > 0) uses Ws1, Ws3 [H, Fs], Ws2 [Fs, H] (+ Ss* scales
+ * for FP8) and is added with weight 1. X [T, H] and Y [T, H] in act_dt.
+ * Optional outputs (NULL to skip): logits [T,E], topk_idx [T,k],
+ * topk_w [T,k], counts [E].
+ * Workspace: moe_forward_workspace_bytes(desc, T) bytes.
+ * ------------------------------------------------------------------------- */
+typedef struct moe_layer_desc {
+    int H, F, E, k, Fs;
+    moe_dtype act_dt, w_dt;
+    moe_ffn_path path;
+    const void *Wg;          /* [H, E], act_dt */
+    const float *gate_bias;  /* [E] or NULL */
+    const void *W1, *W3, *W2;
+    const float *S1, *S3, *S2;
+    const void *Ws1, *Ws3, *Ws2;
+    const float *Ss1, *Ss3, *Ss2;
+} moe_layer_desc;
+
+size_t moe_forward_workspace_bytes(const moe_layer_desc *desc, int T);
+moe_status moe_forward(const moe_layer_desc *desc, const void *X, int T, void *Y,
+                       void *ws, size_t ws_bytes, hipStream_t stream,
+                       float *logits_out, int32_t *topk_idx_out, float *topk_w_out,
+                       int32_t *counts_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,13 @@
+"""MoE layer forward on one AMD Instinct MI355X (gfx950).
+
+The layer: router (gate projection, softmax, top-k, renormalised weights) ->
+dispatch (per-expert counts, offsets, stable permutation, inverse map) ->
+grouped SwiGLU expert FFN (+ optional shared expert) -> combine. Every stage
+is a HIP kernel in libmoe.so (C ABI: include/moe.h); this package is its thin
+Python binding, with torch providing device memory and streams.
+"""
+from ._lib import (
+    LIB_PATH, MoEError, MoELayer, combine, grouped_ffn, lib, permute, route,
+)
+
+__all__ = ["LIB_PATH", "MoEError", "MoELayer", "combine", "grouped_ffn", "lib", "permute", "route"]

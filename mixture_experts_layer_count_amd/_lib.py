@@ -1,0 +1,241 @@
+"""ctypes binding of libmoe (include/moe.h).
+
+Argument marshalling only: torch tensors provide device memory and the HIP
+stream; every computation runs in libmoe's HIP kernels. The library must be
+built (python -m mixture_experts_layer_count_amd.build); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+PATHS = {"auto": 0, "gemv": 1, "tiled": 2}
+
+# Every function include/moe.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_route": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
+    "moe_grouped_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "moe_grouped_ffn": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _P, _I,
+                             _P, _SZ, _P]),
+    "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _I, _P, _P]),
+    "moe_forward_workspace_bytes": (_SZ, [_P, _I]),
+    "moe_forward": (_I, [_P, _P, _I, _P, _P, _SZ, _P, _P, _P, _P, _P]),
+}
+
+
+class LayerDesc(ctypes.Structure):
+    """Mirror of moe_layer_desc."""
+    _fields_ = [
+        ("H", _I), ("F", _I), ("E", _I), ("k", _I), ("Fs", _I),
+        ("act_dt", _I), ("w_dt", _I), ("path", _I),
+        ("Wg", _P), ("gate_bias", _P),
+        ("W1", _P), ("W3", _P), ("W2", _P),
+        ("S1", _P), ("S3", _P), ("S2", _P),
+        ("Ws1", _P), ("Ws3", _P), ("Ws2", _P),
+        ("Ss1", _P), ("Ss3", _P), ("Ss2", _P),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_count_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().moe_status_string(status).decode()
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoEError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def act_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"activation dtype must be float32 or bfloat16, got {t.dtype}")
+
+
+def weight_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.uint8 or t.dtype == torch.float8_e4m3fn:
+        return MOE_FP8_E4M3
+    return act_dtype(t)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libmoe takes device tensors")
+        if not t.is_contiguous():
+            raise ValueError("libmoe takes contiguous tensors")
+
+
+def _i32(t):
+    if t is not None and t.dtype != torch.int32:
+        raise TypeError(f"expected int32 tensor, got {t.dtype}")
+    return t
+
+
+def route(X, Wg, k: int, gate_bias=None):
+    """-> (logits [T,E] f32, topk_idx [T,k] i32, topk_w [T,k] f32)."""
+    _dev(X, Wg, gate_bias)
+    T, H = X.shape
+    E = Wg.shape[1]
+    logits = torch.empty((T, E), dtype=torch.float32, device=X.device)
+    idx = torch.empty((T, k), dtype=torch.int32, device=X.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=X.device)
+    _check("moe_route", lib().moe_route(_ptr(X), act_dtype(X), _ptr(Wg), _ptr(gate_bias), T, H, E, k,
+                                        _ptr(logits), _ptr(idx), _ptr(w), _stream()))
+    return logits, idx, w
+
+
+def permute(topk_idx, E: int, X=None):
+    """-> (counts [E], offsets [E+1], row_src [A], assign_row [A], Xp [A,H] or None)."""
+    _dev(topk_idx, X)
+    _i32(topk_idx)
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    A = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_src = torch.empty(A, dtype=torch.int32, device=dev)
+    assign_row = torch.empty(A, dtype=torch.int32, device=dev)
+    Xp = None
+    H, xdt = 0, MOE_F32
+    if X is not None:
+        H = X.shape[1]
+        xdt = act_dtype(X)
+        Xp = torch.empty((A, H), dtype=X.dtype, device=dev)
+    nbytes = lib().moe_permute_workspace_bytes(T, k, E)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check("moe_permute", lib().moe_permute(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets),
+                                            _ptr(row_src), _ptr(assign_row), _ptr(X), xdt, H, _ptr(Xp),
+                                            _ptr(ws), nbytes, _stream()))
+    return counts, offsets, row_src, assign_row, Xp
+
+
+def grouped_ffn(Xin, offsets, W1, W3, W2, S1=None, S3=None, S2=None, row_src=None, k: int = 1,
+                M: int | None = None, path: str = "auto"):
+    """Yp [M,H] = per-group SwiGLU FFN of the input rows (see moe_grouped_ffn)."""
+    _dev(Xin, offsets, W1, W3, W2, S1, S3, S2, row_src)
+    _i32(offsets)
+    _i32(row_src)
+    G, H, F = W1.shape
+    if M is None:
+        M = row_src.numel() if row_src is not None else Xin.shape[0]
+    adt, wdt = act_dtype(Xin), weight_dtype(W1)
+    Yp = torch.empty((M, H), dtype=Xin.dtype, device=Xin.device)
+    p = PATHS[path]
+    nbytes = lib().moe_grouped_ffn_workspace_bytes(M, G, H, F, adt, wdt, p)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=Xin.device)
+    _check("moe_grouped_ffn", lib().moe_grouped_ffn(
+        _ptr(Xin), _ptr(row_src), k, M, _ptr(offsets), G, H, F, _ptr(W1), _ptr(W3), _ptr(W2), wdt,
+        _ptr(S1), _ptr(S3), _ptr(S2), adt, _ptr(Yp), p, _ptr(ws), nbytes, _stream()))
+    return Yp
+
+
+def combine(Yp, assign_row, topk_w, S=None):
+    """Y [T,H] = sum_j w[t,j] * Yp[assign_row[t*k+j]] (+ S[t])."""
+    _dev(Yp, assign_row, topk_w, S)
+    _i32(assign_row)
+    T, k = topk_w.shape
+    H = Yp.shape[1]
+    Y = torch.empty((T, H), dtype=Yp.dtype, device=Yp.device)
+    _check("moe_combine", lib().moe_combine(_ptr(Yp), _ptr(assign_row), _ptr(topk_w), T, k, H, _ptr(S),
+                                            act_dtype(Yp), _ptr(Y), _stream()))
+    return Y
+
+
+class MoELayer:
+    """One MoE layer's device weights plus a reusable workspace.
+
+    `weights` holds device tensors under the keys Wg, gate_bias, W1, W3, W2,
+    S1, S3, S2 and (shared expert, optional) Ws1, Ws3, Ws2, Ss1, Ss3, Ss2.
+    """
+
+    def __init__(self, weights: dict, k: int, path: str = "auto"):
+        self.w = {key: weights.get(key) for key in
+                  ("Wg", "gate_bias", "W1", "W3", "W2", "S1", "S3", "S2",
+                   "Ws1", "Ws3", "Ws2", "Ss1", "Ss3", "Ss2")}
+        _dev(*[v for v in self.w.values() if v is not None])
+        W1 = self.w["W1"]
+        E, H, F = W1.shape
+        Fs = 0 if self.w["Ws1"] is None else self.w["Ws1"].shape[1]
+        d = LayerDesc()
+        d.H, d.F, d.E, d.k, d.Fs = H, F, E, k, Fs
+        d.act_dt = act_dtype(self.w["Wg"])
+        d.w_dt = weight_dtype(W1)
+        d.path = PATHS[path]
+        for key in self.w:
+            setattr(d, key, None if self.w[key] is None else self.w[key].data_ptr())
+        self.desc = d
+        self.k = k
+        self.E, self.H, self.F, self.Fs = E, H, F, Fs
+        self._ws = None
+
+    def workspace_bytes(self, T: int) -> int:
+        return lib().moe_forward_workspace_bytes(ctypes.byref(self.desc), T)
+
+    def workspace(self, T: int, device) -> torch.Tensor:
+        n = max(self.workspace_bytes(T), 1)
+        if self._ws is None or self._ws.numel() < n or self._ws.device != device:
+            self._ws = torch.empty(n, dtype=torch.uint8, device=device)
+        return self._ws
+
+    def forward(self, X, Y=None, aux: bool = False):
+        """Y [T,H]; with aux=True also (logits, topk_idx, topk_w, counts)."""
+        _dev(X, Y)
+        T = X.shape[0]
+        dev = X.device
+        if Y is None:
+            Y = torch.empty_like(X)
+        ws = self.workspace(T, dev)
+        outs = [None] * 4
+        if aux:
+            outs = [torch.empty((T, self.E), dtype=torch.float32, device=dev),
+                    torch.empty((T, self.k), dtype=torch.int32, device=dev),
+                    torch.empty((T, self.k), dtype=torch.float32, device=dev),
+                    torch.empty(self.E, dtype=torch.int32, device=dev)]
+        _check("moe_forward", lib().moe_forward(ctypes.byref(self.desc), _ptr(X), T, _ptr(Y), _ptr(ws),
+                                                ws.numel(), _stream(), *[_ptr(o) for o in outs]))
+        return (Y, *outs) if aux else Y

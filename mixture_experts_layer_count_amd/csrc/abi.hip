@@ -1,0 +1,467 @@
+// libmoe public entry points: argument validation, workspace layout and the
+// order of stage launches. Every launch goes to the caller's stream; nothing
+// here synchronises with the device or allocates device memory.
+#include <string.h>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kGemvBM = 16;  // rows per tile of the row-streaming GEMM
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Bump allocator over a caller-provided workspace. With base == NULL it only
+// measures.
+struct Carver {
+    char *base;
+    size_t used = 0;
+    explicit Carver(void *b) : base(static_cast<char *>(b)) {}
+    void *take(size_t bytes) {
+        void *p = base ? base + used : nullptr;
+        used += align_up(bytes);
+        return p;
+    }
+};
+
+size_t dt_size(moe_dtype d) { return d == MOE_F32 ? 4 : d == MOE_BF16 ? 2 : 1; }
+
+bool act_ok(moe_dtype a) { return a == MOE_F32 || a == MOE_BF16; }
+
+bool pair_ok(moe_dtype act, moe_dtype w) {
+    return (act == MOE_F32 && w == MOE_F32) || (act == MOE_BF16 && w == MOE_BF16) ||
+           (act == MOE_BF16 && w == MOE_FP8_E4M3);
+}
+
+WType wtype(moe_dtype w) { return w == MOE_F32 ? W_F32 : w == MOE_BF16 ? W_BF16 : W_FP8; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                                  \
+    do {                                               \
+        hipError_t e_ = (expr);                        \
+        if (e_ != hipSuccess) return MOE_ERR_HIP;      \
+    } while (0)
+
+// Shape rules for expert matrices [K][N].
+moe_status check_ffn_dims(int H, int F, moe_dtype w_dt) {
+    if (H < 1 || F < 1) return MOE_ERR_INVALID_ARG;
+    if (H % 32 || F % 32) return MOE_ERR_UNSUPPORTED;
+    if (w_dt == MOE_FP8_E4M3 && (H % 128 || F % 128)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Expert FFN planning (shared by moe_grouped_ffn and moe_forward)
+// ---------------------------------------------------------------------------
+struct FfnPlan {
+    bool tiled;
+    int bm;
+    int ksplit2;  // split-K of the down projection (row-streaming path)
+    int kchunk2;
+};
+
+FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path) {
+    FfnPlan p{};
+    const WType wt = wtype(w_dt);
+    const bool can_tile = tiled_gemm_supports(wt, F, H) && tiled_gemm_supports(wt, H, F);
+    if (path == MOE_PATH_TILED) p.tiled = can_tile;
+    else if (path == MOE_PATH_GEMV) p.tiled = false;
+    else p.tiled = can_tile && (long long)M >= 48LL * G;
+    p.bm = p.tiled ? tiled_gemm_bm() : kGemvBM;
+    p.ksplit2 = 1;
+    p.kchunk2 = F;
+    if (!p.tiled) {
+        // enough wavefronts in flight to cover HBM latency: ~2048
+        const long long tiles_est = M < G ? M : G;
+        const long long waves = tiles_est * ((H + 63) / 64);
+        int ks = (int)((2048 + waves - 1) / (waves > 0 ? waves : 1));
+        ks = ks < 1 ? 1 : ks > 8 ? 8 : ks;
+        const int gran = w_dt == MOE_FP8_E4M3 ? 128 : 32;
+        int chunk = (F + ks - 1) / ks;
+        chunk = (chunk + gran - 1) / gran * gran;
+        p.kchunk2 = chunk;
+        p.ksplit2 = (F + chunk - 1) / chunk;
+    }
+    return p;
+}
+
+struct FfnWs {
+    int32_t *tiles, *n_tiles;
+    void *h;       // [M + extra_rows][F]
+    void *part;    // [ksplit][rows][H] fp32 partials (row-streaming path)
+};
+
+size_t ffn_ws_carve(Carver &c, FfnWs &w, const FfnPlan &p, int M, int G, int H, int F,
+                    int extra_rows, int Fs, moe_dtype act_dt, bool want_part) {
+    const long long max_tiles = (M + p.bm - 1) / p.bm + G;
+    w.tiles = static_cast<int32_t *>(c.take(sizeof(int32_t) * 2 * max_tiles));
+    w.n_tiles = static_cast<int32_t *>(c.take(sizeof(int32_t)));
+    const int hw = F > Fs ? F : Fs;
+    w.h = c.take(dt_size(act_dt) * (size_t)(M + extra_rows) * hw);
+    w.part = want_part ? c.take(sizeof(float) * (size_t)p.ksplit2 * (M + extra_rows) * H) : nullptr;
+    return c.used;
+}
+
+GemmProblem gate_up_problem(const void *X, const int32_t *row_src, int gk, const int32_t *tiles,
+                            const int32_t *n_tiles, const int32_t *offsets, int max_tiles, int M,
+                            int H, int F, const void *W1, const void *W3, const float *S1,
+                            const float *S3, void *h) {
+    GemmProblem g{};
+    g.A = X;
+    g.row_src = row_src;
+    g.gk = gk;
+    g.lda = H;
+    g.tiles = tiles;
+    g.n_tiles = n_tiles;
+    g.offsets = offsets;
+    g.max_tiles = max_tiles;
+    g.M = M;
+    g.N = F;
+    g.K = H;
+    g.B0 = W1;
+    g.B1 = W3;
+    g.b_stride = (long long)H * F;
+    g.S0 = S1;
+    g.S1 = S3;
+    g.s_stride = (long long)(H / 128) * (F / 128);
+    g.C = h;
+    g.ldc = F;
+    g.c_split_stride = 0;
+    g.ksplit = 1;
+    g.kchunk = H;
+    return g;
+}
+
+GemmProblem down_problem(const void *h, const int32_t *tiles, const int32_t *n_tiles,
+                         const int32_t *offsets, int max_tiles, int M, int H, int F, const void *W2,
+                         const float *S2, void *C, long long split_stride, int ksplit, int kchunk) {
+    GemmProblem g{};
+    g.A = h;
+    g.row_src = nullptr;
+    g.gk = 1;
+    g.lda = F;
+    g.tiles = tiles;
+    g.n_tiles = n_tiles;
+    g.offsets = offsets;
+    g.max_tiles = max_tiles;
+    g.M = M;
+    g.N = H;
+    g.K = F;
+    g.B0 = W2;
+    g.B1 = nullptr;
+    g.b_stride = (long long)F * H;
+    g.S0 = S2;
+    g.s_stride = (long long)(F / 128) * (H / 128);
+    g.C = C;
+    g.ldc = H;
+    g.c_split_stride = split_stride;
+    g.ksplit = ksplit;
+    g.kchunk = kchunk;
+    return g;
+}
+
+hipError_t run_gemm(const FfnPlan &p, const GemmProblem &g, WType wt, bool swiglu, bool out_bf16,
+                    hipStream_t s) {
+    return p.tiled ? launch_tiled_gemm(g, wt, swiglu, out_bf16, s)
+                   : launch_stream_gemm(g, wt, swiglu, out_bf16, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(moe_status s) {
+    switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported dtype or shape";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch failed";
+    }
+    return "unknown moe_status";
+}
+
+// ---------------------------------------------------------------------------
+moe_status moe_route(const void *X, moe_dtype x_dt, const void *Wg, const float *gate_bias, int T,
+                     int H, int E, int k, float *logits, int32_t *topk_idx, float *topk_w,
+                     hipStream_t stream) {
+    if (T < 0 || H < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+    if (!act_ok(x_dt)) return MOE_ERR_UNSUPPORTED;
+    if (E > 1024 || k > 64 || E % 4 || H % 32) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!X || !Wg || !logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+    GemmProblem g{};
+    g.A = X;
+    g.gk = 1;
+    g.lda = H;
+    g.M = T;
+    g.N = E;
+    g.K = H;
+    g.B0 = Wg;
+    g.C = logits;
+    g.ldc = E;
+    g.ksplit = 1;
+    g.kchunk = H;
+    MOE_TRY(launch_stream_gemm(g, x_dt == MOE_F32 ? W_F32 : W_BF16, false, false, stream));
+    return hip_status(launch_topk(logits, gate_bias, T, E, k, topk_idx, topk_w, stream));
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_permute_workspace_bytes(int T, int k, int E) {
+    if (T < 0 || k < 1 || E < 1) return 0;
+    return align_up(permute_ws_bytes(T * k, E));
+}
+
+moe_status moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *counts,
+                       int32_t *offsets, int32_t *row_src, int32_t *assign_row, const void *X,
+                       moe_dtype x_dt, int H, void *Xp, void *ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    if (T < 0 || k < 1 || E < 1 || k > E) return MOE_ERR_INVALID_ARG;
+    if (E > 1024) return MOE_ERR_UNSUPPORTED;
+    if ((long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!topk_idx || !counts || !offsets || !row_src || !assign_row) return MOE_ERR_INVALID_ARG;
+    if (Xp) {
+        if (!X || H < 1) return MOE_ERR_INVALID_ARG;
+        if (!act_ok(x_dt)) return MOE_ERR_UNSUPPORTED;
+        if ((H * dt_size(x_dt)) % 16) return MOE_ERR_UNSUPPORTED;
+    }
+    const size_t need = permute_ws_bytes(T * k, E);
+    if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    MOE_TRY(launch_permute(topk_idx, T * k, E, counts, offsets, row_src, assign_row, ws, stream));
+    if (Xp) MOE_TRY(launch_gather_rows(X, (int)dt_size(x_dt), H, row_src, k, T * k, Xp, stream));
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_grouped_ffn_workspace_bytes(int M, int G, int H, int F, moe_dtype act_dt,
+                                       moe_dtype w_dt, moe_ffn_path path) {
+    if (M < 0 || G < 1 || H < 1 || F < 1) return 0;
+    const FfnPlan p = plan_ffn(M, G, H, F, w_dt, path);
+    Carver c(nullptr);
+    FfnWs w{};
+    return ffn_ws_carve(c, w, p, M, G, H, F, 0, 0, act_dt, true);
+}
+
+moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M,
+                           const int32_t *offsets, int G, int H, int F, const void *W1,
+                           const void *W3, const void *W2, moe_dtype w_dt, const float *S1,
+                           const float *S3, const float *S2, moe_dtype act_dt, void *Yp,
+                           moe_ffn_path path, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (M < 0 || G < 1 || k < 1) return MOE_ERR_INVALID_ARG;
+    if (!pair_ok(act_dt, w_dt)) return MOE_ERR_UNSUPPORTED;
+    moe_status st = check_ffn_dims(H, F, w_dt);
+    if (st != MOE_OK) return st;
+    if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_TILED)
+        return MOE_ERR_INVALID_ARG;
+    if (M == 0) return MOE_OK;
+    if (!Xin || !offsets || !W1 || !W3 || !W2 || !Yp) return MOE_ERR_INVALID_ARG;
+    const bool fp8 = w_dt == MOE_FP8_E4M3;
+    if (fp8 != (S1 != nullptr) || fp8 != (S3 != nullptr) || fp8 != (S2 != nullptr))
+        return MOE_ERR_INVALID_ARG;
+    const FfnPlan p = plan_ffn(M, G, H, F, w_dt, path);
+    if (path == MOE_PATH_TILED && !p.tiled) return MOE_ERR_UNSUPPORTED;
+    Carver c(ws);
+    FfnWs w{};
+    const size_t need = ffn_ws_carve(c, w, p, M, G, H, F, 0, 0, act_dt, true);
+    if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    const WType wt = wtype(w_dt);
+    const bool bf = act_dt == MOE_BF16;
+    const int max_tiles = (M + p.bm - 1) / p.bm + G;
+
+    MOE_TRY(launch_build_tiles(offsets, G, p.bm, w.tiles, w.n_tiles, stream));
+    GemmProblem g1 = gate_up_problem(Xin, row_src, k, w.tiles, w.n_tiles, offsets, max_tiles, M, H, F,
+                                     W1, W3, S1, S3, w.h);
+    MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
+    if (p.tiled) {
+        GemmProblem g2 = down_problem(w.h, w.tiles, w.n_tiles, offsets, max_tiles, M, H, F, W2, S2, Yp,
+                                      0, 1, F);
+        MOE_TRY(run_gemm(p, g2, wt, false, bf, stream));
+    } else {
+        const long long split_stride = (long long)M * H;
+        GemmProblem g2 = down_problem(w.h, w.tiles, w.n_tiles, offsets, max_tiles, M, H, F, W2, S2,
+                                      w.part, split_stride, p.ksplit2, p.kchunk2);
+        MOE_TRY(run_gemm(p, g2, wt, false, false, stream));
+        MOE_TRY(launch_reduce_splits(static_cast<const float *>(w.part), split_stride, p.ksplit2, M, H,
+                                     act_dt, Yp, stream));
+    }
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+moe_status moe_combine(const void *Yp, const int32_t *assign_row, const float *topk_w, int T, int k,
+                       int H, const void *S, moe_dtype act_dt, void *Y, hipStream_t stream) {
+    if (T < 0 || k < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+    if (!act_ok(act_dt)) return MOE_ERR_UNSUPPORTED;
+    if (H % 4 || T > 65535) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!Yp || !assign_row || !topk_w || !Y) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_combine(Yp, S, 0, 1, act_dt, assign_row, topk_w, T, k, H, act_dt, Y, stream));
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+
+moe_status check_desc(const moe_layer_desc *d) {
+    if (!d) return MOE_ERR_INVALID_ARG;
+    if (d->E < 1 || d->k < 1 || d->k > d->E || d->Fs < 0) return MOE_ERR_INVALID_ARG;
+    if (!pair_ok(d->act_dt, d->w_dt)) return MOE_ERR_UNSUPPORTED;
+    if (d->E > 1024 || d->k > 64 || d->E % 4) return MOE_ERR_UNSUPPORTED;
+    moe_status st = check_ffn_dims(d->H, d->F, d->w_dt);
+    if (st != MOE_OK) return st;
+    if (d->Fs > 0 && (st = check_ffn_dims(d->H, d->Fs, d->w_dt)) != MOE_OK) return st;
+    if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_GEMV && d->path != MOE_PATH_TILED)
+        return MOE_ERR_INVALID_ARG;
+    if (!d->Wg || !d->W1 || !d->W3 || !d->W2) return MOE_ERR_INVALID_ARG;
+    const bool fp8 = d->w_dt == MOE_FP8_E4M3;
+    if (fp8 != (d->S1 != nullptr) || fp8 != (d->S3 != nullptr) || fp8 != (d->S2 != nullptr))
+        return MOE_ERR_INVALID_ARG;
+    if (d->Fs > 0) {
+        if (!d->Ws1 || !d->Ws3 || !d->Ws2) return MOE_ERR_INVALID_ARG;
+        if (fp8 != (d->Ss1 != nullptr) || fp8 != (d->Ss3 != nullptr) || fp8 != (d->Ss2 != nullptr))
+            return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
+}
+
+struct ForwardWs {
+    float *logits, *w;
+    int32_t *idx, *counts, *offsets, *row_src, *assign_row;
+    void *perm_ws;
+    FfnWs ffn;
+    FfnPlan plan, plan_s;
+    size_t bytes;
+};
+
+ForwardWs carve_forward(const moe_layer_desc *d, int T, void *base) {
+    ForwardWs f{};
+    Carver c(base);
+    const int A = T * d->k;
+    f.logits = static_cast<float *>(c.take(sizeof(float) * (size_t)T * d->E));
+    f.w = static_cast<float *>(c.take(sizeof(float) * (size_t)A));
+    f.idx = static_cast<int32_t *>(c.take(sizeof(int32_t) * (size_t)A));
+    f.counts = static_cast<int32_t *>(c.take(sizeof(int32_t) * (size_t)d->E));
+    f.offsets = static_cast<int32_t *>(c.take(sizeof(int32_t) * (size_t)(d->E + 1)));
+    f.row_src = static_cast<int32_t *>(c.take(sizeof(int32_t) * (size_t)A));
+    f.assign_row = static_cast<int32_t *>(c.take(sizeof(int32_t) * (size_t)A));
+    f.perm_ws = c.take(permute_ws_bytes(A, d->E));
+    f.plan = plan_ffn(A, d->E, d->H, d->F, d->w_dt, d->path);
+    if (d->Fs > 0) {
+        // routed and shared rows share one Yp buffer, so both use one format
+        f.plan_s = plan_ffn(T, 1, d->H, d->Fs, d->w_dt, f.plan.tiled ? MOE_PATH_TILED : MOE_PATH_GEMV);
+        if (f.plan_s.tiled != f.plan.tiled) {
+            f.plan = plan_ffn(A, d->E, d->H, d->F, d->w_dt, MOE_PATH_GEMV);
+            f.plan_s = plan_ffn(T, 1, d->H, d->Fs, d->w_dt, MOE_PATH_GEMV);
+        }
+        if (!f.plan.tiled && f.plan_s.ksplit2 > f.plan.ksplit2) f.plan.ksplit2 = f.plan_s.ksplit2;
+    }
+    const int extra = d->Fs > 0 ? T : 0;
+    // h for routed rows then shared rows; Yp for routed rows then shared rows
+    const long long max_tiles = (A + f.plan.bm - 1) / f.plan.bm + d->E;
+    f.ffn.tiles = static_cast<int32_t *>(c.take(sizeof(int32_t) * 2 * max_tiles));
+    f.ffn.n_tiles = static_cast<int32_t *>(c.take(sizeof(int32_t)));
+    const int hw = d->F > d->Fs ? d->F : d->Fs;
+    f.ffn.h = c.take(dt_size(d->act_dt) * (size_t)(A + extra) * hw);
+    if (f.plan.tiled)
+        f.ffn.part = c.take(dt_size(d->act_dt) * (size_t)(A + extra) * d->H);
+    else
+        f.ffn.part = c.take(sizeof(float) * (size_t)f.plan.ksplit2 * (A + extra) * d->H);
+    f.bytes = c.used;
+    return f;
+}
+
+}  // namespace
+
+size_t moe_forward_workspace_bytes(const moe_layer_desc *desc, int T) {
+    if (check_desc(desc) != MOE_OK || T < 0) return 0;
+    return carve_forward(desc, T, nullptr).bytes;
+}
+
+moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, void *ws,
+                       size_t ws_bytes, hipStream_t stream, float *logits_out,
+                       int32_t *topk_idx_out, float *topk_w_out, int32_t *counts_out) {
+    moe_status st = check_desc(d);
+    if (st != MOE_OK) return st;
+    if (T < 0) return MOE_ERR_INVALID_ARG;
+    if ((long long)T * d->k > 0x7fffffffLL || T > 65535) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!X || !Y) return MOE_ERR_INVALID_ARG;
+    ForwardWs f = carve_forward(d, T, ws);
+    if (!ws || ws_bytes < f.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (logits_out) f.logits = logits_out;
+    if (topk_idx_out) f.idx = topk_idx_out;
+    if (topk_w_out) f.w = topk_w_out;
+    if (counts_out) f.counts = counts_out;
+
+    const int A = T * d->k, H = d->H, F = d->F, E = d->E;
+    const WType wt = wtype(d->w_dt);
+    const bool bf = d->act_dt == MOE_BF16;
+
+    // 1. router
+    st = moe_route(X, d->act_dt, d->Wg, d->gate_bias, T, H, E, d->k, f.logits, f.idx, f.w, stream);
+    if (st != MOE_OK) return st;
+    // 2. dispatch (the row gather is fused into the gate/up GEMM's loads)
+    MOE_TRY(launch_permute(f.idx, A, E, f.counts, f.offsets, f.row_src, f.assign_row, f.perm_ws, stream));
+    // 3. expert FFN
+    const FfnPlan &p = f.plan;
+    const int max_tiles = (A + p.bm - 1) / p.bm + E;
+    MOE_TRY(launch_build_tiles(f.offsets, E, p.bm, f.ffn.tiles, f.ffn.n_tiles, stream));
+    GemmProblem g1 = gate_up_problem(X, f.row_src, d->k, f.ffn.tiles, f.ffn.n_tiles, f.offsets, max_tiles,
+                                     A, H, F, d->W1, d->W3, d->S1, d->S3, f.ffn.h);
+    MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
+    const size_t hb = dt_size(d->act_dt);
+    void *h_s = static_cast<char *>(f.ffn.h) + hb * (size_t)A * (d->F > d->Fs ? d->F : d->Fs);
+    if (d->Fs > 0) {
+        GemmProblem gs = gate_up_problem(X, nullptr, 1, nullptr, nullptr, nullptr, 0, T, H, d->Fs, d->Ws1,
+                                         d->Ws3, d->Ss1, d->Ss3, h_s);
+        MOE_TRY(run_gemm(f.plan_s, gs, wt, true, bf, stream));
+    }
+    const int rows = A + (d->Fs > 0 ? T : 0);
+    const void *S = nullptr;
+    long long split_stride = 0;
+    int nsplit = 1;
+    moe_dtype yp_dt = d->act_dt;
+    if (p.tiled) {
+        GemmProblem g2 = down_problem(f.ffn.h, f.ffn.tiles, f.ffn.n_tiles, f.offsets, max_tiles, A, H, F,
+                                      d->W2, d->S2, f.ffn.part, 0, 1, F);
+        MOE_TRY(run_gemm(p, g2, wt, false, bf, stream));
+        if (d->Fs > 0) {
+            void *Sp = static_cast<char *>(f.ffn.part) + hb * (size_t)A * H;
+            GemmProblem g2s = down_problem(h_s, nullptr, nullptr, nullptr, 0, T, H, d->Fs, d->Ws2, d->Ss2, Sp,
+                                           0, 1, d->Fs);
+            MOE_TRY(run_gemm(f.plan_s, g2s, wt, false, bf, stream));
+            S = Sp;
+        }
+    } else {
+        split_stride = (long long)rows * H;
+        nsplit = p.ksplit2;
+        yp_dt = MOE_F32;
+        // both down projections write all nsplit slices (an empty K range
+        // writes zeros), so combine can sum a fixed number of slices
+        const int gran = d->w_dt == MOE_FP8_E4M3 ? 128 : 32;
+        auto chunk_for = [&](int K) {
+            int c = (K + nsplit - 1) / nsplit;
+            return (c + gran - 1) / gran * gran;
+        };
+        GemmProblem g2 = down_problem(f.ffn.h, f.ffn.tiles, f.ffn.n_tiles, f.offsets, max_tiles, A, H, F,
+                                      d->W2, d->S2, f.ffn.part, split_stride, nsplit, chunk_for(F));
+        MOE_TRY(run_gemm(p, g2, wt, false, false, stream));
+        if (d->Fs > 0) {
+            float *Sp = static_cast<float *>(f.ffn.part) + (size_t)A * H;
+            GemmProblem g2s = down_problem(h_s, nullptr, nullptr, nullptr, 0, T, H, d->Fs, d->Ws2, d->Ss2, Sp,
+                                           split_stride, nsplit, chunk_for(d->Fs));
+            MOE_TRY(run_gemm(f.plan_s, g2s, wt, false, false, stream));
+            S = Sp;
+        }
+    }
+    // 4. combine
+    MOE_TRY(launch_combine(f.ffn.part, S, split_stride, nsplit, yp_dt, f.assign_row, f.w, T, d->k, H,
+                           d->act_dt, Y, stream));
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+// Internal helpers shared by the libmoe HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Vector types for MFMA operands and wide loads
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> f32 (bf16 is carried as raw uint16 bits)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even f32 -> bf16 bits; NaN stays NaN (quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// silu(z) = z / (1 + e^-z)
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// Block-wide exclusive scan of one int per thread (blockDim.x <= 1024,
+// multiple of 64). `lds` must hold 16 ints. Returns the exclusive prefix;
+// *total receives the block sum. Contains barriers: all threads must call.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int block_exclusive_scan(int v, int *lds, int *total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) lds[wid] = x;
+    __syncthreads();
+    if (wid == 0) {
+        int s = lane < nw ? lds[lane] : 0;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) {
+            int y = __shfl_up(s, d, 64);
+            if (lane >= d) s += y;
+        }
+        if (lane < 16) lds[lane] = s;  // inclusive prefix over waves
+    }
+    __syncthreads();
+    int base = wid > 0 ? lds[wid - 1] : 0;
+    *total = lds[nw - 1];
+    __syncthreads();  // lds may be reused by the caller
+    return base + x - v;
+}
+
+// ---------------------------------------------------------------------------
+// Internal launchers (host side). All enqueue on `s` and return hipError_t.
+// ---------------------------------------------------------------------------
+
+// Weight element type of a GEMM: matches moe_dtype for the B operand.
+enum WType { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+
+// Row-streaming grouped GEMM (small rows per group).
+//   C[r, n] = sum_k A(r)[k] * B_g[k, n]   (PLAIN)      or
+//   C[r, n] = silu(A(r) B0_g)[n] * (A(r) B1_g)[n]   (SWIGLU)
+// A(r) = A[row_src[r]/gk] if row_src else A[r]; rows >= n_direct map to
+// A[r - n_direct] (used for the identity-gather shared expert).
+struct GemmProblem {
+    const void *A;
+    const int32_t *row_src;
+    int gk;
+    int lda;
+    const int32_t *tiles;     // (group, row0) pairs, NULL: one group of M rows
+    const int32_t *n_tiles;   // device count of tiles
+    const int32_t *offsets;   // [G+1]; NULL with tiles == NULL
+    int max_tiles;            // host upper bound on tiles
+    int M, N, K;
+    const void *B0, *B1;      // [G][K][N]
+    long long b_stride;       // elements per group
+    const float *S0, *S1;     // fp8 block scales [G][K/128][N/128]
+    long long s_stride;
+    void *C;                  // output rows; split s at C + s * c_split_stride
+    int ldc;
+    long long c_split_stride;
+    int ksplit;
+    int kchunk;               // K elements per split (multiple of 32, or 128 for fp8)
+};
+
+hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,
+                              hipStream_t s);
+
+// LDS-tiled grouped GEMM (many rows per group). Same problem statement;
+// ksplit must be 1. Returns hipErrorInvalidValue for unsupported shapes.
+hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,
+                             hipStream_t s);
+int tiled_gemm_bm();   // rows per tile of the tiled kernel
+bool tiled_gemm_supports(WType wt, int N, int K);
+
+// Tile list (group, row0) for groups of rows given by offsets, bm rows per tile.
+hipError_t launch_build_tiles(const int32_t *offsets, int G, int bm, int32_t *tiles,
+                              int32_t *n_tiles, hipStream_t s);
+
+// Router top-k over fp32 logits (bias added in place first when given).
+hipError_t launch_topk(float *logits, const float *bias, int T, int E, int k,
+                       int32_t *idx, float *w, hipStream_t s);
+
+// Permutation (count / scan / scatter) and optional row gather.
+size_t permute_ws_bytes(int A, int E);
+hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int32_t *offsets,
+                          int32_t *row_src, int32_t *assign_row, void *ws, hipStream_t s);
+hipError_t launch_gather_rows(const void *X, int elem_bytes, int H, const int32_t *row_src,
+                              int gk, int A, void *Xp, hipStream_t s);
+
+// Combine: Y[t] = sum_j w[t,j] * sum_s Yp_s[assign_row[t*k+j]] (+ sum_s S_s[t]).
+// in_dt/out_dt: MOE_F32 or MOE_BF16.
+hipError_t launch_combine(const void *Yp, const void *S, long long split_stride, int nsplit,
+                          moe_dtype in_dt, const int32_t *assign_row, const float *w, int T,
+                          int k, int H, moe_dtype out_dt, void *Y, hipStream_t s);
+
+// Sum fp32 split partials [nsplit][M][N] into out [M][N] (f32 or bf16).
+hipError_t launch_reduce_splits(const float *part, long long split_stride, int nsplit, int M,
+                                int N, moe_dtype out_dt, void *out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,187 @@
+// Dispatch on one GPU: per-expert counts, offsets and a stable permutation.
+//
+// Page "MOE推理流程解析" §二: the T*k assignments are grouped by expert into
+// contiguous matrices and each row keeps its token id; §三: the permutation
+// writes rows in expert order and records an inverse map for combine.
+//
+// Rows of an expert block are in ascending assignment order. The order is
+// decided without atomics, so the result is bit-identical run to run:
+//  1. rank: one 1024-thread block per chunk of 1024 assignments. Inside a
+//     wavefront, lanes holding the same expert are found with log2(E)
+//     ballots; a lane's rank among them is a popcount of the lower lanes.
+//     Per-wave counts go to LDS and are prefix-summed across the 16 waves.
+//     The block writes its per-expert totals and each assignment's rank
+//     within the chunk.
+//  2. scan (one block): per expert, an exclusive sum over chunks, then an
+//     exclusive scan over experts gives offsets; chunk bases are offset by it.
+//  3. scatter: row = chunk base + rank; row_src[row] = a, assign_row[a] = row.
+// When all assignments fit one chunk, the three steps run in one block.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = 1024;
+
+__device__ __forceinline__ int ceil_log2(int E) {
+    int b = 0;
+    while ((1 << b) < E) ++b;
+    return b;
+}
+
+template <bool SINGLE>
+__global__ __launch_bounds__(kChunk) void permute_rank_kernel(
+    const int32_t *idx, int A, int E, int32_t *chunk_counts, int32_t *rank, int32_t *counts,
+    int32_t *offsets, int32_t *row_src, int32_t *assign_row) {
+    // [16][E] per-wave counts, then per-wave prefixes (<= 1024: 16 bits)
+    extern __shared__ unsigned short lds[];
+    __shared__ int scan_lds[16];
+    __shared__ int off_lds[SINGLE ? 1024 : 1];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int a = blockIdx.x * kChunk + tid;
+
+    int e = (a < A) ? idx[a] : -1;
+    if (e < 0 || e >= E) e = -1;
+
+    for (int i = tid; i < 16 * E; i += kChunk) lds[i] = 0;
+    __syncthreads();
+
+    const unsigned long long valid = __ballot(e >= 0);
+    unsigned long long same = valid;
+    const int nbits = ceil_log2(E);
+    for (int b = 0; b < nbits; ++b) {
+        const int bit = (e >> b) & 1;
+        const unsigned long long bal = __ballot(bit);
+        same &= bit ? bal : ~bal;
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const int r_in_wave = __popcll(same & below);
+    if (e >= 0 && r_in_wave == 0) lds[wid * E + e] = (unsigned short)__popcll(same);
+    __syncthreads();
+
+    // exclusive prefix over the 16 waves, per expert (one thread per expert)
+    int total = 0;
+    if (tid < E) {
+        for (int w = 0; w < 16; ++w) {
+            const int c = lds[w * E + tid];
+            lds[w * E + tid] = (unsigned short)total;
+            total += c;
+        }
+    }
+    __syncthreads();
+    const int r_in_chunk = (e >= 0) ? lds[wid * E + e] + r_in_wave : 0;
+
+    if constexpr (!SINGLE) {
+        if (tid < E) chunk_counts[(long long)blockIdx.x * E + tid] = total;
+        if (e >= 0) rank[a] = r_in_chunk;
+    } else {
+        int all = 0;
+        const int off = block_exclusive_scan(tid < E ? total : 0, scan_lds, &all);
+        if (tid < E) {
+            counts[tid] = total;
+            offsets[tid] = off;
+            off_lds[tid] = off;
+        }
+        if (tid == 0) offsets[E] = all;
+        __syncthreads();
+        if (e >= 0) {
+            const int row = off_lds[e] + r_in_chunk;
+            row_src[row] = a;
+            assign_row[a] = row;
+        }
+    }
+}
+
+__global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t *chunk_counts, int nchunks,
+                                                            int E, int32_t *counts,
+                                                            int32_t *offsets) {
+    __shared__ int scan_lds[16];
+    const int tid = threadIdx.x;
+    int total = 0;
+    if (tid < E) {
+        for (int c = 0; c < nchunks; ++c) {
+            const long long i = (long long)c * E + tid;
+            const int v = chunk_counts[i];
+            chunk_counts[i] = total;
+            total += v;
+        }
+    }
+    int all = 0;
+    const int off = block_exclusive_scan(tid < E ? total : 0, scan_lds, &all);
+    if (tid < E) {
+        counts[tid] = total;
+        offsets[tid] = off;
+        for (int c = 0; c < nchunks; ++c) chunk_counts[(long long)c * E + tid] += off;
+    }
+    if (tid == 0) offsets[E] = all;
+}
+
+__global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t *idx, int A, int E,
+                                                              const int32_t *chunk_base,
+                                                              const int32_t *rank,
+                                                              int32_t *row_src,
+                                                              int32_t *assign_row) {
+    const int a = blockIdx.x * 256 + threadIdx.x;
+    if (a >= A) return;
+    const int e = idx[a];
+    if (e < 0 || e >= E) return;
+    const int row = chunk_base[(long long)(a / kChunk) * E + e] + rank[a];
+    row_src[row] = a;
+    assign_row[a] = row;
+}
+
+// Xp[r] = X[row_src[r] / gk]; one block per row, 16-byte vectors.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *X, int row_vecs,
+                                                          const int32_t *row_src, int gk,
+                                                          uint4 *Xp) {
+    const int r = blockIdx.x;
+    const long long src = row_src[r] / gk;
+    for (int i = threadIdx.x; i < row_vecs; i += 256)
+        Xp[(long long)r * row_vecs + i] = X[src * row_vecs + i];
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int A, int E) {
+    const long long nchunks = (A + kChunk - 1) / kChunk;
+    if (nchunks <= 1) return 0;
+    return (size_t)(nchunks * E + A) * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int32_t *offsets,
+                          int32_t *row_src, int32_t *assign_row, void *ws, hipStream_t s) {
+    if (A < 0 || E < 1 || E > 1024) return hipErrorInvalidValue;
+    const int nchunks = (A + kChunk - 1) / kChunk;
+    const size_t lds = (size_t)16 * E * sizeof(unsigned short);
+    if (nchunks <= 1) {
+        hipLaunchKernelGGL(permute_rank_kernel<true>, dim3(1), dim3(kChunk), lds, s, idx, A, E,
+                           nullptr, nullptr, counts, offsets, row_src, assign_row);
+        return hipGetLastError();
+    }
+    int32_t *chunk_counts = reinterpret_cast<int32_t *>(ws);
+    int32_t *rank = chunk_counts + (size_t)nchunks * E;
+    hipLaunchKernelGGL(permute_rank_kernel<false>, dim3(nchunks), dim3(kChunk), lds, s, idx, A, E,
+                       chunk_counts, rank, nullptr, nullptr, nullptr, nullptr);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, E,
+                       counts, offsets);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3((A + 255) / 256), dim3(256), 0, s, idx, A, E,
+                       chunk_counts, rank, row_src, assign_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void *X, int elem_bytes, int H, const int32_t *row_src,
+                              int gk, int A, void *Xp, hipStream_t s) {
+    if (A <= 0) return hipSuccess;
+    const long long row_bytes = (long long)H * elem_bytes;
+    if (row_bytes % 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(A), dim3(256), 0, s,
+                       reinterpret_cast<const uint4 *>(X), (int)(row_bytes / 16), row_src, gk,
+                       reinterpret_cast<uint4 *>(Xp));
+    return hipGetLastError();
+}
+
+}  // namespace moe

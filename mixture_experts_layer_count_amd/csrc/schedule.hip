@@ -1,0 +1,51 @@
+// Device-side tile list for the grouped GEMMs.
+//
+// Page "MOE推理流程解析" §二: one launch runs every expert's matrix even though
+// their row counts differ. The row counts live on the device (they come out
+// of the permutation), so the list of (expert, first row) tiles is built on
+// the device too: no device-to-host copy, and the whole layer stays capturable
+// in a HIP graph. The GEMM grids are sized for the worst case
+// (ceil(M / bm) + G tiles) and surplus workgroups exit at once.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *offsets, int G, int bm,
+                                                           int32_t *tiles, int32_t *n_tiles) {
+    __shared__ int scan_lds[16];
+    __shared__ int base_lds;
+    int carry = 0;
+    // groups in rounds of 1024; each thread emits its group's tiles
+    for (int g0 = 0; g0 < G; g0 += 1024) {
+        const int g = g0 + threadIdx.x;
+        int lo = 0, n = 0;
+        if (g < G) {
+            lo = offsets[g];
+            n = (offsets[g + 1] - lo + bm - 1) / bm;
+            if (n < 0) n = 0;
+        }
+        int total = 0;
+        const int first = block_exclusive_scan(n, scan_lds, &total) + carry;
+        for (int i = 0; i < n; ++i) {
+            tiles[2 * (first + i)] = g;
+            tiles[2 * (first + i) + 1] = lo + i * bm;
+        }
+        carry += total;
+    }
+    if (threadIdx.x == 0) {
+        base_lds = carry;
+        *n_tiles = carry;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_build_tiles(const int32_t *offsets, int G, int bm, int32_t *tiles,
+                              int32_t *n_tiles, hipStream_t s) {
+    if (G < 1 || bm < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, G, bm, tiles, n_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace moe

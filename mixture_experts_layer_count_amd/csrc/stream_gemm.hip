@@ -1,0 +1,304 @@
+// Row-streaming grouped GEMM for few rows per expert (decode).
+//
+// The decode case of the grouped expert computation (page "MoE-推理部署",
+// operator section: with one or two tokens per expert the fused MoE kernel is
+// in effect a batched GEMV and needs its own tile strategy; page
+// "MOE推理流程解析" §二: grouped GEMM runs every expert's row block in one
+// launch). Each wavefront owns one (expert row tile of 16 rows, 64-column
+// slice of the weight) pair and streams that slice of the expert's weights
+// from HBM exactly once, over its K range. Only experts that received rows
+// produce tiles, so untouched experts' weights are never read.
+//
+// MI355X mapping:
+//  * the weight matrices are stored [K][N] (N contiguous). A lane loads VEC
+//    consecutive columns from 8 consecutive K rows; v_perm packs them into
+//    K-contiguous bf16 pairs, which is exactly the B operand layout of
+//    v_mfma_f32_16x16x32_bf16 (no LDS round trip).
+//  * the token rows (<= 16, zero-padded) are the A operand, read directly in
+//    their natural K-contiguous layout, gathered through row_src.
+//  * fp8 E4M3 weights are decoded to bf16 in registers
+//    (v_cvt_scalef32_pk_bf16_fp8, scale 1: exact), multiplied on the bf16
+//    MFMA, and each 128-deep K block's partial sum is multiplied by its fp32
+//    block scale before it joins the accumulator.
+//  * f32 weights use v_mfma_f32_16x16x4_f32 with no transpose.
+//  * the next K step's weight loads are issued before the current step's
+//    MFMAs (register double buffering) to keep HBM requests in flight.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = 4;   // wavefronts per block
+constexpr int kBM = 16;     // rows per tile
+constexpr int kVec = 4;     // weight columns per lane
+constexpr int kNS = 16 * kVec;  // columns per wavefront slice
+
+template <int WT> struct WTraits;
+template <> struct WTraits<W_BF16> {
+    typedef uint16_t elem;
+    typedef u32x2 raw;  // 4 columns
+    typedef uint16_t act;
+};
+template <> struct WTraits<W_FP8> {
+    typedef uint8_t elem;
+    typedef uint32_t raw;  // 4 columns
+    typedef uint16_t act;
+};
+template <> struct WTraits<W_F32> {
+    typedef float elem;
+    typedef f32x4 raw;  // 4 columns
+    typedef float act;
+};
+
+// Pack element `c` (0..3) of 8 consecutive K rows (each row: 4 bf16 columns
+// in two dwords) into a K-contiguous bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 column_frag(const u32x2 (&r)[8], int c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 v;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = (c < 2) ? r[2 * p].x : r[2 * p].y;
+        const uint32_t hi = (c < 2) ? r[2 * p + 1].x : r[2 * p + 1].y;
+        v[p] = __builtin_amdgcn_perm(hi, lo, sel);
+    }
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t q) {
+    u32x2 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, false));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, true));
+    return o;
+}
+
+template <int WT>
+__device__ __forceinline__ void load_rows(typename WTraits<WT>::raw (&r)[8],
+                                          const typename WTraits<WT>::elem *B, long long ldb,
+                                          bool ok) {
+    typedef typename WTraits<WT>::raw R;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (ok) r[i] = *reinterpret_cast<const R *>(B + i * ldb);
+        else r[i] = R{};
+    }
+}
+
+// One K step (32 deep) of acc[c] += A * B[:, c] for the wave's 4 column tiles.
+template <int WT>
+__device__ __forceinline__ void mma_step(f32x4 (&acc)[kVec], const typename WTraits<WT>::raw (&r)[8],
+                                         const void *afrag);
+
+template <>
+__device__ __forceinline__ void mma_step<W_BF16>(f32x4 (&acc)[kVec], const u32x2 (&r)[8],
+                                                 const void *afrag) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(afrag);
+#pragma unroll
+    for (int c = 0; c < kVec; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, column_frag(r, c), acc[c], 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mma_step<W_FP8>(f32x4 (&acc)[kVec], const uint32_t (&q)[8],
+                                                const void *afrag) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(afrag);
+    u32x2 r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = fp8x4_to_bf16x4(q[i]);
+#pragma unroll
+    for (int c = 0; c < kVec; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, column_frag(r, c), acc[c], 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mma_step<W_F32>(f32x4 (&acc)[kVec], const f32x4 (&r)[8],
+                                                const void *afrag) {
+    const float *a = reinterpret_cast<const float *>(afrag);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int c = 0; c < kVec; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], r[s][c], acc[c], 0, 0, 0);
+}
+
+// A fragment: 8 consecutive K values of the lane's row (bf16: 16 B, f32: 32 B).
+template <int WT> struct AFrag;
+template <> struct AFrag<W_BF16> { u32x4 v; };
+template <> struct AFrag<W_FP8> { u32x4 v; };
+template <> struct AFrag<W_F32> { f32x4 v[2]; };
+
+template <int WT>
+__device__ __forceinline__ void load_a(AFrag<WT> &f, const typename WTraits<WT>::act *p, bool ok) {
+    if constexpr (WT == W_F32) {
+        if (ok) {
+            f.v[0] = *reinterpret_cast<const f32x4 *>(p);
+            f.v[1] = *reinterpret_cast<const f32x4 *>(p + 4);
+        } else {
+            f.v[0] = f32x4{};
+            f.v[1] = f32x4{};
+        }
+    } else {
+        f.v = ok ? *reinterpret_cast<const u32x4 *>(p) : u32x4{};
+    }
+}
+
+template <int WT, bool SWIGLU, bool OUT_BF16>
+__global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p, int n_slices) {
+    typedef typename WTraits<WT>::elem E;
+    typedef typename WTraits<WT>::act AT;
+    typedef typename WTraits<WT>::raw R;
+
+    const int lane = threadIdx.x & 63;
+    const long long wave = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int mt = (int)(wave / n_slices);
+    const int ns = (int)(wave - (long long)mt * n_slices);
+    const int split = blockIdx.y;
+
+    int g, row0, row_end;
+    if (p.tiles) {
+        if (mt >= p.max_tiles || mt >= *p.n_tiles) return;
+        g = p.tiles[2 * mt];
+        row0 = p.tiles[2 * mt + 1];
+        row_end = min(row0 + kBM, p.offsets[g + 1]);
+    } else {
+        g = 0;
+        row0 = mt * kBM;
+        if (row0 >= p.M) return;
+        row_end = min(row0 + kBM, p.M);
+    }
+
+    const int kg = lane >> 4;
+    const int col = ns * kNS + kVec * (lane & 15);
+    const bool colok = col < p.N;
+    const int kbeg = split * p.kchunk;
+    const int kend = min(p.K, kbeg + p.kchunk);
+
+    // this lane's activation row (MFMA A operand row = lane & 15)
+    const int r = row0 + (lane & 15);
+    const bool rok = r < row_end;
+    long long arow = 0;
+    if (rok) arow = p.row_src ? (long long)(p.row_src[r] / p.gk) : (long long)r;
+    const AT *Ap = reinterpret_cast<const AT *>(p.A) + arow * p.lda + 8 * kg;
+
+    const long long ldb = p.N;
+    const E *B0 = reinterpret_cast<const E *>(p.B0) + (long long)g * p.b_stride + col + (8 * kg) * ldb;
+    const E *B1 = SWIGLU ? reinterpret_cast<const E *>(p.B1) + (long long)g * p.b_stride + col + (8 * kg) * ldb
+                         : nullptr;
+
+    f32x4 acc0[kVec], acc1[kVec];
+    f32x4 tmp0[kVec], tmp1[kVec];  // fp8: current 128-deep K block
+#pragma unroll
+    for (int c = 0; c < kVec; ++c) {
+        acc0[c] = f32x4{};
+        acc1[c] = f32x4{};
+        tmp0[c] = f32x4{};
+        tmp1[c] = f32x4{};
+    }
+
+    R w0[8], w1[8];
+    AFrag<WT> af;
+    if (kbeg < kend) {
+        load_rows<WT>(w0, B0 + (long long)kbeg * ldb, ldb, colok);
+        if (SWIGLU) load_rows<WT>(w1, B1 + (long long)kbeg * ldb, ldb, colok);
+        load_a<WT>(af, Ap + kbeg, rok);
+    }
+    for (int k0 = kbeg; k0 < kend; k0 += 32) {
+        // prefetch the next K step while this one is multiplied
+        R n0[8], n1[8];
+        AFrag<WT> naf;
+        const bool more = k0 + 32 < kend;
+        if (more) {
+            load_rows<WT>(n0, B0 + (long long)(k0 + 32) * ldb, ldb, colok);
+            if (SWIGLU) load_rows<WT>(n1, B1 + (long long)(k0 + 32) * ldb, ldb, colok);
+            load_a<WT>(naf, Ap + k0 + 32, rok);
+        }
+        if constexpr (WT == W_FP8) {
+            mma_step<WT>(tmp0, w0, &af);
+            if (SWIGLU) mma_step<WT>(tmp1, w1, &af);
+            if ((k0 & 127) == 96 || !more) {
+                // end of a 128-deep scale block: acc += block partial * scale
+                const long long sidx = (long long)g * p.s_stride + (long long)(k0 >> 7) * (p.N >> 7) + (col >> 7);
+                const float s0 = colok ? p.S0[sidx] : 0.0f;
+                const float s1 = (SWIGLU && colok) ? p.S1[sidx] : 0.0f;
+#pragma unroll
+                for (int c = 0; c < kVec; ++c) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc0[c][i] = fmaf(tmp0[c][i], s0, acc0[c][i]);
+                        if (SWIGLU) acc1[c][i] = fmaf(tmp1[c][i], s1, acc1[c][i]);
+                    }
+                    tmp0[c] = f32x4{};
+                    tmp1[c] = f32x4{};
+                }
+            }
+        } else {
+            mma_step<WT>(acc0, w0, &af);
+            if (SWIGLU) mma_step<WT>(acc1, w1, &af);
+        }
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                w0[i] = n0[i];
+                if (SWIGLU) w1[i] = n1[i];
+            }
+            af = naf;
+        }
+    }
+
+    // epilogue: lane holds C[row0 + 4*(lane>>4) + i][col + c]
+    if (!colok) return;
+    char *Cb = reinterpret_cast<char *>(p.C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = row0 + 4 * kg + i;
+        if (row >= row_end) continue;
+        float v[kVec];
+#pragma unroll
+        for (int c = 0; c < kVec; ++c)
+            v[c] = SWIGLU ? silu_f32(acc0[c][i]) * acc1[c][i] : acc0[c][i];
+        const long long off = (long long)split * p.c_split_stride + (long long)row * p.ldc + col;
+        if (OUT_BF16) {
+            u32x2 o;
+            o.x = pack_bf16x2(v[0], v[1]);
+            o.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<u32x2 *>(Cb + off * 2) = o;
+        } else {
+            *reinterpret_cast<f32x4 *>(Cb + off * 4) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+    }
+}
+
+template <int WT, bool SWIGLU, bool OUT_BF16>
+hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
+    const int n_slices = (p.N + kNS - 1) / kNS;
+    const long long mtiles = p.tiles ? (long long)p.max_tiles : (long long)((p.M + kBM - 1) / kBM);
+    const long long waves = mtiles * n_slices;
+    const long long blocks = (waves + kWaves - 1) / kWaves;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    dim3 grid((unsigned)blocks, (unsigned)p.ksplit);
+    hipLaunchKernelGGL((stream_gemm_kernel<WT, SWIGLU, OUT_BF16>), grid, dim3(kWaves * 64), 0, s, p,
+                       n_slices);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,
+                              hipStream_t s) {
+    if (p.K % 32 || p.N % kVec || p.kchunk % 32 || p.ksplit < 1) return hipErrorInvalidValue;
+    if (wt == W_FP8 && (p.K % 128 || p.N % 128 || p.kchunk % 128)) return hipErrorInvalidValue;
+    switch (wt) {
+    case W_BF16:
+        if (swiglu) return out_bf16 ? launch_t<W_BF16, true, true>(p, s) : launch_t<W_BF16, true, false>(p, s);
+        return out_bf16 ? launch_t<W_BF16, false, true>(p, s) : launch_t<W_BF16, false, false>(p, s);
+    case W_FP8:
+        if (swiglu) return out_bf16 ? launch_t<W_FP8, true, true>(p, s) : launch_t<W_FP8, true, false>(p, s);
+        return out_bf16 ? launch_t<W_FP8, false, true>(p, s) : launch_t<W_FP8, false, false>(p, s);
+    case W_F32:
+        if (out_bf16) return hipErrorInvalidValue;
+        return swiglu ? launch_t<W_F32, true, false>(p, s) : launch_t<W_F32, false, false>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

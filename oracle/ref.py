@@ -55,6 +55,17 @@ def e4m3_decode(codes) -> np.ndarray:
     return np.where((e == 15) & (m == 7), np.nan, val)
 
 
+_E4M3_TABLE = None
+
+
+def _e4m3_table() -> np.ndarray:
+    """The 256 decoded E4M3 values (e4m3_decode of every code), tabulated once."""
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = e4m3_decode(np.arange(256, dtype=np.uint8))
+    return _E4M3_TABLE
+
+
 def dequant_blocks(codes, scales, block: int = 128) -> np.ndarray:
     """W[r, c] = decode(code[r, c]) * scale[r // block, c // block], in float64.
 
@@ -63,9 +74,13 @@ def dequant_blocks(codes, scales, block: int = 128) -> np.ndarray:
     expert and per 128x128 block, the per-expert granularity the page
     "MoE-推理部署" asks for in its expert-quantisation section.
     """
-    q = e4m3_decode(codes)
+    if torch is not None and isinstance(codes, torch.Tensor):
+        codes = codes.detach().to("cpu").numpy()
+    q = _e4m3_table()[np.asarray(codes, dtype=np.uint8)]
     s = to_f64(scales)
-    return q * np.repeat(np.repeat(s, block, axis=0), block, axis=1)
+    R, C = q.shape
+    q = q.reshape(R // block, block, C // block, block)
+    return (q * s[:, None, :, None]).reshape(R, C)
 
 
 # ----------------------------------------------------------------------------

@@ -56,8 +56,8 @@ CONFIGS = {
 # not multiples of the kernels' tiles where the format allows it).
 MINI_CONFIGS = {
     c.name: c for c in [
-        LayerConfig("mini_f32", T=37, H=96, F=160, E=5, k=2, act="f32", w="f32", seed=1),
-        LayerConfig("mini_bf16_decode", T=13, H=512, F=640, E=8, k=2, seed=2),
+        LayerConfig("mini_f32", T=37, H=96, F=160, E=12, k=2, act="f32", w="f32", seed=1),
+        LayerConfig("mini_bf16_decode", T=13, H=544, F=672, E=8, k=2, seed=2),
         LayerConfig("mini_bf16_prefill", T=700, H=512, F=384, E=8, k=2, zipf_s=1.1, seed=3),
         LayerConfig("mini_bf16_wide", T=300, H=256, F=192, E=64, k=8, seed=4),
         LayerConfig("mini_fp8_decode", T=20, H=384, F=256, E=16, k=4, Fs=256, w="fp8", seed=5),

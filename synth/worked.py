@@ -27,12 +27,17 @@ def load_fixture(path: str = FIXTURE) -> dict:
         return json.load(fh)
 
 
-def worked_example_layer(F: int = 8, device="cpu", fixture: dict | None = None) -> dict:
+def worked_example_layer(F: int = 8, device="cpu", fixture: dict | None = None, H: int | None = None) -> dict:
+    """H defaults to T; a larger H pads X with zero columns and the gate with
+    zero rows, which leaves every score unchanged."""
     fx = fixture or load_fixture()
     T, E, k = fx["T"], fx["E"], fx["k"]
-    H = T
+    H = T if H is None else H
+    if H < T:
+        raise ValueError("H must be at least T")
     cfg = LayerConfig("worked_example", T=T, H=H, F=F, E=E, k=k, act="f32", w="f32", w_std=0.5)
-    Wg = torch.full((H, E), math.log(0.1), dtype=torch.float64)
+    Wg = torch.zeros((H, E), dtype=torch.float64)
+    Wg[:T] = math.log(0.1)
     for t, pairs in enumerate(fx["choices"]):
         for e1, w in pairs:
             Wg[t, e1 - 1] = math.log(w)

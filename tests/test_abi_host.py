@@ -1,0 +1,131 @@
+"""The C ABI on the host: every declared symbol is exported, and argument
+validation answers with status codes before anything is launched (these
+calls never reach the GPU, so they run without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_count_amd as moe
+from mixture_experts_layer_count_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+F32, BF16, FP8 = 0, 1, 2
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_expected_api():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
+              "moe_forward_workspace_bytes", "moe_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libmoe.so does not export {name}"
+    assert set(declared_functions()) == set(_lib.SIGNATURES), "binding signatures out of sync with moe.h"
+
+
+def test_status_strings():
+    lib = moe.lib()
+    for code in range(5):
+        assert lib.moe_status_string(code).startswith(b"MOE_")
+    assert b"unknown" in lib.moe_status_string(99)
+
+
+def test_route_validation():
+    lib = moe.lib()
+    # k > E, k < 1, bad dtype, E not a multiple of 4, H not a multiple of 32
+    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 8, 9, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 8, 0, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_route(FAKE, FP8, FAKE, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 6, 2, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 48, 8, 2, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.moe_route(None, BF16, FAKE, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None) == INVALID
+    # T == 0: nothing to do, nothing launched
+    assert lib.moe_route(None, BF16, None, None, 0, 64, 8, 2, None, None, None, None) == OK
+
+
+def test_permute_validation_and_workspace():
+    lib = moe.lib()
+    assert lib.moe_permute_workspace_bytes(16, 2, 8) == 0           # one chunk: no workspace
+    n = lib.moe_permute_workspace_bytes(8192, 8, 128)
+    assert n >= (64 * 128 + 65536) * 4 and n % 256 == 0
+    assert lib.moe_permute(FAKE, 8192, 8, 128, FAKE, FAKE, FAKE, FAKE, None, BF16, 0, None,
+                           None, 0, None) == WS_SMALL
+    assert lib.moe_permute(FAKE, 4, 3, 2, FAKE, FAKE, FAKE, FAKE, None, BF16, 0, None,
+                           None, 0, None) == INVALID
+    assert lib.moe_permute(FAKE, 4, 2, 2048, FAKE, FAKE, FAKE, FAKE, None, BF16, 0, None,
+                           None, 0, None) == UNSUPPORTED
+    assert lib.moe_permute(None, 0, 2, 8, None, None, None, None, None, BF16, 0, None,
+                           None, 0, None) == OK
+
+
+def _ffn(lib, **kw):
+    a = dict(Xin=FAKE, row_src=None, k=1, M=64, offsets=FAKE, G=8, H=256, F=512, W1=FAKE, W3=FAKE,
+             W2=FAKE, w_dt=BF16, S1=None, S3=None, S2=None, act_dt=BF16, Yp=FAKE, path=0, ws=FAKE,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.moe_grouped_ffn(*a.values())
+
+
+def test_grouped_ffn_validation():
+    lib = moe.lib()
+    assert _ffn(lib, w_dt=FP8) == INVALID                      # fp8 needs scales
+    assert _ffn(lib, S1=FAKE, S3=FAKE, S2=FAKE) == INVALID     # scales only for fp8
+    assert _ffn(lib, act_dt=F32) == UNSUPPORTED                # f32 activations need f32 weights
+    assert _ffn(lib, H=200) == UNSUPPORTED                     # H % 32
+    assert _ffn(lib, w_dt=FP8, S1=FAKE, S3=FAKE, S2=FAKE, F=480) == UNSUPPORTED  # fp8: F % 128
+    assert _ffn(lib, ws_bytes=16) == WS_SMALL
+    assert _ffn(lib, path=7) == INVALID
+    assert _ffn(lib, M=0, Xin=None) == OK
+
+
+def test_combine_validation():
+    lib = moe.lib()
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 2, 30, None, BF16, FAKE, None) == UNSUPPORTED
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 0, 32, None, BF16, FAKE, None) == INVALID
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 2, 32, None, FP8, FAKE, None) == UNSUPPORTED
+    assert lib.moe_combine(None, None, None, 0, 2, 32, None, BF16, None, None) == OK
+
+
+def _desc(**kw):
+    d = _lib.LayerDesc()
+    base = dict(H=512, F=1024, E=8, k=2, Fs=0, act_dt=BF16, w_dt=BF16, path=0,
+                Wg=0x1000, W1=0x1000, W3=0x1000, W2=0x1000)
+    base.update(kw)
+    for key, v in base.items():
+        setattr(d, key, v)
+    return d
+
+
+def test_forward_validation_and_workspace():
+    lib = moe.lib()
+    d = _desc()
+    n16 = lib.moe_forward_workspace_bytes(ctypes.byref(d), 16)
+    n4k = lib.moe_forward_workspace_bytes(ctypes.byref(d), 4096)
+    assert 0 < n16 < n4k
+    bad = _desc(k=9)
+    assert lib.moe_forward_workspace_bytes(ctypes.byref(bad), 16) == 0
+    assert lib.moe_forward(ctypes.byref(bad), FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None, None) == INVALID
+    assert lib.moe_forward(None, FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None, None) == INVALID
+    fp8_no_scales = _desc(w_dt=FP8)
+    assert lib.moe_forward(ctypes.byref(fp8_no_scales), FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None,
+                           None) == INVALID
+    shared_missing = _desc(Fs=512)
+    assert lib.moe_forward(ctypes.byref(shared_missing), FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None,
+                           None) == INVALID
+    assert lib.moe_forward(ctypes.byref(d), FAKE, 16, FAKE, FAKE, 16, None, None, None, None, None) == WS_SMALL
+    assert lib.moe_forward(ctypes.byref(d), None, 0, None, None, 0, None, None, None, None, None) == OK

@@ -1,0 +1,244 @@
+"""GPU parity: libmoe (through its C ABI) against the fp64 oracle.
+
+Bars: routing (top-k indices), counts, offsets, permutation and inverse map
+bit-exact given the same fp32 logits; layer outputs within the max relative
+error max|Y - Y_ref| / max|Y_ref| of 2e-2 (bf16), 6e-2 (fp8 weights) and 1e-4
+(f32). Inputs are seeded, with top-k logit gaps of at least 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_count_amd as moe
+import oracle
+from synth import CONFIGS, MINI_CONFIGS, LayerConfig
+from synth.worked import load_fixture, worked_example_layer
+from _gpu import rel_err, say, screened_layer, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    moe.lib()  # the HIP library must load: no fallback exists
+
+
+def _to_dev_i32(a):
+    return torch.as_tensor(np.asarray(a), dtype=torch.int32).cuda()
+
+
+def _check_routing(cfg, d, logits, idx, w):
+    L64 = oracle.router_logits(d["X"], d["Wg"], d.get("gate_bias"))
+    lg = logits.cpu().numpy()
+    assert rel_err(lg, L64) < 1e-5
+    idx_np = idx.cpu().numpy()
+    np.testing.assert_array_equal(idx_np, oracle.select_topk(lg, cfg.k))   # same fp32 decision
+    np.testing.assert_array_equal(idx_np, oracle.select_topk(L64, cfg.k))  # = exact decision
+    np.testing.assert_allclose(w.cpu().numpy(), oracle.routing_weights(lg.astype(np.float64), idx_np),
+                               rtol=0, atol=2e-6)
+    return idx_np
+
+
+# ----------------------------------------------------------------------------
+# route
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(MINI_CONFIGS))
+def test_route(name):
+    cfg = MINI_CONFIGS[name]
+    say(f"[route] {name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k}")
+    d = screened_layer(cfg, experts=False)
+    logits, idx, w = moe.route(d["X"], d["Wg"], cfg.k, d["gate_bias"])
+    torch.cuda.synchronize()
+    _check_routing(cfg, d, logits, idx, w)
+
+
+def test_route_worked_example():
+    fx = load_fixture()
+    say("[route] worked example (H padded to 32)")
+    d = worked_example_layer(F=32, H=32, device="cuda")
+    logits, idx, w = moe.route(d["X"], d["Wg"], fx["k"])
+    torch.cuda.synchronize()
+    exp_idx = [[e - 1 for e, _ in sorted(p, key=lambda q: (-q[1], q[0]))] for p in fx["choices"]]
+    exp_w = [[v for _, v in sorted(p, key=lambda q: (-q[1], q[0]))] for p in fx["choices"]]
+    np.testing.assert_array_equal(idx.cpu().numpy(), exp_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), exp_w, atol=1e-6)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 4, 1), (33, 8, 8), (70, 256, 8), (5, 1024, 64), (129, 64, 1)])
+def test_route_shapes(T, E, k):
+    cfg = LayerConfig(f"route_{T}_{E}_{k}", T=T, H=256, F=32, E=E, k=k, w_std=0.2, seed=T + E)
+    say(f"[route] T={T} E={E} k={k}")
+    d = screened_layer(cfg, experts=False)
+    logits, idx, w = moe.route(d["X"], d["Wg"], k)
+    torch.cuda.synchronize()
+    _check_routing(cfg, d, logits, idx, w)
+    np.testing.assert_allclose(w.sum(dim=1).cpu().numpy(), 1.0, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------
+# permute
+# ----------------------------------------------------------------------------
+
+def _idx(T, k, E, mode, seed):
+    rng = np.random.default_rng(seed)
+    if mode == "one":  # every token picks the same k experts
+        return np.tile(np.arange(k)[::-1] + 1, (T, 1)) % E
+    if mode == "zipf":
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        return np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)])
+    return np.argsort(rng.random((T, E)), axis=1)[:, :k]
+
+
+@pytest.mark.parametrize("T,k,E,mode", [
+    (1, 1, 4, "rand"), (13, 2, 8, "rand"), (5, 4, 4, "rand"), (600, 2, 8, "zipf"), (1000, 8, 128, "rand"),
+    (8192, 8, 128, "rand"), (4096, 8, 256, "rand"), (3000, 2, 8, "zipf"), (777, 4, 16, "one"),
+    (1025, 3, 1024, "rand"), (64, 8, 256, "rand"),
+])
+def test_permute(T, k, E, mode):
+    say(f"[permute] T={T} k={k} E={E} {mode}")
+    idx = _idx(T, k, E, mode, T * 31 + E)
+    X = torch.randn((T, 64), device="cuda").to(torch.bfloat16)
+    counts, offsets, row_src, assign_row, Xp = moe.permute(_to_dev_i32(idx), E, X)
+    torch.cuda.synchronize()
+    rc, ro, rr, ra = oracle.permute(idx, E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), rc)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), ro)
+    np.testing.assert_array_equal(row_src.cpu().numpy(), rr)
+    np.testing.assert_array_equal(assign_row.cpu().numpy(), ra)
+    assert torch.equal(Xp, X[torch.as_tensor(rr // k, device="cuda")])
+    again = moe.permute(_to_dev_i32(idx), E)
+    torch.cuda.synchronize()
+    for a, b in zip((counts, offsets, row_src, assign_row), again[:4]):
+        assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------
+# grouped FFN and combine
+# ----------------------------------------------------------------------------
+
+FFN_CASES = [(n, p) for n in MINI_CONFIGS for p in ("gemv",)]
+
+
+@pytest.mark.parametrize("name,path", FFN_CASES)
+def test_grouped_ffn(name, path):
+    cfg = MINI_CONFIGS[name]
+    say(f"[ffn] {name} path={path}")
+    d = screened_layer(cfg)
+    L = oracle.Layer(d, cfg.k)
+    _, idx, _ = oracle.route(L.X(), L.Wg(), L.gate_bias(), cfg.k)
+    counts, offsets, row_src, assign_row = oracle.permute(idx, cfg.E)
+    Xp = L.X()[row_src // cfg.k]
+    ref = oracle.grouped_ffn(Xp, offsets, L.expert)
+    off_d, rs_d = _to_dev_i32(offsets), _to_dev_i32(row_src)
+    # gather fused into the loads
+    Yp = moe.grouped_ffn(d["X"], off_d, d["W1"], d["W3"], d["W2"], d["S1"], d["S3"], d["S2"],
+                         row_src=rs_d, k=cfg.k, path=path)
+    # pre-permuted rows
+    Xp_d = d["X"][torch.as_tensor(row_src // cfg.k, device="cuda")].contiguous()
+    Yp2 = moe.grouped_ffn(Xp_d, off_d, d["W1"], d["W3"], d["W2"], d["S1"], d["S3"], d["S2"], path=path)
+    torch.cuda.synchronize()
+    tol = tol_for(cfg)
+    assert rel_err(Yp, ref) <= tol
+    assert torch.equal(Yp, Yp2)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shared", [False, True])
+def test_combine(dtype, shared):
+    T, k, H = 300, 4, 1024
+    say(f"[combine] {dtype} shared={shared}")
+    rng = np.random.default_rng(7)
+    idx = np.argsort(rng.random((T, 16)), axis=1)[:, :k]
+    _, _, _, assign_row = oracle.permute(idx, 16)
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    Yp = torch.randn((T * k, H), device="cuda").to(dtype)
+    S = torch.randn((T, H), device="cuda").to(dtype) if shared else None
+    Y = moe.combine(Yp, _to_dev_i32(assign_row), torch.as_tensor(w).cuda(), S)
+    torch.cuda.synchronize()
+    ref = oracle.combine(oracle.to_f64(Yp), assign_row, w.astype(np.float64), T, k,
+                         None if S is None else oracle.to_f64(S))
+    assert rel_err(Y, ref) <= (1e-6 if dtype == torch.float32 else 4e-3)
+
+
+# ----------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------
+
+def _check_forward(cfg, d, layer, tokens=None):
+    Y, logits, idx, w, counts = layer.forward(d["X"], aux=True)
+    torch.cuda.synchronize()
+    idx_np = _check_routing(cfg, d, logits, idx, w)
+    np.testing.assert_array_equal(counts.cpu().numpy(), oracle.permute(idx_np, cfg.E)[0])
+    L = oracle.Layer(d, cfg.k)
+    if tokens is None:
+        tokens = np.arange(cfg.T)
+    ref = oracle.forward_tokens(L, tokens, idx=idx_np[tokens])
+    err = rel_err(Y[torch.as_tensor(tokens, device="cuda")], ref["Y"])
+    say(f"    max rel err {err:.3e} (tol {tol_for(cfg)})")
+    assert err <= tol_for(cfg)
+    assert torch.isfinite(Y.float()).all()
+    return Y
+
+
+@pytest.mark.parametrize("name,path", FFN_CASES)
+def test_forward_mini(name, path):
+    cfg = MINI_CONFIGS[name]
+    say(f"[forward] {name} path={path}")
+    d = screened_layer(cfg)
+    Y = _check_forward(cfg, d, moe.MoELayer(d, cfg.k, path=path))
+    Y2 = moe.MoELayer(d, cfg.k, path=path).forward(d["X"])
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)  # deterministic
+
+
+def test_forward_worked_example():
+    say("[forward] worked example (H, F padded to 32)")
+    d = worked_example_layer(F=32, H=32, device="cuda")
+    cfg = d["cfg"].with_(H=32, F=32)
+    _check_forward(cfg, d, moe.MoELayer(d, cfg.k))
+
+
+@pytest.mark.parametrize("variant", ["k1", "kE", "one_hot_expert", "T1"])
+def test_forward_edge_cases(variant):
+    base = MINI_CONFIGS["mini_bf16_decode"]
+    cfg = {"k1": base.with_(k=1), "kE": base.with_(k=8), "T1": base.with_(T=1),
+           "one_hot_expert": base.with_(T=200)}[variant]
+    say(f"[forward] edge case {variant}")
+    d = screened_layer(cfg)
+    if variant == "one_hot_expert":
+        # a large gate bias sends every token to expert 3 first and expert 5 second
+        b = torch.zeros(cfg.E, dtype=torch.float32, device="cuda")
+        b[3], b[5] = 60.0, 40.0
+        d["gate_bias"] = b
+    _check_forward(cfg, d, moe.MoELayer(d, cfg.k))
+
+
+def test_forward_empty_batch():
+    cfg = MINI_CONFIGS["mini_bf16_decode"]
+    d = screened_layer(cfg)
+    layer = moe.MoELayer(d, cfg.k)
+    X = d["X"][:0]
+    Y = layer.forward(X)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, cfg.H)
+
+
+FULL_SAMPLES = {"toy_fp32": None, "mixtral_decode": None, "qwen3_decode": None,
+                "mixtral_prefill": 6, "qwen3_prefill": 8, "dsv3_decode": 4, "dsv3_prefill": 4}
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_forward_full_size(name):
+    cfg = CONFIGS[name]
+    say(f"[forward] full size {name} T={cfg.T} H={cfg.H} F={cfg.F} E={cfg.E} k={cfg.k} Fs={cfg.Fs} w={cfg.w}")
+    d = screened_layer(cfg)
+    n = FULL_SAMPLES[name]
+    tokens = None
+    if n is not None:
+        rng = np.random.default_rng(cfg.T)
+        tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, size=n - 2, replace=False)]))
+    _check_forward(cfg, d, moe.MoELayer(d, cfg.k), tokens)
