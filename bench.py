@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""MoE layer forward throughput on one MI355X.
+
+One step = one full MoE layer forward (router, dispatch, grouped SwiGLU expert
+FFN, combine) over one batch of T tokens, through libmoe's C ABI, with inputs
+and weights already resident in HBM. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+The dominant kernel (the routed gate/up grouped GEMM with fused SwiGLU, which
+streams two thirds of the touched expert weights) is timed with HIP events
+recorded by libmoe on its own stream around that kernel, in every timed step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at 1 GPU + % HBM peak (decode) / % MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+DECODE_WORKLOADS = {"toy_fp32", "mixtral_decode", "qwen3_decode", "dsv3_decode"}
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("stream_gemm.hip", "tiled_gemm.hip", "common.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        p = os.path.join(ROOT, "mixture_experts_layer_count_amd", "csrc", name)
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from a committed PMC summary, or None
+    when none exists or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def weight_bytes(cfg) -> float:
+    return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0}[cfg.w]
+
+
+def cpu_baseline(cfg, d, k: int) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same layer."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    n = cfg.T if cfg.T <= 64 and cfg.E <= 16 else (16 if cfg.E <= 16 else 4)
+    tokens = np.arange(min(n, cfg.T))
+    host = {key: (v.cpu() if hasattr(v, "cpu") else v) for key, v in d.items()}
+    L = oracle.Layer(host, k)
+    t0 = time.perf_counter()
+    oracle.forward_tokens(L, tokens)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(tokens)} of {cfg.T} tokens, full fp64 layer forward (route over all E, "
+                      f"SwiGLU of each chosen expert, combine); {dt:.1f} s on {platform.processor() or 'host'}"}
+
+
+def copy_calibration(nbytes: int = 1 << 30) -> None:
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral_decode")
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "tiled"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the MoE layer here runs on a "
+              f"single MI355X with all experts resident, and no multi-GPU path is built.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    import mixture_experts_layer_count_amd as moe
+    from mixture_experts_layer_count_amd._lib import MOE_N_EVENTS
+    from synth import get_config, make_layer
+
+    cfg = get_config(args.workload)
+    d = make_layer(cfg, device="cuda")
+    layer = moe.MoELayer(d, cfg.k, path=args.path)
+    X = d["X"]
+    Y = torch.empty_like(X)
+
+    # routing of this batch: which experts are touched (bytes actually streamed)
+    _, _, idx, _, counts = layer.forward(X, Y, aux=True)
+    torch.cuda.synchronize()
+    touched = int((counts > 0).sum().item())
+    A = cfg.T * cfg.k
+
+    EV_SCHED, EV_GATE_UP = 3, 4
+    evs = [moe.StageEvents(want=[EV_SCHED, EV_GATE_UP]) for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        layer.forward(X, Y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        layer.forward(X, Y, events=evs[i].handles)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    gate_up_ms = statistics.fmean(e.elapsed_ms(EV_SCHED, EV_GATE_UP) for e in evs)
+
+    # per-stage breakdown (separate, untimed pass: every marker recorded)
+    stage_runs = []
+    for _ in range(max(5, min(args.steps, 20))):
+        ev = moe.StageEvents()
+        layer.forward(X, Y, events=ev.handles)
+        stage_runs.append([ev.elapsed_ms(i, i + 1) for i in range(MOE_N_EVENTS - 1)])
+    torch.cuda.synchronize()
+    stages_ms = {name: round(statistics.median(r[i] for r in stage_runs), 4) for i, name in enumerate(moe.STAGES)}
+
+    # algorithmic work of the dominant kernel (routed gate/up + SwiGLU), per launch
+    wb = weight_bytes(cfg)
+    ab = 4.0 if cfg.act == "f32" else 2.0
+    gate_up_w = touched * 2 * cfg.H * cfg.F * wb
+    if cfg.w == "fp8":
+        gate_up_w += touched * 2 * (cfg.H // 128) * (cfg.F // 128) * 4
+    gate_up_bytes = gate_up_w + cfg.T * cfg.H * ab + A * cfg.F * ab
+    gate_up_flops = 4.0 * A * cfg.H * cfg.F
+    decode = args.workload in DECODE_WORKLOADS
+    kernel_name = "gate_up_swiglu"
+    if decode:
+        achieved = gate_up_bytes / (gate_up_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        mfma_dt = "f32" if cfg.w == "f32" else "bf16"  # fp8 weights are decoded to bf16 for the MFMA
+        achieved = gate_up_flops / (gate_up_ms * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[mfma_dt]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    roof["traffic"] = measured_traffic(args.workload, kernel_name)
+    roof["kernel"] = kernel_name
+    roof["kernel_ms"] = round(gate_up_ms, 4)
+    roof["algorithmic_bytes"] = gate_up_bytes
+    roof["algorithmic_flops"] = gate_up_flops
+
+    # whole-layer view: touched expert weights (+ gate, shared expert) over the step time
+    layer_w = touched * 3 * cfg.H * cfg.F * wb + cfg.H * cfg.E * ab + 3 * cfg.H * cfg.Fs * wb
+    if cfg.w == "fp8":
+        layer_w += (touched * 3 * (cfg.H // 128) * (cfg.F // 128) + 3 * (cfg.H // 128) * (cfg.Fs // 128)) * 4
+    layer_flops = 6.0 * A * cfg.H * cfg.F + 6.0 * cfg.T * cfg.H * cfg.Fs + 2.0 * cfg.T * cfg.H * cfg.E
+
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[cfg.w],
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
+                   "Fs": cfg.Fs, "weights": cfg.w, "activations": cfg.act, "path": args.path},
+        "roofline": roof,
+        "layer": {"touched_experts": touched, "weight_bytes": layer_w,
+                  "hbm_frac": round(layer_w / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                  "mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / (MFMA_PEAK_TFLOPS["bf16"] * 1e12), 4),
+                  "stages_ms": stages_ms},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, d, cfg.k)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

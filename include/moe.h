@@ -154,7 +154,7 @@ moe_status moe_combine(const void *Yp, const int32_t *assign_row, const float *t
  * shared expert (Fs > 0) uses Ws1, Ws3 [H, Fs], Ws2 [Fs, H] (+ Ss* scales
  * for FP8) and is added with weight 1. X [T, H] and Y [T, H] in act_dt.
  * Optional outputs (NULL to skip): logits [T,E], topk_idx [T,k],
- * topk_w [T,k], counts [E].
+ * topk_w [T,k], counts [E]. Optional `events`: see MOE_EV_* below.
  * Workspace: moe_forward_workspace_bytes(desc, T) bytes.
  * ------------------------------------------------------------------------- */
 typedef struct moe_layer_desc {
@@ -169,11 +169,29 @@ typedef struct moe_layer_desc {
     const float *Ss1, *Ss3, *Ss2;
 } moe_layer_desc;
 
+/* Stage markers for moe_forward's `events` argument: events[i] is recorded on
+ * `stream` right after stage i (events[MOE_EV_START] before the first
+ * launch). The page "MOE推理流程解析" (sections 三 and 十) asks for routing,
+ * permutation, expert GEMM and combine to be timed separately; elapsed time
+ * between consecutive markers is exactly one stage. Entries may be NULL. */
+enum {
+    MOE_EV_START = 0,
+    MOE_EV_ROUTE,          /* router GEMM + top-k done */
+    MOE_EV_PERMUTE,        /* counts / offsets / permutation done */
+    MOE_EV_SCHEDULE,       /* tile list built */
+    MOE_EV_GATE_UP,        /* routed gate/up GEMM + SwiGLU done */
+    MOE_EV_SHARED_GATE_UP, /* shared expert gate/up done (no-op without one) */
+    MOE_EV_DOWN,           /* routed down projection done */
+    MOE_EV_SHARED_DOWN,    /* shared expert down projection done */
+    MOE_EV_COMBINE,        /* combine done: Y written */
+    MOE_N_EVENTS
+};
+
 size_t moe_forward_workspace_bytes(const moe_layer_desc *desc, int T);
 moe_status moe_forward(const moe_layer_desc *desc, const void *X, int T, void *Y,
                        void *ws, size_t ws_bytes, hipStream_t stream,
                        float *logits_out, int32_t *topk_idx_out, float *topk_w_out,
-                       int32_t *counts_out);
+                       int32_t *counts_out, hipEvent_t const *events /* [MOE_N_EVENTS] or NULL */);
 
 #ifdef __cplusplus
 }

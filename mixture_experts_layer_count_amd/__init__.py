@@ -7,7 +7,9 @@ is a HIP kernel in libmoe.so (C ABI: include/moe.h); this package is its thin
 Python binding, with torch providing device memory and streams.
 """
 from ._lib import (
-    LIB_PATH, MoEError, MoELayer, combine, grouped_ffn, lib, permute, route,
+    LIB_PATH, MOE_N_EVENTS, STAGES, MoEError, MoELayer, StageEvents, combine, grouped_ffn, lib,
+    permute, route,
 )
 
-__all__ = ["LIB_PATH", "MoEError", "MoELayer", "combine", "grouped_ffn", "lib", "permute", "route"]
+__all__ = ["LIB_PATH", "MOE_N_EVENTS", "STAGES", "MoEError", "MoELayer", "StageEvents", "combine",
+           "grouped_ffn", "lib", "permute", "route"]

@@ -32,7 +32,7 @@ SIGNATURES = {
                              _P, _SZ, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _I, _P, _P]),
     "moe_forward_workspace_bytes": (_SZ, [_P, _I]),
-    "moe_forward": (_I, [_P, _P, _I, _P, _P, _SZ, _P, _P, _P, _P, _P]),
+    "moe_forward": (_I, [_P, _P, _I, _P, _P, _SZ, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -222,8 +222,11 @@ class MoELayer:
             self._ws = torch.empty(n, dtype=torch.uint8, device=device)
         return self._ws
 
-    def forward(self, X, Y=None, aux: bool = False):
-        """Y [T,H]; with aux=True also (logits, topk_idx, topk_w, counts)."""
+    def forward(self, X, Y=None, aux: bool = False, events=None):
+        """Y [T,H]; with aux=True also (logits, topk_idx, topk_w, counts).
+
+        `events`: optional ctypes array of MOE_N_EVENTS hipEvent_t handles
+        (see StageEvents) recorded after each stage."""
         _dev(X, Y)
         T = X.shape[0]
         dev = X.device
@@ -237,5 +240,73 @@ class MoELayer:
                     torch.empty((T, self.k), dtype=torch.float32, device=dev),
                     torch.empty(self.E, dtype=torch.int32, device=dev)]
         _check("moe_forward", lib().moe_forward(ctypes.byref(self.desc), _ptr(X), T, _ptr(Y), _ptr(ws),
-                                                ws.numel(), _stream(), *[_ptr(o) for o in outs]))
+                                                ws.numel(), _stream(), *[_ptr(o) for o in outs], events))
         return (Y, *outs) if aux else Y
+
+
+# ---------------------------------------------------------------------------
+# Stage timing with HIP events (plumbing for measurement only)
+# ---------------------------------------------------------------------------
+MOE_N_EVENTS = 9
+STAGES = ["route", "permute", "schedule", "gate_up", "shared_gate_up", "down", "shared_down", "combine"]
+
+_hip = None
+
+
+def hip_runtime() -> ctypes.CDLL:
+    global _hip
+    if _hip is None:
+        # the runtime torch already loaded (same soname as libmoe's dependency)
+        for name in ("libamdhip64.so.7", "libamdhip64.so"):
+            try:
+                _hip = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if _hip is None:
+            raise RuntimeError("libamdhip64.so not found")
+        # event handles are pointers: declare every signature so ctypes never
+        # narrows them to C int
+        _hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        _hip.hipEventCreate.restype = ctypes.c_int
+        _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hip.hipEventDestroy.restype = ctypes.c_int
+        _hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        _hip.hipEventSynchronize.restype = ctypes.c_int
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        _hip.hipEventElapsedTime.restype = ctypes.c_int
+    return _hip
+
+
+class StageEvents:
+    """MOE_N_EVENTS timing events; `want` selects which markers are recorded."""
+
+    def __init__(self, want=None):
+        hip = hip_runtime()
+        self.handles = (ctypes.c_void_p * MOE_N_EVENTS)()
+        self._owned = []
+        want = range(MOE_N_EVENTS) if want is None else want
+        for i in want:
+            ev = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles[i] = ev
+            self._owned.append(ev)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        """Milliseconds between markers i and j (both must have been recorded)."""
+        hip = hip_runtime()
+        ms = ctypes.c_float()
+        if hip.hipEventSynchronize(self.handles[j]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        if hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[i], self.handles[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        try:
+            hip = hip_runtime()
+            for ev in self._owned:
+                hip.hipEventDestroy(ev)
+        except Exception:
+            pass

@@ -383,7 +383,11 @@ size_t moe_forward_workspace_bytes(const moe_layer_desc *desc, int T) {
 
 moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, void *ws,
                        size_t ws_bytes, hipStream_t stream, float *logits_out,
-                       int32_t *topk_idx_out, float *topk_w_out, int32_t *counts_out) {
+                       int32_t *topk_idx_out, float *topk_w_out, int32_t *counts_out,
+                       hipEvent_t const *events) {
+    auto mark = [&](int i) -> hipError_t {
+        return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess;
+    };
     moe_status st = check_desc(d);
     if (st != MOE_OK) return st;
     if (T < 0) return MOE_ERR_INVALID_ARG;
@@ -401,18 +405,23 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     const WType wt = wtype(d->w_dt);
     const bool bf = d->act_dt == MOE_BF16;
 
+    MOE_TRY(mark(MOE_EV_START));
     // 1. router
     st = moe_route(X, d->act_dt, d->Wg, d->gate_bias, T, H, E, d->k, f.logits, f.idx, f.w, stream);
     if (st != MOE_OK) return st;
+    MOE_TRY(mark(MOE_EV_ROUTE));
     // 2. dispatch (the row gather is fused into the gate/up GEMM's loads)
     MOE_TRY(launch_permute(f.idx, A, E, f.counts, f.offsets, f.row_src, f.assign_row, f.perm_ws, stream));
+    MOE_TRY(mark(MOE_EV_PERMUTE));
     // 3. expert FFN
     const FfnPlan &p = f.plan;
     const int max_tiles = (A + p.bm - 1) / p.bm + E;
     MOE_TRY(launch_build_tiles(f.offsets, E, p.bm, f.ffn.tiles, f.ffn.n_tiles, stream));
+    MOE_TRY(mark(MOE_EV_SCHEDULE));
     GemmProblem g1 = gate_up_problem(X, f.row_src, d->k, f.ffn.tiles, f.ffn.n_tiles, f.offsets, max_tiles,
                                      A, H, F, d->W1, d->W3, d->S1, d->S3, f.ffn.h);
     MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
+    MOE_TRY(mark(MOE_EV_GATE_UP));
     const size_t hb = dt_size(d->act_dt);
     void *h_s = static_cast<char *>(f.ffn.h) + hb * (size_t)A * (d->F > d->Fs ? d->F : d->Fs);
     if (d->Fs > 0) {
@@ -420,6 +429,7 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
                                          d->Ws3, d->Ss1, d->Ss3, h_s);
         MOE_TRY(run_gemm(f.plan_s, gs, wt, true, bf, stream));
     }
+    MOE_TRY(mark(MOE_EV_SHARED_GATE_UP));
     const int rows = A + (d->Fs > 0 ? T : 0);
     const void *S = nullptr;
     long long split_stride = 0;
@@ -429,6 +439,7 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
         GemmProblem g2 = down_problem(f.ffn.h, f.ffn.tiles, f.ffn.n_tiles, f.offsets, max_tiles, A, H, F,
                                       d->W2, d->S2, f.ffn.part, 0, 1, F);
         MOE_TRY(run_gemm(p, g2, wt, false, bf, stream));
+        MOE_TRY(mark(MOE_EV_DOWN));
         if (d->Fs > 0) {
             void *Sp = static_cast<char *>(f.ffn.part) + hb * (size_t)A * H;
             GemmProblem g2s = down_problem(h_s, nullptr, nullptr, nullptr, 0, T, H, d->Fs, d->Ws2, d->Ss2, Sp,
@@ -450,6 +461,7 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
         GemmProblem g2 = down_problem(f.ffn.h, f.ffn.tiles, f.ffn.n_tiles, f.offsets, max_tiles, A, H, F,
                                       d->W2, d->S2, f.ffn.part, split_stride, nsplit, chunk_for(F));
         MOE_TRY(run_gemm(p, g2, wt, false, false, stream));
+        MOE_TRY(mark(MOE_EV_DOWN));
         if (d->Fs > 0) {
             float *Sp = static_cast<float *>(f.ffn.part) + (size_t)A * H;
             GemmProblem g2s = down_problem(h_s, nullptr, nullptr, nullptr, 0, T, H, d->Fs, d->Ws2, d->Ss2, Sp,
@@ -458,9 +470,11 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
             S = Sp;
         }
     }
+    MOE_TRY(mark(MOE_EV_SHARED_DOWN));
     // 4. combine
     MOE_TRY(launch_combine(f.ffn.part, S, split_stride, nsplit, yp_dt, f.assign_row, f.w, T, d->k, H,
                            d->act_dt, Y, stream));
+    MOE_TRY(mark(MOE_EV_COMBINE));
     return MOE_OK;
 }
 

@@ -119,13 +119,13 @@ def test_forward_validation_and_workspace():
     assert 0 < n16 < n4k
     bad = _desc(k=9)
     assert lib.moe_forward_workspace_bytes(ctypes.byref(bad), 16) == 0
-    assert lib.moe_forward(ctypes.byref(bad), FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None, None) == INVALID
-    assert lib.moe_forward(None, FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None, None) == INVALID
+    assert lib.moe_forward(ctypes.byref(bad), FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None, None, None) == INVALID
+    assert lib.moe_forward(None, FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None, None, None) == INVALID
     fp8_no_scales = _desc(w_dt=FP8)
     assert lib.moe_forward(ctypes.byref(fp8_no_scales), FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None,
-                           None) == INVALID
+                           None, None) == INVALID
     shared_missing = _desc(Fs=512)
     assert lib.moe_forward(ctypes.byref(shared_missing), FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None,
-                           None) == INVALID
-    assert lib.moe_forward(ctypes.byref(d), FAKE, 16, FAKE, FAKE, 16, None, None, None, None, None) == WS_SMALL
-    assert lib.moe_forward(ctypes.byref(d), None, 0, None, None, 0, None, None, None, None, None) == OK
+                           None, None) == INVALID
+    assert lib.moe_forward(ctypes.byref(d), FAKE, 16, FAKE, FAKE, 16, None, None, None, None, None, None) == WS_SMALL
+    assert lib.moe_forward(ctypes.byref(d), None, 0, None, None, 0, None, None, None, None, None, None) == OK
