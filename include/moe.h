@@ -89,10 +89,16 @@ const char *moe_status_string(moe_status s);
  * X [T,H] and Wg [H,E] in x_dt (F32 or BF16); gate_bias [E] fp32 or NULL.
  * Outputs: logits [T,E] fp32, topk_idx [T,k] int32, topk_w [T,k] fp32.
  * NaN logits are never selected while a non-NaN logit is left.
+ * The sum over h is split into fixed K ranges whose fp32 partial sums are
+ * added in a fixed order, so results are identical run to run.
+ * Workspace: moe_route_workspace_bytes(T, H, E) bytes (may be 0; then ws may
+ * be NULL).
  * ------------------------------------------------------------------------- */
+size_t moe_route_workspace_bytes(int T, int H, int E);
 moe_status moe_route(const void *X, moe_dtype x_dt, const void *Wg, const float *gate_bias,
                      int T, int H, int E, int k,
-                     float *logits, int32_t *topk_idx, float *topk_w, hipStream_t stream);
+                     float *logits, int32_t *topk_idx, float *topk_w,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Dispatch on one GPU: group the A = T*k assignments by expert.

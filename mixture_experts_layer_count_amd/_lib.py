@@ -24,7 +24,8 @@ _I = ctypes.c_int
 _SZ = ctypes.c_size_t
 SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
-    "moe_route": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_route_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "moe_route": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
     "moe_grouped_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
@@ -124,8 +125,10 @@ def route(X, Wg, k: int, gate_bias=None):
     logits = torch.empty((T, E), dtype=torch.float32, device=X.device)
     idx = torch.empty((T, k), dtype=torch.int32, device=X.device)
     w = torch.empty((T, k), dtype=torch.float32, device=X.device)
+    nbytes = lib().moe_route_workspace_bytes(T, H, E)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device)
     _check("moe_route", lib().moe_route(_ptr(X), act_dtype(X), _ptr(Wg), _ptr(gate_bias), T, H, E, k,
-                                        _ptr(logits), _ptr(idx), _ptr(w), _stream()))
+                                        _ptr(logits), _ptr(idx), _ptr(w), _ptr(ws), nbytes, _stream()))
     return logits, idx, w
 
 

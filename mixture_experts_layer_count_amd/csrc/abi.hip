@@ -186,14 +186,36 @@ const char *moe_status_string(moe_status s) {
 }
 
 // ---------------------------------------------------------------------------
-moe_status moe_route(const void *X, moe_dtype x_dt, const void *Wg, const float *gate_bias, int T,
-                     int H, int E, int k, float *logits, int32_t *topk_idx, float *topk_w,
-                     hipStream_t stream) {
-    if (T < 0 || H < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
-    if (!act_ok(x_dt)) return MOE_ERR_UNSUPPORTED;
-    if (E > 1024 || k > 64 || E % 4 || H % 32) return MOE_ERR_UNSUPPORTED;
-    if (T == 0) return MOE_OK;
-    if (!X || !Wg || !logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+namespace {
+
+// Split of the router's sum over h: enough wavefronts (16 rows x 64 experts
+// each) to keep the gate and token reads in flight, at least 4 K steps each.
+struct RoutePlan {
+    int ksplit, kchunk;
+};
+
+RoutePlan plan_route(int T, int H, int E) {
+    long long base = (long long)((T + 15) / 16) * ((E + 63) / 64);
+    if (base < 1) base = 1;
+    long long ks = (1024 + base - 1) / base;
+    const long long max_ks = H / 128 > 0 ? H / 128 : 1;
+    if (ks > max_ks) ks = max_ks;
+    if (ks < 1) ks = 1;
+    int chunk = (int)((H + ks - 1) / ks);
+    chunk = (chunk + 31) / 32 * 32;
+    return RoutePlan{(H + chunk - 1) / chunk, chunk};
+}
+
+size_t route_ws_bytes(int T, int H, int E) {
+    const RoutePlan r = plan_route(T, H, E);
+    return r.ksplit > 1 ? (size_t)r.ksplit * T * E * sizeof(float) : 0;
+}
+
+moe_status route_impl(const void *X, moe_dtype x_dt, const void *Wg, const float *gate_bias, int T, int H,
+                      int E, int k, float *logits, int32_t *topk_idx, float *topk_w, void *ws,
+                      hipStream_t stream) {
+    const RoutePlan r = plan_route(T, H, E);
+    float *part = r.ksplit > 1 ? static_cast<float *>(ws) : logits;
     GemmProblem g{};
     g.A = X;
     g.gk = 1;
@@ -202,12 +224,40 @@ moe_status moe_route(const void *X, moe_dtype x_dt, const void *Wg, const float 
     g.N = E;
     g.K = H;
     g.B0 = Wg;
-    g.C = logits;
+    g.C = part;
     g.ldc = E;
-    g.ksplit = 1;
-    g.kchunk = H;
+    g.c_split_stride = (long long)T * E;
+    g.ksplit = r.ksplit;
+    g.kchunk = r.kchunk;
     MOE_TRY(launch_stream_gemm(g, x_dt == MOE_F32 ? W_F32 : W_BF16, false, false, stream));
-    return hip_status(launch_topk(logits, gate_bias, T, E, k, topk_idx, topk_w, stream));
+    return hip_status(launch_topk(part, r.ksplit, (long long)T * E, gate_bias, T, E, k, logits, topk_idx,
+                                  topk_w, stream));
+}
+
+moe_status check_route(moe_dtype x_dt, int T, int H, int E, int k) {
+    if (T < 0 || H < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+    if (!act_ok(x_dt)) return MOE_ERR_UNSUPPORTED;
+    if (E > 1024 || k > 64 || E % 4 || H % 32) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+}  // namespace
+
+size_t moe_route_workspace_bytes(int T, int H, int E) {
+    if (T < 0 || H < 1 || E < 1) return 0;
+    return align_up(route_ws_bytes(T, H, E));
+}
+
+moe_status moe_route(const void *X, moe_dtype x_dt, const void *Wg, const float *gate_bias, int T,
+                     int H, int E, int k, float *logits, int32_t *topk_idx, float *topk_w, void *ws,
+                     size_t ws_bytes, hipStream_t stream) {
+    moe_status st = check_route(x_dt, T, H, E, k);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!X || !Wg || !logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+    const size_t need = route_ws_bytes(T, H, E);
+    if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return route_impl(X, x_dt, Wg, gate_bias, T, H, E, k, logits, topk_idx, topk_w, ws, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -331,7 +381,7 @@ moe_status check_desc(const moe_layer_desc *d) {
 struct ForwardWs {
     float *logits, *w;
     int32_t *idx, *counts, *offsets, *row_src, *assign_row;
-    void *perm_ws;
+    void *perm_ws, *route_ws;
     FfnWs ffn;
     FfnPlan plan, plan_s;
     size_t bytes;
@@ -349,6 +399,7 @@ ForwardWs carve_forward(const moe_layer_desc *d, int T, void *base) {
     f.row_src = static_cast<int32_t *>(c.take(sizeof(int32_t) * (size_t)A));
     f.assign_row = static_cast<int32_t *>(c.take(sizeof(int32_t) * (size_t)A));
     f.perm_ws = c.take(permute_ws_bytes(A, d->E));
+    f.route_ws = c.take(route_ws_bytes(T, d->H, d->E));
     f.plan = plan_ffn(A, d->E, d->H, d->F, d->w_dt, d->path);
     if (d->Fs > 0) {
         // routed and shared rows share one Yp buffer, so both use one format
@@ -407,7 +458,8 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
 
     MOE_TRY(mark(MOE_EV_START));
     // 1. router
-    st = moe_route(X, d->act_dt, d->Wg, d->gate_bias, T, H, E, d->k, f.logits, f.idx, f.w, stream);
+    st = route_impl(X, d->act_dt, d->Wg, d->gate_bias, T, H, E, d->k, f.logits, f.idx, f.w, f.route_ws,
+                    stream);
     if (st != MOE_OK) return st;
     MOE_TRY(mark(MOE_EV_ROUTE));
     // 2. dispatch (the row gather is fused into the gate/up GEMM's loads)

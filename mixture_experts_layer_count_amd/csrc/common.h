@@ -32,8 +32,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     u += 0x7fffu + ((u >> 16) & 1u);
     return u >> 16;
 }
+// Two f32 -> packed bf16 pair (round to nearest even: v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // silu(z) = z / (1 + e^-z)
@@ -80,8 +84,7 @@ enum WType { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
 // Row-streaming grouped GEMM (small rows per group).
 //   C[r, n] = sum_k A(r)[k] * B_g[k, n]   (PLAIN)      or
 //   C[r, n] = silu(A(r) B0_g)[n] * (A(r) B1_g)[n]   (SWIGLU)
-// A(r) = A[row_src[r]/gk] if row_src else A[r]; rows >= n_direct map to
-// A[r - n_direct] (used for the identity-gather shared expert).
+// A(r) = A[row_src[r]/gk] if row_src else A[r].
 struct GemmProblem {
     const void *A;
     const int32_t *row_src;
@@ -117,9 +120,11 @@ bool tiled_gemm_supports(WType wt, int N, int K);
 hipError_t launch_build_tiles(const int32_t *offsets, int G, int bm, int32_t *tiles,
                               int32_t *n_tiles, hipStream_t s);
 
-// Router top-k over fp32 logits (bias added in place first when given).
-hipError_t launch_topk(float *logits, const float *bias, int T, int E, int k,
-                       int32_t *idx, float *w, hipStream_t s);
+// Router top-k. logits[t,e] = sum_s part[s][t][e] (s ascending) + bias[e] is
+// written to `logits`, then the k best are selected. part may alias logits
+// when nsplit == 1.
+hipError_t launch_topk(const float *part, int nsplit, long long split_stride, const float *bias,
+                       int T, int E, int k, float *logits, int32_t *idx, float *w, hipStream_t s);
 
 // Permutation (count / scan / scatter) and optional row gather.
 size_t permute_ws_bytes(int A, int E);

@@ -26,11 +26,14 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
 }
 
 template <int NPER>
-__global__ __launch_bounds__(kWaves * 64) void topk_kernel(float *logits, const float *bias, int T,
-                                                           int E, int k, int32_t *idx, float *w) {
+__global__ __launch_bounds__(kWaves * 64) void topk_kernel(const float *part, int nsplit,
+                                                           long long split_stride, const float *bias,
+                                                           int T, int E, int k, float *logits,
+                                                           int32_t *idx, float *w) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (t >= T) return;
+    const float *prow = part + (long long)t * E;
     float *row = logits + (long long)t * E;
 
     float v[NPER];   // logit used for ranking (NaN -> -inf)
@@ -41,11 +44,10 @@ __global__ __launch_bounds__(kWaves * 64) void topk_kernel(float *logits, const 
         const int e = lane + 64 * i;
         float x = -INFINITY;
         if (e < E) {
-            x = row[e];
-            if (bias) {
-                x += bias[e];
-                row[e] = x;
-            }
+            x = prow[e];
+            for (int sp = 1; sp < nsplit; ++sp) x += prow[sp * split_stride + e];
+            if (bias) x += bias[e];
+            row[e] = x;
         }
         raw[i] = x;
         v[i] = (x != x) ? -INFINITY : x;
@@ -101,22 +103,21 @@ __global__ __launch_bounds__(kWaves * 64) void topk_kernel(float *logits, const 
 
 }  // namespace
 
-hipError_t launch_topk(float *logits, const float *bias, int T, int E, int k, int32_t *idx,
-                       float *w, hipStream_t s) {
+hipError_t launch_topk(const float *part, int nsplit, long long split_stride, const float *bias,
+                       int T, int E, int k, float *logits, int32_t *idx, float *w, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     if (E < 1 || E > 1024 || k < 1 || k > E || k > 64) return hipErrorInvalidValue;
     const dim3 grid((T + kWaves - 1) / kWaves), block(kWaves * 64);
     const int nper = (E + 63) / 64;
-    if (nper <= 1)
-        hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, bias, T, E, k, idx, w);
-    else if (nper <= 2)
-        hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, bias, T, E, k, idx, w);
-    else if (nper <= 4)
-        hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, bias, T, E, k, idx, w);
-    else if (nper <= 8)
-        hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, bias, T, E, k, idx, w);
-    else
-        hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, bias, T, E, k, idx, w);
+#define MOE_TOPK(N)                                                                                 \
+    hipLaunchKernelGGL(topk_kernel<N>, grid, block, 0, s, part, nsplit, split_stride, bias, T, E, k, \
+                       logits, idx, w)
+    if (nper <= 1) MOE_TOPK(1);
+    else if (nper <= 2) MOE_TOPK(2);
+    else if (nper <= 4) MOE_TOPK(4);
+    else if (nper <= 8) MOE_TOPK(8);
+    else MOE_TOPK(16);
+#undef MOE_TOPK
     return hipGetLastError();
 }
 

@@ -48,14 +48,17 @@ def test_status_strings():
 def test_route_validation():
     lib = moe.lib()
     # k > E, k < 1, bad dtype, E not a multiple of 4, H not a multiple of 32
-    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 8, 9, FAKE, FAKE, FAKE, None) == INVALID
-    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 8, 0, FAKE, FAKE, FAKE, None) == INVALID
-    assert lib.moe_route(FAKE, FP8, FAKE, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None) == UNSUPPORTED
-    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 6, 2, FAKE, FAKE, FAKE, None) == UNSUPPORTED
-    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 48, 8, 2, FAKE, FAKE, FAKE, None) == UNSUPPORTED
-    assert lib.moe_route(None, BF16, FAKE, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 8, 9, FAKE, FAKE, FAKE, None, 0, None) == INVALID
+    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 8, 0, FAKE, FAKE, FAKE, None, 0, None) == INVALID
+    assert lib.moe_route(FAKE, FP8, FAKE, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
+    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 6, 2, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
+    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 48, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
+    assert lib.moe_route(None, BF16, FAKE, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == INVALID
+    # split-K partials need a workspace
+    assert lib.moe_route_workspace_bytes(16, 4096, 8) > 0
+    assert lib.moe_route(FAKE, BF16, FAKE, None, 16, 4096, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == WS_SMALL
     # T == 0: nothing to do, nothing launched
-    assert lib.moe_route(None, BF16, None, None, 0, 64, 8, 2, None, None, None, None) == OK
+    assert lib.moe_route(None, BF16, None, None, 0, 64, 8, 2, None, None, None, None, 0, None) == OK
 
 
 def test_permute_validation_and_workspace():
@@ -117,6 +120,10 @@ def test_forward_validation_and_workspace():
     n16 = lib.moe_forward_workspace_bytes(ctypes.byref(d), 16)
     n4k = lib.moe_forward_workspace_bytes(ctypes.byref(d), 4096)
     assert 0 < n16 < n4k
+    # empty batches size their workspace without dividing by zero
+    assert lib.moe_forward_workspace_bytes(ctypes.byref(d), 0) >= 0
+    assert lib.moe_route_workspace_bytes(0, 4096, 8) == 0
+    assert lib.moe_grouped_ffn_workspace_bytes(0, 8, 512, 1024, BF16, BF16, 0) >= 0
     bad = _desc(k=9)
     assert lib.moe_forward_workspace_bytes(ctypes.byref(bad), 16) == 0
     assert lib.moe_forward(ctypes.byref(bad), FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None, None, None) == INVALID

@@ -119,7 +119,8 @@ def test_permute(T, k, E, mode):
 # grouped FFN and combine
 # ----------------------------------------------------------------------------
 
-FFN_CASES = [(n, p) for n in MINI_CONFIGS for p in ("gemv",)]
+FFN_CASES = [(n, p) for n in MINI_CONFIGS for p in ("gemv", "tiled")
+             if not (p == "tiled" and MINI_CONFIGS[n].w == "f32")]
 
 
 @pytest.mark.parametrize("name,path", FFN_CASES)
