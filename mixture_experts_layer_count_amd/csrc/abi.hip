@@ -71,7 +71,7 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path) 
     if (path == MOE_PATH_TILED) p.tiled = can_tile;
     else if (path == MOE_PATH_GEMV) p.tiled = false;
     else p.tiled = can_tile && (long long)M >= 48LL * G;
-    p.bm = p.tiled ? tiled_gemm_bm() : kGemvBM;
+    p.bm = p.tiled ? tiled_gemm_bm(M, G) : kGemvBM;
     p.ksplit2 = 1;
     p.kchunk2 = F;
     if (!p.tiled) {
@@ -90,7 +90,7 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path) 
 }
 
 struct FfnWs {
-    int32_t *tiles, *n_tiles;
+    int32_t *tiles, *n_tiles, *group_tile_start;
     void *h;       // [M + extra_rows][F]
     void *part;    // [ksplit][rows][H] fp32 partials (row-streaming path)
 };
@@ -100,17 +100,21 @@ size_t ffn_ws_carve(Carver &c, FfnWs &w, const FfnPlan &p, int M, int G, int H, 
     const long long max_tiles = (M + p.bm - 1) / p.bm + G;
     w.tiles = static_cast<int32_t *>(c.take(sizeof(int32_t) * 2 * max_tiles));
     w.n_tiles = static_cast<int32_t *>(c.take(sizeof(int32_t)));
+    w.group_tile_start = static_cast<int32_t *>(c.take(sizeof(int32_t) * (G + 1)));
     const int hw = F > Fs ? F : Fs;
     w.h = c.take(dt_size(act_dt) * (size_t)(M + extra_rows) * hw);
     w.part = want_part ? c.take(sizeof(float) * (size_t)p.ksplit2 * (M + extra_rows) * H) : nullptr;
     return c.used;
 }
 
-GemmProblem gate_up_problem(const void *X, const int32_t *row_src, int gk, const int32_t *tiles,
-                            const int32_t *n_tiles, const int32_t *offsets, int max_tiles, int M,
-                            int H, int F, const void *W1, const void *W3, const float *S1,
-                            const float *S3, void *h) {
+GemmProblem gate_up_problem(const void *X, const int32_t *row_src, int gk, const FfnWs *ws,
+                            const int32_t *offsets, int G, int max_tiles, int M, int H, int F,
+                            const void *W1, const void *W3, const float *S1, const float *S3, void *h) {
     GemmProblem g{};
+    const int32_t *tiles = ws ? ws->tiles : nullptr;
+    const int32_t *n_tiles = ws ? ws->n_tiles : nullptr;
+    g.group_tile_start = ws ? ws->group_tile_start : nullptr;
+    g.G = G;
     g.A = X;
     g.row_src = row_src;
     g.gk = gk;
@@ -136,10 +140,14 @@ GemmProblem gate_up_problem(const void *X, const int32_t *row_src, int gk, const
     return g;
 }
 
-GemmProblem down_problem(const void *h, const int32_t *tiles, const int32_t *n_tiles,
-                         const int32_t *offsets, int max_tiles, int M, int H, int F, const void *W2,
-                         const float *S2, void *C, long long split_stride, int ksplit, int kchunk) {
+GemmProblem down_problem(const void *h, const FfnWs *ws, const int32_t *offsets, int G, int max_tiles,
+                         int M, int H, int F, const void *W2, const float *S2, void *C,
+                         long long split_stride, int ksplit, int kchunk) {
     GemmProblem g{};
+    const int32_t *tiles = ws ? ws->tiles : nullptr;
+    const int32_t *n_tiles = ws ? ws->n_tiles : nullptr;
+    g.group_tile_start = ws ? ws->group_tile_start : nullptr;
+    g.G = G;
     g.A = h;
     g.row_src = nullptr;
     g.gk = 1;
@@ -166,7 +174,7 @@ GemmProblem down_problem(const void *h, const int32_t *tiles, const int32_t *n_t
 
 hipError_t run_gemm(const FfnPlan &p, const GemmProblem &g, WType wt, bool swiglu, bool out_bf16,
                     hipStream_t s) {
-    return p.tiled ? launch_tiled_gemm(g, wt, swiglu, out_bf16, s)
+    return p.tiled ? launch_tiled_gemm(g, wt, swiglu, out_bf16, p.bm, s)
                    : launch_stream_gemm(g, wt, swiglu, out_bf16, s);
 }
 
@@ -323,18 +331,16 @@ moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M
     const bool bf = act_dt == MOE_BF16;
     const int max_tiles = (M + p.bm - 1) / p.bm + G;
 
-    MOE_TRY(launch_build_tiles(offsets, G, p.bm, w.tiles, w.n_tiles, stream));
-    GemmProblem g1 = gate_up_problem(Xin, row_src, k, w.tiles, w.n_tiles, offsets, max_tiles, M, H, F,
-                                     W1, W3, S1, S3, w.h);
+    MOE_TRY(launch_build_tiles(offsets, G, p.bm, w.tiles, w.n_tiles, w.group_tile_start, stream));
+    GemmProblem g1 = gate_up_problem(Xin, row_src, k, &w, offsets, G, max_tiles, M, H, F, W1, W3, S1, S3, w.h);
     MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
     if (p.tiled) {
-        GemmProblem g2 = down_problem(w.h, w.tiles, w.n_tiles, offsets, max_tiles, M, H, F, W2, S2, Yp,
-                                      0, 1, F);
+        GemmProblem g2 = down_problem(w.h, &w, offsets, G, max_tiles, M, H, F, W2, S2, Yp, 0, 1, F);
         MOE_TRY(run_gemm(p, g2, wt, false, bf, stream));
     } else {
         const long long split_stride = (long long)M * H;
-        GemmProblem g2 = down_problem(w.h, w.tiles, w.n_tiles, offsets, max_tiles, M, H, F, W2, S2,
-                                      w.part, split_stride, p.ksplit2, p.kchunk2);
+        GemmProblem g2 = down_problem(w.h, &w, offsets, G, max_tiles, M, H, F, W2, S2, w.part, split_stride,
+                                      p.ksplit2, p.kchunk2);
         MOE_TRY(run_gemm(p, g2, wt, false, false, stream));
         MOE_TRY(launch_reduce_splits(static_cast<const float *>(w.part), split_stride, p.ksplit2, M, H,
                                      act_dt, Yp, stream));
@@ -415,6 +421,7 @@ ForwardWs carve_forward(const moe_layer_desc *d, int T, void *base) {
     const long long max_tiles = (A + f.plan.bm - 1) / f.plan.bm + d->E;
     f.ffn.tiles = static_cast<int32_t *>(c.take(sizeof(int32_t) * 2 * max_tiles));
     f.ffn.n_tiles = static_cast<int32_t *>(c.take(sizeof(int32_t)));
+    f.ffn.group_tile_start = static_cast<int32_t *>(c.take(sizeof(int32_t) * (d->E + 1)));
     const int hw = d->F > d->Fs ? d->F : d->Fs;
     f.ffn.h = c.take(dt_size(d->act_dt) * (size_t)(A + extra) * hw);
     if (f.plan.tiled)
@@ -468,17 +475,17 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     // 3. expert FFN
     const FfnPlan &p = f.plan;
     const int max_tiles = (A + p.bm - 1) / p.bm + E;
-    MOE_TRY(launch_build_tiles(f.offsets, E, p.bm, f.ffn.tiles, f.ffn.n_tiles, stream));
+    MOE_TRY(launch_build_tiles(f.offsets, E, p.bm, f.ffn.tiles, f.ffn.n_tiles, f.ffn.group_tile_start, stream));
     MOE_TRY(mark(MOE_EV_SCHEDULE));
-    GemmProblem g1 = gate_up_problem(X, f.row_src, d->k, f.ffn.tiles, f.ffn.n_tiles, f.offsets, max_tiles,
-                                     A, H, F, d->W1, d->W3, d->S1, d->S3, f.ffn.h);
+    GemmProblem g1 = gate_up_problem(X, f.row_src, d->k, &f.ffn, f.offsets, E, max_tiles, A, H, F, d->W1,
+                                     d->W3, d->S1, d->S3, f.ffn.h);
     MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
     MOE_TRY(mark(MOE_EV_GATE_UP));
     const size_t hb = dt_size(d->act_dt);
     void *h_s = static_cast<char *>(f.ffn.h) + hb * (size_t)A * (d->F > d->Fs ? d->F : d->Fs);
     if (d->Fs > 0) {
-        GemmProblem gs = gate_up_problem(X, nullptr, 1, nullptr, nullptr, nullptr, 0, T, H, d->Fs, d->Ws1,
-                                         d->Ws3, d->Ss1, d->Ss3, h_s);
+        GemmProblem gs = gate_up_problem(X, nullptr, 1, nullptr, nullptr, 1, 0, T, H, d->Fs, d->Ws1, d->Ws3,
+                                         d->Ss1, d->Ss3, h_s);
         MOE_TRY(run_gemm(f.plan_s, gs, wt, true, bf, stream));
     }
     MOE_TRY(mark(MOE_EV_SHARED_GATE_UP));
@@ -488,14 +495,14 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     int nsplit = 1;
     moe_dtype yp_dt = d->act_dt;
     if (p.tiled) {
-        GemmProblem g2 = down_problem(f.ffn.h, f.ffn.tiles, f.ffn.n_tiles, f.offsets, max_tiles, A, H, F,
-                                      d->W2, d->S2, f.ffn.part, 0, 1, F);
+        GemmProblem g2 = down_problem(f.ffn.h, &f.ffn, f.offsets, E, max_tiles, A, H, F, d->W2, d->S2,
+                                      f.ffn.part, 0, 1, F);
         MOE_TRY(run_gemm(p, g2, wt, false, bf, stream));
         MOE_TRY(mark(MOE_EV_DOWN));
         if (d->Fs > 0) {
             void *Sp = static_cast<char *>(f.ffn.part) + hb * (size_t)A * H;
-            GemmProblem g2s = down_problem(h_s, nullptr, nullptr, nullptr, 0, T, H, d->Fs, d->Ws2, d->Ss2, Sp,
-                                           0, 1, d->Fs);
+            GemmProblem g2s = down_problem(h_s, nullptr, nullptr, 1, 0, T, H, d->Fs, d->Ws2, d->Ss2, Sp, 0, 1,
+                                           d->Fs);
             MOE_TRY(run_gemm(f.plan_s, g2s, wt, false, bf, stream));
             S = Sp;
         }
@@ -510,13 +517,13 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
             int c = (K + nsplit - 1) / nsplit;
             return (c + gran - 1) / gran * gran;
         };
-        GemmProblem g2 = down_problem(f.ffn.h, f.ffn.tiles, f.ffn.n_tiles, f.offsets, max_tiles, A, H, F,
-                                      d->W2, d->S2, f.ffn.part, split_stride, nsplit, chunk_for(F));
+        GemmProblem g2 = down_problem(f.ffn.h, &f.ffn, f.offsets, E, max_tiles, A, H, F, d->W2, d->S2,
+                                      f.ffn.part, split_stride, nsplit, chunk_for(F));
         MOE_TRY(run_gemm(p, g2, wt, false, false, stream));
         MOE_TRY(mark(MOE_EV_DOWN));
         if (d->Fs > 0) {
             float *Sp = static_cast<float *>(f.ffn.part) + (size_t)A * H;
-            GemmProblem g2s = down_problem(h_s, nullptr, nullptr, nullptr, 0, T, H, d->Fs, d->Ws2, d->Ss2, Sp,
+            GemmProblem g2s = down_problem(h_s, nullptr, nullptr, 1, 0, T, H, d->Fs, d->Ws2, d->Ss2, Sp,
                                            split_stride, nsplit, chunk_for(d->Fs));
             MOE_TRY(run_gemm(f.plan_s, g2s, wt, false, false, stream));
             S = Sp;

@@ -93,6 +93,8 @@ struct GemmProblem {
     const int32_t *tiles;     // (group, row0) pairs, NULL: one group of M rows
     const int32_t *n_tiles;   // device count of tiles
     const int32_t *offsets;   // [G+1]; NULL with tiles == NULL
+    const int32_t *group_tile_start;  // [G+1] first tile of each group (tiled kernel)
+    int G;                    // number of groups in the tile list
     int max_tiles;            // host upper bound on tiles
     int M, N, K;
     const void *B0, *B1;      // [G][K][N]
@@ -110,15 +112,18 @@ hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool 
                               hipStream_t s);
 
 // LDS-tiled grouped GEMM (many rows per group). Same problem statement;
-// ksplit must be 1. Returns hipErrorInvalidValue for unsupported shapes.
-hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,
+// ksplit must be 1; bm (rows per tile) must be tiled_gemm_bm(avg rows) and
+// the tile list must have been built with it. Returns hipErrorInvalidValue
+// for unsupported shapes.
+hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16, int bm,
                              hipStream_t s);
-int tiled_gemm_bm();   // rows per tile of the tiled kernel
+int tiled_gemm_bm(long long rows, int groups);  // rows per tile for this row distribution
 bool tiled_gemm_supports(WType wt, int N, int K);
 
-// Tile list (group, row0) for groups of rows given by offsets, bm rows per tile.
+// Tile list (group, row0) for groups of rows given by offsets, bm rows per
+// tile, and (optional) the first tile index of every group, [G+1].
 hipError_t launch_build_tiles(const int32_t *offsets, int G, int bm, int32_t *tiles,
-                              int32_t *n_tiles, hipStream_t s);
+                              int32_t *n_tiles, int32_t *group_tile_start, hipStream_t s);
 
 // Router top-k. logits[t,e] = sum_s part[s][t][e] (s ascending) + bias[e] is
 // written to `logits`, then the k best are selected. part may alias logits

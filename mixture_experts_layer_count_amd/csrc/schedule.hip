@@ -12,9 +12,9 @@ namespace moe {
 namespace {
 
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *offsets, int G, int bm,
-                                                           int32_t *tiles, int32_t *n_tiles) {
+                                                           int32_t *tiles, int32_t *n_tiles,
+                                                           int32_t *group_tile_start) {
     __shared__ int scan_lds[16];
-    __shared__ int base_lds;
     int carry = 0;
     // groups in rounds of 1024; each thread emits its group's tiles
     for (int g0 = 0; g0 < G; g0 += 1024) {
@@ -27,6 +27,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *offset
         }
         int total = 0;
         const int first = block_exclusive_scan(n, scan_lds, &total) + carry;
+        if (g < G && group_tile_start) group_tile_start[g] = first;
         for (int i = 0; i < n; ++i) {
             tiles[2 * (first + i)] = g;
             tiles[2 * (first + i) + 1] = lo + i * bm;
@@ -34,17 +35,18 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *offset
         carry += total;
     }
     if (threadIdx.x == 0) {
-        base_lds = carry;
         *n_tiles = carry;
+        if (group_tile_start) group_tile_start[G] = carry;
     }
 }
 
 }  // namespace
 
 hipError_t launch_build_tiles(const int32_t *offsets, int G, int bm, int32_t *tiles,
-                              int32_t *n_tiles, hipStream_t s) {
+                              int32_t *n_tiles, int32_t *group_tile_start, hipStream_t s) {
     if (G < 1 || bm < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, G, bm, tiles, n_tiles);
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, G, bm, tiles, n_tiles,
+                       group_tile_start);
     return hipGetLastError();
 }
 

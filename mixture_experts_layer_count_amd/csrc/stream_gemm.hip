@@ -21,8 +21,8 @@
 //    MFMA, and each 128-deep K block's partial sum is multiplied by its fp32
 //    block scale before it joins the accumulator.
 //  * f32 weights use v_mfma_f32_16x16x4_f32 with no transpose.
-//  * the next K step's weight loads are issued before the current step's
-//    MFMAs (register double buffering) to keep HBM requests in flight.
+//  * a ring of register stages keeps the weight, token and scale loads of
+//    the next K steps in flight while the current step is multiplied.
 #include "common.h"
 
 namespace moe {
@@ -141,11 +141,25 @@ __device__ __forceinline__ void load_a(AFrag<WT> &f, const typename WTraits<WT>:
     }
 }
 
+#ifndef MOE_STREAM_DEPTH
+#define MOE_STREAM_DEPTH 3
+#endif
+constexpr int kDepth = MOE_STREAM_DEPTH;  // K steps whose loads are in flight
+
+// One K step's operands for one lane: weight rows of both matrices, the token
+// fragment and (fp8) the block scales of the step's 128-deep K block.
+template <int WT, bool SWIGLU>
+struct Stage {
+    typename WTraits<WT>::raw w0[8];
+    typename WTraits<WT>::raw w1[SWIGLU ? 8 : 1];
+    AFrag<WT> a;
+    float s0, s1;
+};
+
 template <int WT, bool SWIGLU, bool OUT_BF16>
 __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p, int n_slices) {
     typedef typename WTraits<WT>::elem E;
     typedef typename WTraits<WT>::act AT;
-    typedef typename WTraits<WT>::raw R;
 
     const int lane = threadIdx.x & 63;
     const long long wave = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -171,18 +185,33 @@ __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p,
     const bool colok = col < p.N;
     const int kbeg = split * p.kchunk;
     const int kend = min(p.K, kbeg + p.kchunk);
+    const int nsteps = kend > kbeg ? (kend - kbeg) / 32 : 0;
 
     // this lane's activation row (MFMA A operand row = lane & 15)
     const int r = row0 + (lane & 15);
     const bool rok = r < row_end;
     long long arow = 0;
     if (rok) arow = p.row_src ? (long long)(p.row_src[r] / p.gk) : (long long)r;
-    const AT *Ap = reinterpret_cast<const AT *>(p.A) + arow * p.lda + 8 * kg;
+    const AT *Ap = reinterpret_cast<const AT *>(p.A) + arow * p.lda + 8 * kg + kbeg;
 
     const long long ldb = p.N;
-    const E *B0 = reinterpret_cast<const E *>(p.B0) + (long long)g * p.b_stride + col + (8 * kg) * ldb;
-    const E *B1 = SWIGLU ? reinterpret_cast<const E *>(p.B1) + (long long)g * p.b_stride + col + (8 * kg) * ldb
+    const E *B0 = reinterpret_cast<const E *>(p.B0) + (long long)g * p.b_stride + col + (8 * kg + kbeg) * ldb;
+    const E *B1 = SWIGLU ? reinterpret_cast<const E *>(p.B1) + (long long)g * p.b_stride + col +
+                               (8 * kg + kbeg) * ldb
                          : nullptr;
+    const long long sbase = (long long)g * p.s_stride + (col >> 7);
+    const int sstride = p.N >> 7;
+
+    auto issue = [&](Stage<WT, SWIGLU> &st, int step) {
+        load_rows<WT>(st.w0, B0 + (long long)step * 32 * ldb, ldb, colok);
+        if constexpr (SWIGLU) load_rows<WT>(st.w1, B1 + (long long)step * 32 * ldb, ldb, colok);
+        load_a<WT>(st.a, Ap + step * 32, rok);
+        if constexpr (WT == W_FP8) {
+            const long long si = sbase + (long long)((kbeg + step * 32) >> 7) * sstride;
+            st.s0 = colok ? p.S0[si] : 0.0f;
+            st.s1 = (SWIGLU && colok) ? p.S1[si] : 0.0f;
+        }
+    };
 
     f32x4 acc0[kVec], acc1[kVec];
     f32x4 tmp0[kVec], tmp1[kVec];  // fp8: current 128-deep K block
@@ -194,53 +223,42 @@ __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p,
         tmp1[c] = f32x4{};
     }
 
-    R w0[8], w1[8];
-    AFrag<WT> af;
-    if (kbeg < kend) {
-        load_rows<WT>(w0, B0 + (long long)kbeg * ldb, ldb, colok);
-        if (SWIGLU) load_rows<WT>(w1, B1 + (long long)kbeg * ldb, ldb, colok);
-        load_a<WT>(af, Ap + kbeg, rok);
-    }
-    for (int k0 = kbeg; k0 < kend; k0 += 32) {
-        // prefetch the next K step while this one is multiplied
-        R n0[8], n1[8];
-        AFrag<WT> naf;
-        const bool more = k0 + 32 < kend;
-        if (more) {
-            load_rows<WT>(n0, B0 + (long long)(k0 + 32) * ldb, ldb, colok);
-            if (SWIGLU) load_rows<WT>(n1, B1 + (long long)(k0 + 32) * ldb, ldb, colok);
-            load_a<WT>(naf, Ap + k0 + 32, rok);
-        }
+    auto consume = [&](Stage<WT, SWIGLU> &st, int step) {
         if constexpr (WT == W_FP8) {
-            mma_step<WT>(tmp0, w0, &af);
-            if (SWIGLU) mma_step<WT>(tmp1, w1, &af);
-            if ((k0 & 127) == 96 || !more) {
+            mma_step<WT>(tmp0, st.w0, &st.a);
+            if constexpr (SWIGLU) mma_step<WT>(tmp1, st.w1, &st.a);
+            const int k0 = kbeg + step * 32;
+            if ((k0 & 127) == 96 || step + 1 == nsteps) {
                 // end of a 128-deep scale block: acc += block partial * scale
-                const long long sidx = (long long)g * p.s_stride + (long long)(k0 >> 7) * (p.N >> 7) + (col >> 7);
-                const float s0 = colok ? p.S0[sidx] : 0.0f;
-                const float s1 = (SWIGLU && colok) ? p.S1[sidx] : 0.0f;
 #pragma unroll
                 for (int c = 0; c < kVec; ++c) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        acc0[c][i] = fmaf(tmp0[c][i], s0, acc0[c][i]);
-                        if (SWIGLU) acc1[c][i] = fmaf(tmp1[c][i], s1, acc1[c][i]);
+                        acc0[c][i] = fmaf(tmp0[c][i], st.s0, acc0[c][i]);
+                        if (SWIGLU) acc1[c][i] = fmaf(tmp1[c][i], st.s1, acc1[c][i]);
                     }
                     tmp0[c] = f32x4{};
                     tmp1[c] = f32x4{};
                 }
             }
         } else {
-            mma_step<WT>(acc0, w0, &af);
-            if (SWIGLU) mma_step<WT>(acc1, w1, &af);
+            mma_step<WT>(acc0, st.w0, &st.a);
+            if constexpr (SWIGLU) mma_step<WT>(acc1, st.w1, &st.a);
         }
-        if (more) {
+    };
+
+    // ring of kDepth stages: step j lives in slot j % kDepth
+    Stage<WT, SWIGLU> ring[kDepth];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                w0[i] = n0[i];
-                if (SWIGLU) w1[i] = n1[i];
-            }
-            af = naf;
+    for (int d = 0; d < kDepth - 1; ++d)
+        if (d < nsteps) issue(ring[d], d);
+    for (int s0 = 0; s0 < nsteps; s0 += kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            const int step = s0 + d;
+            const int ahead = step + kDepth - 1;
+            if (ahead < nsteps) issue(ring[(d + kDepth - 1) % kDepth], ahead);
+            if (step < nsteps) consume(ring[d], step);
         }
     }
 
