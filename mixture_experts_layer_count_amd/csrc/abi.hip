@@ -91,38 +91,54 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path) 
 
 struct FfnWs {
     int32_t *tiles, *n_tiles, *group_tile_start;
-    void *h;       // [M + extra_rows][F]
-    void *part;    // [ksplit][rows][H] fp32 partials (row-streaming path)
+    void *h;     // [rows][hw] SwiGLU activations
+    void *part;  // Yp: [ksplit][rows][H] fp32 (row-streaming) or [rows][H] act_dt (tiled)
 };
 
-size_t ffn_ws_carve(Carver &c, FfnWs &w, const FfnPlan &p, int M, int G, int H, int F,
-                    int extra_rows, int Fs, moe_dtype act_dt, bool want_part) {
-    const long long max_tiles = (M + p.bm - 1) / p.bm + G;
-    w.tiles = static_cast<int32_t *>(c.take(sizeof(int32_t) * 2 * max_tiles));
+// Weights of the optional extra group: the always-on shared expert run in
+// the same grouped launch as the routed experts (same width F).
+struct ExtraGroup {
+    int rows = 0;
+    const void *W1 = nullptr, *W3 = nullptr, *W2 = nullptr;
+    const float *S1 = nullptr, *S3 = nullptr, *S2 = nullptr;
+};
+
+long long max_tiles_for(long long rows, int groups, int bm) { return (rows + bm - 1) / bm + groups; }
+
+size_t ffn_ws_carve(Carver &c, FfnWs &w, const FfnPlan &p, int rows, int groups, int H, int hw,
+                    moe_dtype act_dt) {
+    const long long max_tiles = max_tiles_for(rows, groups, p.bm);
+    w.tiles = static_cast<int32_t *>(c.take(sizeof(int32_t) * 4 * max_tiles));
     w.n_tiles = static_cast<int32_t *>(c.take(sizeof(int32_t)));
-    w.group_tile_start = static_cast<int32_t *>(c.take(sizeof(int32_t) * (G + 1)));
-    const int hw = F > Fs ? F : Fs;
-    w.h = c.take(dt_size(act_dt) * (size_t)(M + extra_rows) * hw);
-    w.part = want_part ? c.take(sizeof(float) * (size_t)p.ksplit2 * (M + extra_rows) * H) : nullptr;
+    w.group_tile_start = static_cast<int32_t *>(c.take(sizeof(int32_t) * (groups + 1)));
+    w.h = c.take(dt_size(act_dt) * (size_t)rows * hw);
+    w.part = p.tiled ? c.take(dt_size(act_dt) * (size_t)rows * H)
+                     : c.take(sizeof(float) * (size_t)p.ksplit2 * rows * H);
     return c.used;
 }
 
-GemmProblem gate_up_problem(const void *X, const int32_t *row_src, int gk, const FfnWs *ws,
-                            const int32_t *offsets, int G, int max_tiles, int M, int H, int F,
-                            const void *W1, const void *W3, const float *S1, const float *S3, void *h) {
+GemmProblem base_problem(const FfnWs *ws, int G, int max_tiles, const ExtraGroup &ex, int extra_row0) {
     GemmProblem g{};
-    const int32_t *tiles = ws ? ws->tiles : nullptr;
-    const int32_t *n_tiles = ws ? ws->n_tiles : nullptr;
+    g.tiles = ws ? ws->tiles : nullptr;
+    g.n_tiles = ws ? ws->n_tiles : nullptr;
     g.group_tile_start = ws ? ws->group_tile_start : nullptr;
-    g.G = G;
+    g.n_groups = G + (ex.rows > 0 ? 1 : 0);
+    g.max_tiles = max_tiles;
+    g.extra_group = ex.rows > 0 ? G : -1;
+    g.extra_row0 = extra_row0;
+    return g;
+}
+
+// h[r] = silu(x_r W1) * (x_r W3) for M rows (routed rows, then extra rows).
+GemmProblem gate_up_problem(const void *X, const int32_t *row_src, int gk, const FfnWs *ws, int G,
+                            int max_tiles, int M, int H, int F, const void *W1, const void *W3,
+                            const float *S1, const float *S3, const ExtraGroup &ex, int extra_row0,
+                            void *h) {
+    GemmProblem g = base_problem(ws, G, max_tiles, ex, extra_row0);
     g.A = X;
     g.row_src = row_src;
     g.gk = gk;
     g.lda = H;
-    g.tiles = tiles;
-    g.n_tiles = n_tiles;
-    g.offsets = offsets;
-    g.max_tiles = max_tiles;
     g.M = M;
     g.N = F;
     g.K = H;
@@ -132,6 +148,10 @@ GemmProblem gate_up_problem(const void *X, const int32_t *row_src, int gk, const
     g.S0 = S1;
     g.S1 = S3;
     g.s_stride = (long long)(H / 128) * (F / 128);
+    g.Bx0 = ex.W1;
+    g.Bx1 = ex.W3;
+    g.Sx0 = ex.S1;
+    g.Sx1 = ex.S3;
     g.C = h;
     g.ldc = F;
     g.c_split_stride = 0;
@@ -140,22 +160,15 @@ GemmProblem gate_up_problem(const void *X, const int32_t *row_src, int gk, const
     return g;
 }
 
-GemmProblem down_problem(const void *h, const FfnWs *ws, const int32_t *offsets, int G, int max_tiles,
-                         int M, int H, int F, const void *W2, const float *S2, void *C,
+// Yp[r] = h[r] W2 for M rows.
+GemmProblem down_problem(const void *h, const FfnWs *ws, int G, int max_tiles, int M, int H, int F,
+                         const void *W2, const float *S2, const ExtraGroup &ex, int extra_row0, void *C,
                          long long split_stride, int ksplit, int kchunk) {
-    GemmProblem g{};
-    const int32_t *tiles = ws ? ws->tiles : nullptr;
-    const int32_t *n_tiles = ws ? ws->n_tiles : nullptr;
-    g.group_tile_start = ws ? ws->group_tile_start : nullptr;
-    g.G = G;
+    GemmProblem g = base_problem(ws, G, max_tiles, ex, extra_row0);
     g.A = h;
     g.row_src = nullptr;
     g.gk = 1;
     g.lda = F;
-    g.tiles = tiles;
-    g.n_tiles = n_tiles;
-    g.offsets = offsets;
-    g.max_tiles = max_tiles;
     g.M = M;
     g.N = H;
     g.K = F;
@@ -164,12 +177,21 @@ GemmProblem down_problem(const void *h, const FfnWs *ws, const int32_t *offsets,
     g.b_stride = (long long)F * H;
     g.S0 = S2;
     g.s_stride = (long long)(F / 128) * (H / 128);
+    g.Bx0 = ex.W2;
+    g.Sx0 = ex.S2;
     g.C = C;
     g.ldc = H;
     g.c_split_stride = split_stride;
     g.ksplit = ksplit;
     g.kchunk = kchunk;
     return g;
+}
+
+// Split-K chunk (rounded to the kernel granule) for a fixed split count.
+int chunk_for(int K, int nsplit, moe_dtype w_dt) {
+    const int gran = w_dt == MOE_FP8_E4M3 ? 128 : 32;
+    int c = (K + nsplit - 1) / nsplit;
+    return (c + gran - 1) / gran * gran;
 }
 
 hipError_t run_gemm(const FfnPlan &p, const GemmProblem &g, WType wt, bool swiglu, bool out_bf16,
@@ -225,6 +247,7 @@ moe_status route_impl(const void *X, moe_dtype x_dt, const void *Wg, const float
     const RoutePlan r = plan_route(T, H, E);
     float *part = r.ksplit > 1 ? static_cast<float *>(ws) : logits;
     GemmProblem g{};
+    g.extra_group = -1;
     g.A = X;
     g.gk = 1;
     g.lda = H;
@@ -299,10 +322,11 @@ moe_status moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *co
 size_t moe_grouped_ffn_workspace_bytes(int M, int G, int H, int F, moe_dtype act_dt,
                                        moe_dtype w_dt, moe_ffn_path path) {
     if (M < 0 || G < 1 || H < 1 || F < 1) return 0;
-    const FfnPlan p = plan_ffn(M, G, H, F, w_dt, path);
+    FfnPlan p = plan_ffn(M, G, H, F, w_dt, path);
     Carver c(nullptr);
     FfnWs w{};
-    return ffn_ws_carve(c, w, p, M, G, H, F, 0, 0, act_dt, true);
+    p.tiled = false;  // the fp32 partial buffer is the larger of the two formats
+    return ffn_ws_carve(c, w, p, M, G, H, F, act_dt);
 }
 
 moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M,
@@ -323,23 +347,25 @@ moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M
         return MOE_ERR_INVALID_ARG;
     const FfnPlan p = plan_ffn(M, G, H, F, w_dt, path);
     if (path == MOE_PATH_TILED && !p.tiled) return MOE_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < moe_grouped_ffn_workspace_bytes(M, G, H, F, act_dt, w_dt, path))
+        return MOE_ERR_WORKSPACE_TOO_SMALL;
     Carver c(ws);
     FfnWs w{};
-    const size_t need = ffn_ws_carve(c, w, p, M, G, H, F, 0, 0, act_dt, true);
-    if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    ffn_ws_carve(c, w, p, M, G, H, F, act_dt);
     const WType wt = wtype(w_dt);
     const bool bf = act_dt == MOE_BF16;
-    const int max_tiles = (M + p.bm - 1) / p.bm + G;
+    const int max_tiles = (int)max_tiles_for(M, G, p.bm);
+    const ExtraGroup none{};
 
-    MOE_TRY(launch_build_tiles(offsets, G, p.bm, w.tiles, w.n_tiles, w.group_tile_start, stream));
-    GemmProblem g1 = gate_up_problem(Xin, row_src, k, &w, offsets, G, max_tiles, M, H, F, W1, W3, S1, S3, w.h);
+    MOE_TRY(launch_build_tiles(offsets, G, 0, p.bm, w.tiles, w.n_tiles, w.group_tile_start, stream));
+    GemmProblem g1 = gate_up_problem(Xin, row_src, k, &w, G, max_tiles, M, H, F, W1, W3, S1, S3, none, M, w.h);
     MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
     if (p.tiled) {
-        GemmProblem g2 = down_problem(w.h, &w, offsets, G, max_tiles, M, H, F, W2, S2, Yp, 0, 1, F);
+        GemmProblem g2 = down_problem(w.h, &w, G, max_tiles, M, H, F, W2, S2, none, M, Yp, 0, 1, F);
         MOE_TRY(run_gemm(p, g2, wt, false, bf, stream));
     } else {
         const long long split_stride = (long long)M * H;
-        GemmProblem g2 = down_problem(w.h, &w, offsets, G, max_tiles, M, H, F, W2, S2, w.part, split_stride,
+        GemmProblem g2 = down_problem(w.h, &w, G, max_tiles, M, H, F, W2, S2, none, M, w.part, split_stride,
                                       p.ksplit2, p.kchunk2);
         MOE_TRY(run_gemm(p, g2, wt, false, false, stream));
         MOE_TRY(launch_reduce_splits(static_cast<const float *>(w.part), split_stride, p.ksplit2, M, H,
@@ -390,6 +416,7 @@ struct ForwardWs {
     void *perm_ws, *route_ws;
     FfnWs ffn;
     FfnPlan plan, plan_s;
+    bool combined;  // shared expert runs as an extra group of the routed launches
     size_t bytes;
 };
 
@@ -407,8 +434,10 @@ ForwardWs carve_forward(const moe_layer_desc *d, int T, void *base) {
     f.perm_ws = c.take(permute_ws_bytes(A, d->E));
     f.route_ws = c.take(route_ws_bytes(T, d->H, d->E));
     f.plan = plan_ffn(A, d->E, d->H, d->F, d->w_dt, d->path);
-    if (d->Fs > 0) {
-        // routed and shared rows share one Yp buffer, so both use one format
+    f.combined = d->Fs > 0 && d->Fs == d->F;
+    if (d->Fs > 0 && !f.combined) {
+        // separate shared-expert launches; one Yp buffer holds routed rows
+        // then shared rows, so both use one format
         f.plan_s = plan_ffn(T, 1, d->H, d->Fs, d->w_dt, f.plan.tiled ? MOE_PATH_TILED : MOE_PATH_GEMV);
         if (f.plan_s.tiled != f.plan.tiled) {
             f.plan = plan_ffn(A, d->E, d->H, d->F, d->w_dt, MOE_PATH_GEMV);
@@ -416,18 +445,10 @@ ForwardWs carve_forward(const moe_layer_desc *d, int T, void *base) {
         }
         if (!f.plan.tiled && f.plan_s.ksplit2 > f.plan.ksplit2) f.plan.ksplit2 = f.plan_s.ksplit2;
     }
-    const int extra = d->Fs > 0 ? T : 0;
-    // h for routed rows then shared rows; Yp for routed rows then shared rows
-    const long long max_tiles = (A + f.plan.bm - 1) / f.plan.bm + d->E;
-    f.ffn.tiles = static_cast<int32_t *>(c.take(sizeof(int32_t) * 2 * max_tiles));
-    f.ffn.n_tiles = static_cast<int32_t *>(c.take(sizeof(int32_t)));
-    f.ffn.group_tile_start = static_cast<int32_t *>(c.take(sizeof(int32_t) * (d->E + 1)));
+    const int rows = A + (d->Fs > 0 ? T : 0);
+    const int groups = d->E + (f.combined ? 1 : 0);
     const int hw = d->F > d->Fs ? d->F : d->Fs;
-    f.ffn.h = c.take(dt_size(d->act_dt) * (size_t)(A + extra) * hw);
-    if (f.plan.tiled)
-        f.ffn.part = c.take(dt_size(d->act_dt) * (size_t)(A + extra) * d->H);
-    else
-        f.ffn.part = c.take(sizeof(float) * (size_t)f.plan.ksplit2 * (A + extra) * d->H);
+    ffn_ws_carve(c, f.ffn, f.plan, rows, groups, d->H, hw, d->act_dt);
     f.bytes = c.used;
     return f;
 }
@@ -462,6 +483,23 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     const int A = T * d->k, H = d->H, F = d->F, E = d->E;
     const WType wt = wtype(d->w_dt);
     const bool bf = d->act_dt == MOE_BF16;
+    const FfnPlan &p = f.plan;
+    const int rows = A + (d->Fs > 0 ? T : 0);
+    const size_t hb = dt_size(d->act_dt);
+    const int hw = d->F > d->Fs ? d->F : d->Fs;
+
+    ExtraGroup ex{};
+    if (f.combined) {
+        ex.rows = T;
+        ex.W1 = d->Ws1;
+        ex.W3 = d->Ws3;
+        ex.W2 = d->Ws2;
+        ex.S1 = d->Ss1;
+        ex.S3 = d->Ss3;
+        ex.S2 = d->Ss2;
+    }
+    const int M = A + ex.rows;  // rows of the grouped launches
+    const int max_tiles = (int)max_tiles_for(M, E + (f.combined ? 1 : 0), p.bm);
 
     MOE_TRY(mark(MOE_EV_START));
     // 1. router
@@ -472,62 +510,55 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     // 2. dispatch (the row gather is fused into the gate/up GEMM's loads)
     MOE_TRY(launch_permute(f.idx, A, E, f.counts, f.offsets, f.row_src, f.assign_row, f.perm_ws, stream));
     MOE_TRY(mark(MOE_EV_PERMUTE));
-    // 3. expert FFN
-    const FfnPlan &p = f.plan;
-    const int max_tiles = (A + p.bm - 1) / p.bm + E;
-    MOE_TRY(launch_build_tiles(f.offsets, E, p.bm, f.ffn.tiles, f.ffn.n_tiles, f.ffn.group_tile_start, stream));
+    // 3. expert FFN; with `combined` the shared expert is group E of the same launches
+    MOE_TRY(launch_build_tiles(f.offsets, E, ex.rows, p.bm, f.ffn.tiles, f.ffn.n_tiles, f.ffn.group_tile_start,
+                               stream));
     MOE_TRY(mark(MOE_EV_SCHEDULE));
-    GemmProblem g1 = gate_up_problem(X, f.row_src, d->k, &f.ffn, f.offsets, E, max_tiles, A, H, F, d->W1,
-                                     d->W3, d->S1, d->S3, f.ffn.h);
+    GemmProblem g1 = gate_up_problem(X, f.row_src, d->k, &f.ffn, E, max_tiles, M, H, F, d->W1, d->W3, d->S1,
+                                     d->S3, ex, A, f.ffn.h);
     MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
     MOE_TRY(mark(MOE_EV_GATE_UP));
-    const size_t hb = dt_size(d->act_dt);
-    void *h_s = static_cast<char *>(f.ffn.h) + hb * (size_t)A * (d->F > d->Fs ? d->F : d->Fs);
-    if (d->Fs > 0) {
-        GemmProblem gs = gate_up_problem(X, nullptr, 1, nullptr, nullptr, 1, 0, T, H, d->Fs, d->Ws1, d->Ws3,
-                                         d->Ss1, d->Ss3, h_s);
+    void *h_s = static_cast<char *>(f.ffn.h) + hb * (size_t)A * hw;
+    const ExtraGroup none{};
+    if (d->Fs > 0 && !f.combined) {
+        GemmProblem gs = gate_up_problem(X, nullptr, 1, nullptr, 1, 0, T, H, d->Fs, d->Ws1, d->Ws3, d->Ss1,
+                                         d->Ss3, none, 0, h_s);
         MOE_TRY(run_gemm(f.plan_s, gs, wt, true, bf, stream));
     }
     MOE_TRY(mark(MOE_EV_SHARED_GATE_UP));
-    const int rows = A + (d->Fs > 0 ? T : 0);
     const void *S = nullptr;
     long long split_stride = 0;
     int nsplit = 1;
     moe_dtype yp_dt = d->act_dt;
     if (p.tiled) {
-        GemmProblem g2 = down_problem(f.ffn.h, &f.ffn, f.offsets, E, max_tiles, A, H, F, d->W2, d->S2,
-                                      f.ffn.part, 0, 1, F);
+        GemmProblem g2 = down_problem(f.ffn.h, &f.ffn, E, max_tiles, M, H, F, d->W2, d->S2, ex, A, f.ffn.part,
+                                      0, 1, F);
         MOE_TRY(run_gemm(p, g2, wt, false, bf, stream));
         MOE_TRY(mark(MOE_EV_DOWN));
-        if (d->Fs > 0) {
-            void *Sp = static_cast<char *>(f.ffn.part) + hb * (size_t)A * H;
-            GemmProblem g2s = down_problem(h_s, nullptr, nullptr, 1, 0, T, H, d->Fs, d->Ws2, d->Ss2, Sp, 0, 1,
+        void *Sp = static_cast<char *>(f.ffn.part) + hb * (size_t)A * H;
+        if (d->Fs > 0 && !f.combined) {
+            GemmProblem g2s = down_problem(h_s, nullptr, 1, 0, T, H, d->Fs, d->Ws2, d->Ss2, none, 0, Sp, 0, 1,
                                            d->Fs);
             MOE_TRY(run_gemm(f.plan_s, g2s, wt, false, bf, stream));
-            S = Sp;
         }
+        if (d->Fs > 0) S = Sp;
     } else {
+        // every down projection writes all nsplit slices (an empty K range
+        // writes zeros), so combine sums a fixed number of slices
         split_stride = (long long)rows * H;
         nsplit = p.ksplit2;
         yp_dt = MOE_F32;
-        // both down projections write all nsplit slices (an empty K range
-        // writes zeros), so combine can sum a fixed number of slices
-        const int gran = d->w_dt == MOE_FP8_E4M3 ? 128 : 32;
-        auto chunk_for = [&](int K) {
-            int c = (K + nsplit - 1) / nsplit;
-            return (c + gran - 1) / gran * gran;
-        };
-        GemmProblem g2 = down_problem(f.ffn.h, &f.ffn, f.offsets, E, max_tiles, A, H, F, d->W2, d->S2,
-                                      f.ffn.part, split_stride, nsplit, chunk_for(F));
+        GemmProblem g2 = down_problem(f.ffn.h, &f.ffn, E, max_tiles, M, H, F, d->W2, d->S2, ex, A, f.ffn.part,
+                                      split_stride, nsplit, chunk_for(F, nsplit, d->w_dt));
         MOE_TRY(run_gemm(p, g2, wt, false, false, stream));
         MOE_TRY(mark(MOE_EV_DOWN));
-        if (d->Fs > 0) {
-            float *Sp = static_cast<float *>(f.ffn.part) + (size_t)A * H;
-            GemmProblem g2s = down_problem(h_s, nullptr, nullptr, 1, 0, T, H, d->Fs, d->Ws2, d->Ss2, Sp,
-                                           split_stride, nsplit, chunk_for(d->Fs));
+        float *Sp = static_cast<float *>(f.ffn.part) + (size_t)A * H;
+        if (d->Fs > 0 && !f.combined) {
+            GemmProblem g2s = down_problem(h_s, nullptr, 1, 0, T, H, d->Fs, d->Ws2, d->Ss2, none, 0, Sp,
+                                           split_stride, nsplit, chunk_for(d->Fs, nsplit, d->w_dt));
             MOE_TRY(run_gemm(f.plan_s, g2s, wt, false, false, stream));
-            S = Sp;
         }
+        if (d->Fs > 0) S = Sp;
     }
     MOE_TRY(mark(MOE_EV_SHARED_DOWN));
     // 4. combine

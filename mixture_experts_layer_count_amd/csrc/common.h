@@ -90,12 +90,18 @@ struct GemmProblem {
     const int32_t *row_src;
     int gk;
     int lda;
-    const int32_t *tiles;     // (group, row0) pairs, NULL: one group of M rows
+    const int32_t *tiles;     // (group, row0, row_end, 0) per tile; NULL: one group of M rows
     const int32_t *n_tiles;   // device count of tiles
-    const int32_t *offsets;   // [G+1]; NULL with tiles == NULL
-    const int32_t *group_tile_start;  // [G+1] first tile of each group (tiled kernel)
-    int G;                    // number of groups in the tile list
+    const int32_t *group_tile_start;  // [n_groups+1] first tile of each group (tiled kernel)
+    int n_groups;             // groups in the tile list (incl. the extra group)
     int max_tiles;            // host upper bound on tiles
+    // optional extra group (the always-on shared expert run in the same
+    // launch): its tiles carry group index extra_group; it uses the Bx/Sx
+    // weights, and its input rows r map to A[r - extra_row0] (no row_src)
+    int extra_group = -1;     // -1: none (never 0 by default: 0 is a real group)
+    int extra_row0 = 0;
+    const void *Bx0 = nullptr, *Bx1 = nullptr;
+    const float *Sx0 = nullptr, *Sx1 = nullptr;
     int M, N, K;
     const void *B0, *B1;      // [G][K][N]
     long long b_stride;       // elements per group
@@ -120,9 +126,11 @@ hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool o
 int tiled_gemm_bm(long long rows, int groups);  // rows per tile for this row distribution
 bool tiled_gemm_supports(WType wt, int N, int K);
 
-// Tile list (group, row0) for groups of rows given by offsets, bm rows per
-// tile, and (optional) the first tile index of every group, [G+1].
-hipError_t launch_build_tiles(const int32_t *offsets, int G, int bm, int32_t *tiles,
+// Tile list (group, row0, row_end, 0) for G groups of rows given by offsets
+// plus, when extra_rows > 0, group G = rows [offsets[G], offsets[G] +
+// extra_rows); bm rows per tile. Also the first tile index of every group,
+// [groups + 1] (optional).
+hipError_t launch_build_tiles(const int32_t *offsets, int G, int extra_rows, int bm, int32_t *tiles,
                               int32_t *n_tiles, int32_t *group_tile_start, hipStream_t s);
 
 // Router top-k. logits[t,e] = sum_s part[s][t][e] (s ascending) + bias[e] is

@@ -11,42 +11,47 @@
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *offsets, int G, int bm,
-                                                           int32_t *tiles, int32_t *n_tiles,
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *offsets, int G, int extra_rows,
+                                                           int bm, int32_t *tiles, int32_t *n_tiles,
                                                            int32_t *group_tile_start) {
     __shared__ int scan_lds[16];
+    const int NG = G + (extra_rows > 0 ? 1 : 0);
     int carry = 0;
     // groups in rounds of 1024; each thread emits its group's tiles
-    for (int g0 = 0; g0 < G; g0 += 1024) {
+    for (int g0 = 0; g0 < NG; g0 += 1024) {
         const int g = g0 + threadIdx.x;
-        int lo = 0, n = 0;
-        if (g < G) {
+        int lo = 0, hi = 0, n = 0;
+        if (g < NG) {
             lo = offsets[g];
-            n = (offsets[g + 1] - lo + bm - 1) / bm;
+            hi = g < G ? offsets[g + 1] : lo + extra_rows;
+            n = (hi - lo + bm - 1) / bm;
             if (n < 0) n = 0;
         }
         int total = 0;
         const int first = block_exclusive_scan(n, scan_lds, &total) + carry;
-        if (g < G && group_tile_start) group_tile_start[g] = first;
+        if (g < NG && group_tile_start) group_tile_start[g] = first;
         for (int i = 0; i < n; ++i) {
-            tiles[2 * (first + i)] = g;
-            tiles[2 * (first + i) + 1] = lo + i * bm;
+            int *t = tiles + 4 * (first + i);
+            t[0] = g;
+            t[1] = lo + i * bm;
+            t[2] = min(lo + (i + 1) * bm, hi);
+            t[3] = 0;
         }
         carry += total;
     }
     if (threadIdx.x == 0) {
         *n_tiles = carry;
-        if (group_tile_start) group_tile_start[G] = carry;
+        if (group_tile_start) group_tile_start[NG] = carry;
     }
 }
 
 }  // namespace
 
-hipError_t launch_build_tiles(const int32_t *offsets, int G, int bm, int32_t *tiles,
+hipError_t launch_build_tiles(const int32_t *offsets, int G, int extra_rows, int bm, int32_t *tiles,
                               int32_t *n_tiles, int32_t *group_tile_start, hipStream_t s) {
-    if (G < 1 || bm < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, G, bm, tiles, n_tiles,
-                       group_tile_start);
+    if (G < 1 || bm < 1 || extra_rows < 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, G, extra_rows, bm, tiles,
+                       n_tiles, group_tile_start);
     return hipGetLastError();
 }
 

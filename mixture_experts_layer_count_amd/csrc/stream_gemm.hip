@@ -141,10 +141,11 @@ __device__ __forceinline__ void load_a(AFrag<WT> &f, const typename WTraits<WT>:
     }
 }
 
-#ifndef MOE_STREAM_DEPTH
-#define MOE_STREAM_DEPTH 3
-#endif
-constexpr int kDepth = MOE_STREAM_DEPTH;  // K steps whose loads are in flight
+// K steps held in the register ring (kDepth - 1 in flight while one is
+// multiplied), the deepest that keeps two wavefronts per SIMD: the
+// single-matrix down projection has registers to spare; fp8 gate/up stages
+// are larger after decoding.
+template <int WT, bool SWIGLU> constexpr int ring_depth() { return !SWIGLU ? 4 : (WT == W_FP8 ? 2 : 3); }
 
 // One K step's operands for one lane: weight rows of both matrices, the token
 // fragment and (fp8) the block scales of the step's 128-deep K block.
@@ -160,6 +161,7 @@ template <int WT, bool SWIGLU, bool OUT_BF16>
 __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p, int n_slices) {
     typedef typename WTraits<WT>::elem E;
     typedef typename WTraits<WT>::act AT;
+    constexpr int kDepth = ring_depth<WT, SWIGLU>();
 
     const int lane = threadIdx.x & 63;
     const long long wave = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -170,9 +172,9 @@ __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p,
     int g, row0, row_end;
     if (p.tiles) {
         if (mt >= p.max_tiles || mt >= *p.n_tiles) return;
-        g = p.tiles[2 * mt];
-        row0 = p.tiles[2 * mt + 1];
-        row_end = min(row0 + kBM, p.offsets[g + 1]);
+        g = p.tiles[4 * mt];
+        row0 = p.tiles[4 * mt + 1];
+        row_end = p.tiles[4 * mt + 2];
     } else {
         g = 0;
         row0 = mt * kBM;
@@ -190,16 +192,22 @@ __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p,
     // this lane's activation row (MFMA A operand row = lane & 15)
     const int r = row0 + (lane & 15);
     const bool rok = r < row_end;
+    const bool extra = g == p.extra_group;
     long long arow = 0;
-    if (rok) arow = p.row_src ? (long long)(p.row_src[r] / p.gk) : (long long)r;
+    if (rok) {
+        if (extra && p.row_src) arow = r - p.extra_row0;
+        else arow = p.row_src ? (long long)(p.row_src[r] / p.gk) : (long long)r;
+    }
     const AT *Ap = reinterpret_cast<const AT *>(p.A) + arow * p.lda + 8 * kg + kbeg;
 
     const long long ldb = p.N;
-    const E *B0 = reinterpret_cast<const E *>(p.B0) + (long long)g * p.b_stride + col + (8 * kg + kbeg) * ldb;
-    const E *B1 = SWIGLU ? reinterpret_cast<const E *>(p.B1) + (long long)g * p.b_stride + col +
-                               (8 * kg + kbeg) * ldb
+    const long long goff = extra ? 0 : (long long)g * p.b_stride;
+    const E *B0 = reinterpret_cast<const E *>(extra ? p.Bx0 : p.B0) + goff + col + (8 * kg + kbeg) * ldb;
+    const E *B1 = SWIGLU ? reinterpret_cast<const E *>(extra ? p.Bx1 : p.B1) + goff + col + (8 * kg + kbeg) * ldb
                          : nullptr;
-    const long long sbase = (long long)g * p.s_stride + (col >> 7);
+    const float *S0p = extra ? p.Sx0 : p.S0;
+    const float *S1p = extra ? p.Sx1 : p.S1;
+    const long long sbase = (extra ? 0 : (long long)g * p.s_stride) + (col >> 7);
     const int sstride = p.N >> 7;
 
     auto issue = [&](Stage<WT, SWIGLU> &st, int step) {
@@ -208,8 +216,8 @@ __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p,
         load_a<WT>(st.a, Ap + step * 32, rok);
         if constexpr (WT == W_FP8) {
             const long long si = sbase + (long long)((kbeg + step * 32) >> 7) * sstride;
-            st.s0 = colok ? p.S0[si] : 0.0f;
-            st.s1 = (SWIGLU && colok) ? p.S1[si] : 0.0f;
+            st.s0 = colok ? S0p[si] : 0.0f;
+            st.s1 = (SWIGLU && colok) ? S1p[si] : 0.0f;
         }
     };
 
@@ -303,6 +311,9 @@ hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
 
 hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,
                               hipStream_t s) {
+    // an extra group needs its own weights (and scales for fp8)
+    if (p.extra_group >= 0 && (!p.Bx0 || (swiglu && !p.Bx1) || (wt == W_FP8 && (!p.Sx0 || (swiglu && !p.Sx1)))))
+        return hipErrorInvalidValue;
     if (p.K % 32 || p.N % kVec || p.kchunk % 32 || p.ksplit < 1) return hipErrorInvalidValue;
     if (wt == W_FP8 && (p.K % 128 || p.N % 128 || p.kchunk % 128)) return hipErrorInvalidValue;
     switch (wt) {

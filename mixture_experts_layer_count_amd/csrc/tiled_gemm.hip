@@ -115,7 +115,7 @@ __device__ __forceinline__ bool pick_tile(const GemmProblem &p, int nN, int bm, 
         return true;
     }
     // group holding id: largest g with starts[g] * nN <= id (binary search)
-    int lo = 0, hi = p.G;
+    int lo = 0, hi = p.n_groups;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (p.group_tile_start[mid] * nN <= id) lo = mid;
@@ -143,9 +143,9 @@ __global__ __launch_bounds__(kThreads, 1) void tiled_gemm_kernel(GemmProblem p, 
     if (!pick_tile(p, nN, BM, mt, nt)) return;
     int g, row0, row_end;
     if (p.tiles) {
-        g = p.tiles[2 * mt];
-        row0 = p.tiles[2 * mt + 1];
-        row_end = min(row0 + BM, p.offsets[g + 1]);
+        g = p.tiles[4 * mt];
+        row0 = p.tiles[4 * mt + 1];
+        row_end = p.tiles[4 * mt + 2];
     } else {
         g = 0;
         row0 = mt * BM;
@@ -160,12 +160,16 @@ __global__ __launch_bounds__(kThreads, 1) void tiled_gemm_kernel(GemmProblem p, 
     const int a_kc = tid & 7;
     const uint16_t *a_src[G::arows];
     bool a_ok[G::arows];
+    const bool extra = g == p.extra_group;
 #pragma unroll
     for (int q = 0; q < G::arows; ++q) {
         const int r = row0 + (tid >> 3) + 32 * q;
         a_ok[q] = r < row_end;
         long long src = 0;
-        if (a_ok[q]) src = p.row_src ? (long long)(p.row_src[r] / p.gk) : (long long)r;
+        if (a_ok[q]) {
+            if (extra && p.row_src) src = r - p.extra_row0;
+            else src = p.row_src ? (long long)(p.row_src[r] / p.gk) : (long long)r;
+        }
         a_src[q] = reinterpret_cast<const uint16_t *>(p.A) + src * p.lda + 8 * a_kc;
     }
 
@@ -175,10 +179,10 @@ __global__ __launch_bounds__(kThreads, 1) void tiled_gemm_kernel(GemmProblem p, 
     const int b_col = (SWIGLU ? n0 : n0 + b_half * kBNH) + 8 * (b_cg & 15);
     const bool b_ok = b_col < p.N;
     typedef typename std::conditional<WT == W_FP8, uint8_t, uint16_t>::type E;
-    const E *b_base = reinterpret_cast<const E *>((SWIGLU && b_half) ? p.B1 : p.B0) +
-                      (long long)g * p.b_stride + b_col;
-    const float *b_scale = (SWIGLU && b_half) ? p.S1 : p.S0;
-    const long long b_sidx = (long long)g * p.s_stride + (b_col >> 7);
+    const void *bsrc = extra ? ((SWIGLU && b_half) ? p.Bx1 : p.Bx0) : ((SWIGLU && b_half) ? p.B1 : p.B0);
+    const E *b_base = reinterpret_cast<const E *>(bsrc) + (extra ? 0 : (long long)g * p.b_stride) + b_col;
+    const float *b_scale = extra ? ((SWIGLU && b_half) ? p.Sx1 : p.Sx0) : ((SWIGLU && b_half) ? p.S1 : p.S0);
+    const long long b_sidx = (extra ? 0 : (long long)g * p.s_stride) + (b_col >> 7);
 
     u32x4 a_reg[G::arows];
     u32x4 b_reg[8];   // bf16: 8 columns per K row
@@ -346,6 +350,9 @@ bool tiled_gemm_supports(WType wt, int N, int K) {
 
 hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16, int bm,
                              hipStream_t s) {
+    // an extra group needs its own weights (and scales for fp8)
+    if (p.extra_group >= 0 && (!p.Bx0 || (swiglu && !p.Bx1) || (wt == W_FP8 && (!p.Sx0 || (swiglu && !p.Sx1)))))
+        return hipErrorInvalidValue;
     if (!out_bf16 || p.ksplit != 1 || !tiled_gemm_supports(wt, p.N, p.K)) return hipErrorInvalidValue;
     if (bm != 128 && bm != 256) return hipErrorInvalidValue;
     switch (wt) {
