@@ -14,10 +14,13 @@ recorded by libmoe on its own stream around that kernel, in every timed step.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
 import platform
+import re
 import statistics
 import sys
 import time
@@ -69,16 +72,106 @@ def cpu_baseline(cfg, d, k: int) -> dict:
     tokens = np.arange(min(n, cfg.T))
     host = {key: (v.cpu() if hasattr(v, "cpu") else v) for key, v in d.items()}
     L = oracle.Layer(host, k)
-    t0 = time.perf_counter()
-    oracle.forward_tokens(L, tokens)
-    dt = time.perf_counter() - t0
+    # repeat the sample until about 10 s of CPU work have been timed
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward_tokens(L, tokens)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or passes >= 64:
+            break
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(tokens)} of {cfg.T} tokens, full fp64 layer forward (route over all E, "
-                      f"SwiGLU of each chosen expert, combine); {dt:.1f} s on {platform.processor() or 'host'}"}
+    return {"value": passes * len(tokens) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(tokens)} of {cfg.T} tokens x {passes} passes, full fp64 layer forward (route over "
+                      f"all E, SwiGLU of each chosen expert, combine); {dt:.1f} s on "
+                      f"{platform.processor() or 'host'}"}
 
 
-def copy_calibration(nbytes: int = 1 << 30) -> None:
+GATE_UP_KERNEL = re.compile(r"(stream|tiled)_gemm_kernel<[^,]+, true")
+
+
+def _pmc_means(run_dir: str, counter: str) -> dict:
+    """Mean per-dispatch value of one counter, per kernel name, from a
+    rocprofv3 `--pmc ... -f csv` output directory."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per_dispatch = {}
+    for f in files:
+        with open(f, newline="", encoding="utf-8") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (f, r["Dispatch_Id"], r["Kernel_Name"])
+                per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    by_kernel = {}
+    for (_, _, name), v in per_dispatch.items():
+        by_kernel.setdefault(name, []).append(v)
+    return {name: (sum(v) / len(v), len(v)) for name, v in by_kernel.items()}
+
+
+def record_traffic(args) -> int:
+    """Turn four rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE of the
+    workload and of the copy calibration) into the committed per-launch HBM
+    traffic record of the gate/up kernel."""
+    fetch, write = _pmc_means(args.pmc_fetch, "FETCH_SIZE"), _pmc_means(args.pmc_write, "WRITE_SIZE")
+    cal_f, cal_w = _pmc_means(args.calib_fetch, "FETCH_SIZE"), _pmc_means(args.calib_write, "WRITE_SIZE")
+    nbytes = COPY_CALIBRATION_BYTES
+    # the copy is the calibration run's kernel that reads the most; every
+    # kernel of that run (fill, copy) writes the whole buffer
+    f_fetch = nbytes / (max(v for v, _ in cal_f.values()) * 1024.0)
+    f_write = nbytes / (max(v for v, _ in cal_w.values()) * 1024.0)
+    names = [n for n in fetch if GATE_UP_KERNEL.search(n)]
+    if len(names) != 1:
+        raise SystemExit(f"expected one gate/up kernel, found {names}")
+    name = names[0]
+    fk, nf = fetch[name]
+    wk, nw = write[name]
+    rec = {
+        "workload": args.workload, "kernel": name, "kernel_source_hash": kernel_source_hash(),
+        "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+        "dispatches": [nf, nw], "calibration_bytes": nbytes,
+        "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4),
+        "hbm_bytes_per_launch": round(fk * 1024.0 * f_fetch + wk * 1024.0 * f_write),
+        "commands": args.commands,
+    }
+    out = os.path.join(PROFILE_DIR, f"gate_up_swiglu_{args.workload}_pmc.json")
+    with open(out, "w", encoding="utf-8") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+    return 0
+
+
+def summarize_trace(args) -> int:
+    """Markdown table of libmoe's kernels from a rocprofv3 `--kernel-trace
+    --stats -f csv` output directory (torch's own kernels left out)."""
+    files = glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {args.summarize_trace}")
+    rows = []
+    with open(files[0], newline="", encoding="utf-8") as fh:
+        for r in csv.DictReader(fh):
+            name = r["Name"]
+            if "moe::" not in name:
+                continue
+            name = re.sub(r"\(moe::GemmProblem, int\)|\((int|float|long|unsigned|short|moe::|const|uint4).*$", "",
+                          name.replace("moe::(anonymous namespace)::", "")).strip()
+            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e3,
+                         float(r["Percentage"])))
+    print(f"# rocprofv3 kernel trace: {args.workload}\n")
+    print("Command, from the repository root:\n\n```\n" + " ".join(args.commands) + "\n```\n")
+    print("| kernel | calls | avg (us) | total (us) | % of GPU time |\n|---|---:|---:|---:|---:|")
+    for name, calls, avg, tot, pct in rows:
+        print(f"| `{name}` | {calls} | {avg:.2f} | {tot:.1f} | {pct:.1f} |")
+    print("\nKernels of torch (input generation, copies) are left out; the percentages are of all GPU time.")
+    return 0
+
+
+COPY_CALIBRATION_BYTES = 1 << 30
+
+
+def copy_calibration(nbytes: int = COPY_CALIBRATION_BYTES) -> None:
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
     x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -99,7 +192,20 @@ def main() -> int:
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "tiled"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--record-traffic", action="store_true",
+                    help="write the gate/up HBM traffic record from rocprofv3 counter runs (no GPU)")
+    ap.add_argument("--pmc-fetch")
+    ap.add_argument("--pmc-write")
+    ap.add_argument("--calib-fetch")
+    ap.add_argument("--calib-write")
+    ap.add_argument("--commands", nargs="*", default=[])
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 kernel-trace run (no GPU)")
     args = ap.parse_args()
+    if args.record_traffic:
+        return record_traffic(args)
+    if args.summarize_trace:
+        return summarize_trace(args)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the MoE layer here runs on a "
@@ -159,8 +265,15 @@ def main() -> int:
     gate_up_w = touched * 2 * cfg.H * cfg.F * wb
     if cfg.w == "fp8":
         gate_up_w += touched * 2 * (cfg.H // 128) * (cfg.F // 128) * 4
-    gate_up_bytes = gate_up_w + cfg.T * cfg.H * ab + A * cfg.F * ab
-    gate_up_flops = 4.0 * A * cfg.H * cfg.F
+    gate_up_rows = A
+    if cfg.Fs > 0 and cfg.Fs == cfg.F:
+        # the always-on shared expert runs as one more group of the same launch
+        gate_up_w += 2 * cfg.H * cfg.Fs * wb
+        if cfg.w == "fp8":
+            gate_up_w += 2 * (cfg.H // 128) * (cfg.Fs // 128) * 4
+        gate_up_rows += cfg.T
+    gate_up_bytes = gate_up_w + cfg.T * cfg.H * ab + gate_up_rows * cfg.F * ab
+    gate_up_flops = 4.0 * gate_up_rows * cfg.H * cfg.F
     decode = args.workload in DECODE_WORKLOADS
     kernel_name = "gate_up_swiglu"
     if decode:

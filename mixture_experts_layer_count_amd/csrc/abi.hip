@@ -227,8 +227,9 @@ struct RoutePlan {
 RoutePlan plan_route(int T, int H, int E) {
     long long base = (long long)((T + 15) / 16) * ((E + 63) / 64);
     if (base < 1) base = 1;
-    long long ks = (1024 + base - 1) / base;
-    const long long max_ks = H / 128 > 0 ? H / 128 : 1;
+    long long ks = (4096 + base - 1) / base;
+    long long max_ks = H / 128 > 0 ? H / 128 : 1;
+    if (max_ks > 16) max_ks = 16;
     if (ks > max_ks) ks = max_ks;
     if (ks < 1) ks = 1;
     int chunk = (int)((H + ks - 1) / ks);

@@ -44,8 +44,18 @@ __global__ __launch_bounds__(kWaves * 64) void topk_kernel(const float *part, in
         const int e = lane + 64 * i;
         float x = -INFINITY;
         if (e < E) {
-            x = prow[e];
-            for (int sp = 1; sp < nsplit; ++sp) x += prow[sp * split_stride + e];
+            // fixed-order sum of the split-K partials; loads issued in
+            // batches of 8 so their latencies overlap
+            x = 0.0f;
+            for (int s0 = 0; s0 < nsplit; s0 += 8) {
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    v[u] = (s0 + u < nsplit) ? prow[(long long)(s0 + u) * split_stride + e] : 0.0f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (s0 + u < nsplit) x = (s0 + u == 0) ? v[u] : x + v[u];
+            }
             if (bias) x += bias[e];
             row[e] = x;
         }
