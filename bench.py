@@ -33,12 +33,15 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 DECODE_WORKLOADS = {"toy_fp32", "mixtral_decode", "qwen3_decode", "dsv3_decode"}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("stream_gemm.hip", "tiled_gemm.hip", "common.h")
+# sources of the gate/up kernel each path launches (the traffic record is
+# void once any of them changes)
+KERNEL_SOURCES = {"stream": ("stream_gemm.hip", "common.h"),
+                  "tiled": ("tiled_gemm_kernel.h", "tiled_gemm_bm128.hip", "tiled_gemm_bm256.hip", "common.h")}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(path: str) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[path]:
         p = os.path.join(ROOT, "mixture_experts_layer_count_amd", "csrc", name)
         with open(p, "rb") as fh:
             h.update(fh.read())
@@ -53,7 +56,8 @@ def measured_traffic(workload: str, kernel: str):
         return None
     with open(path, encoding="utf-8") as fh:
         rec = json.load(fh)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    path = "stream" if "stream_gemm" in rec.get("kernel", "") else "tiled"
+    if rec.get("kernel_source_hash") != kernel_source_hash(path):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -128,7 +132,8 @@ def record_traffic(args) -> int:
     fk, nf = fetch[name]
     wk, nw = write[name]
     rec = {
-        "workload": args.workload, "kernel": name, "kernel_source_hash": kernel_source_hash(),
+        "workload": args.workload, "kernel": name,
+        "kernel_source_hash": kernel_source_hash("stream" if "stream_gemm" in name else "tiled"),
         "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
         "dispatches": [nf, nw], "calibration_bytes": nbytes,
         "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4),
@@ -139,6 +144,16 @@ def record_traffic(args) -> int:
     with open(out, "w", encoding="utf-8") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
+    with open(out[:-5] + ".md", "w", encoding="utf-8") as fh:
+        fh.write(f"# HBM traffic of the gate/up SwiGLU kernel: {args.workload}\n\n"
+                 f"Kernel: `{name}` (sources hash {rec['kernel_source_hash']}).\n\n"
+                 "| counter | KiB per dispatch | dispatches | scale | bytes per launch |\n|---|---:|---:|---:|---:|\n"
+                 f"| FETCH_SIZE | {fk:.1f} | {nf} | {f_fetch:.4f} | {fk * 1024 * f_fetch:.4g} |\n"
+                 f"| WRITE_SIZE | {wk:.1f} | {nw} | {f_write:.4f} | {wk * 1024 * f_write:.4g} |\n\n"
+                 f"HBM bytes per launch: {rec['hbm_bytes_per_launch']:.4g}. The scales are what a {nbytes >> 20} MiB "
+                 "device-to-device copy reads and writes, divided by what these counters report for it (its blit "
+                 "kernel's FETCH_SIZE reports half the bytes read).\n\nCommands, from the repository root R:\n\n```\n"
+                 + "\n".join(args.commands) + "\n```\n")
     print(json.dumps(rec))
     return 0
 

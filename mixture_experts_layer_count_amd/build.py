@@ -27,9 +27,20 @@ FLAGS = [
 ]
 
 
+def _file_flags(src: str) -> list[str]:
+    """Extra flags a source asks for on a `// build-flags: ...` line in its
+    header comment."""
+    with open(src, encoding="utf-8") as fh:
+        for _ in range(12):
+            line = fh.readline()
+            if line.startswith("// build-flags:"):
+                return line.split(":", 1)[1].split()
+    return []
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *_file_flags(src), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

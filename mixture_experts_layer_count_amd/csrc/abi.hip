@@ -71,7 +71,7 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path) 
     if (path == MOE_PATH_TILED) p.tiled = can_tile;
     else if (path == MOE_PATH_GEMV) p.tiled = false;
     else p.tiled = can_tile && (long long)M >= 48LL * G;
-    p.bm = p.tiled ? tiled_gemm_bm(M, G) : kGemvBM;
+    p.bm = p.tiled ? tiled_gemm_bm(wt, M, G) : kGemvBM;
     p.ksplit2 = 1;
     p.kchunk2 = F;
     if (!p.tiled) {

@@ -118,12 +118,12 @@ hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool 
                               hipStream_t s);
 
 // LDS-tiled grouped GEMM (many rows per group). Same problem statement;
-// ksplit must be 1; bm (rows per tile) must be tiled_gemm_bm(avg rows) and
+// ksplit must be 1; bm (rows per tile) must be tiled_gemm_bm(wt, rows, groups) and
 // the tile list must have been built with it. Returns hipErrorInvalidValue
 // for unsupported shapes.
 hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16, int bm,
                              hipStream_t s);
-int tiled_gemm_bm(long long rows, int groups);  // rows per tile for this row distribution
+int tiled_gemm_bm(WType wt, long long rows, int groups);  // rows per tile for this row distribution
 bool tiled_gemm_supports(WType wt, int N, int K);
 
 // Tile list (group, row0, row_end, 0) for G groups of rows given by offsets

@@ -1,0 +1,496 @@
+// LDS-tiled grouped GEMM for many rows per expert (prefill): the kernel
+// template, instantiated per tile height by tiled_gemm_bm128.hip and
+// tiled_gemm_bm256.hip (separate files: each is compiled with the register
+// form that keeps its accumulators in place), launched by tiled_gemm.hip.
+//
+// The grouped GEMM of the page "MoE-推理部署" (operator section) and the page
+// "MOE推理流程解析" §二/§三: every expert's block of rows runs in one launch,
+// with row counts that differ per expert; §三 also asks that fusion keep
+// intermediates out of HBM, so the row gather (permutation) is fused into the
+// A-tile load and SwiGLU into the gate/up epilogue.
+//
+// Tile: BM rows (256, or 128 when experts hold few rows, always 128 for fp8
+// weights) x 256 B-columns x 32 deep; 256 threads = 4 wavefronts in a 2 x 2
+// grid, each owning BM/2 rows x 128 B-columns.
+//  * gate/up (SWIGLU): B-columns 0..127 are W1[:, n0:n0+128] and 128..255 are
+//    W3[:, n0:n0+128]; wavefront column wc holds the W1 and W3 accumulators of
+//    output columns n0 + 64 wc .. +63, so h = silu(g) * u is formed in
+//    registers.
+//  * down (PLAIN): B-columns are W2[:, n0:n0+256]; wavefront column wc owns
+//    n0 + 128 wc .. +127.
+// MI355X mapping:
+//  * operands go global -> LDS with global_load_lds_dwordx4 (no register
+//    staging) into a ring of S stages (S = 4..8, as many as fit in 144 KB), so
+//    S - 1 K tiles are in flight while one is multiplied. Each thread waits
+//    only for its own copies of the next tile (s_waitcnt vmcnt(n), n = copies
+//    issued after it), then one barrier per K tile publishes the tile and
+//    frees the stage read before it. One loop with one MFMA site and a fixed
+//    wait keeps the accumulators in place (no register shuffling).
+//  * the A tile holds 64-byte token rows, 16 rows x 4 chunks per 1 KB copy,
+//    read back as 16-byte MFMA A operands (v_mfma_f32_16x16x32_bf16); the
+//    chunk order inside a row is XOR-swizzled by row / 4 (measured: without
+//    it the operand reads conflict 2-way).
+//  * the B tile keeps the weights' [K][N] layout; the MFMA B operand (8
+//    K-consecutive values of one column) is read with ds_read_b64_tr_b16
+//    (bf16) or ds_read_b64_tr_b8 (fp8). 16-byte chunks of a K row are
+//    XOR-swizzled by the row index (the copies fetch the swizzled chunk, since
+//    a copy's lanes land in consecutive LDS), so each half-wavefront of a
+//    transposing read touches every bank once.
+//  * fp8 E4M3 weights are decoded exactly to bf16 after the transposing read
+//    (v_cvt_scalef32_pk_bf16_fp8, scale 1); every 128-deep K block is
+//    accumulated separately and added to the result times its 128x128 block
+//    scale, as the block-scaled format defines.
+//  * A rows are gathered through row_src by the copies themselves (the
+//    permuted token matrix is never written).
+//  * the next K tile's fragments are read while the current tile's MFMAs run
+//    (two fragment register sets); the copies and reads are spread between
+//    the MFMA groups of the row blocks, so their issue never idles the matrix
+//    cores (measured: issued all at once after the barrier, they took as long
+//    as the MFMAs).
+//  * tile order: the row tiles of one expert times a band of column tiles
+//    are consecutive, and each XCD (own L2) takes a contiguous run of that
+//    order, so an expert's weight tiles and its gathered rows are read from
+//    beyond L2 about once. The real tile count is read on the device, so
+//    surplus workgroups of the worst-case grid exit without unbalancing the
+//    XCDs.
+//  * the epilogue stages the bf16 tile in LDS and writes 16-byte rows.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace moe {
+namespace tiled {
+
+#define AS1 __attribute__((address_space(1)))
+#define AS3 __attribute__((address_space(3)))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kBK = 32;            // K depth per tile: one MFMA step
+constexpr int kXcds = 8;
+constexpr int kBlocksPerXcd = 32;  // one workgroup per CU (LDS-bound)
+constexpr int kRingBudget = 144 * 1024;
+
+template <int WT, int BM>
+struct Ring {
+    static constexpr bool fp8 = WT == W_FP8;
+    static constexpr int a_bytes = BM * kBK * 2;        // 64-byte bf16 rows
+    static constexpr int b_row = fp8 ? 256 : 512;       // one K row of 256 B-columns
+    static constexpr int b_bytes = kBK * b_row;
+    static constexpr int s_bytes = fp8 ? 4 * 256 : 0;   // per-wavefront block-scale copies
+    static constexpr int stage = a_bytes + b_bytes + s_bytes;
+    static constexpr int S = (kRingBudget / stage) < 8 ? (kRingBudget / stage) : 8;
+    static constexpr int nA = a_bytes / (kThreads * 16);  // 16-byte copies per thread per tile
+    static constexpr int nB = b_bytes / (kThreads * 16);
+    static constexpr int per_tile = nA + nB + (fp8 ? 1 : 0);  // vector-memory ops per tile
+    static constexpr int mi = BM / 32;                    // 16-row MFMA blocks per wavefront
+    static constexpr int ring = S * stage;
+};
+
+template <bool SWIGLU>
+struct Out {
+    static constexpr int width = SWIGLU ? 128 : 256;  // output columns per tile
+    static constexpr int ld = width + 8;              // LDS staging row stride (elements)
+};
+
+template <int WT, bool SWIGLU, int BM>
+constexpr int lds_bytes() {
+    return Ring<WT, BM>::ring > BM * Out<SWIGLU>::ld * 2 ? Ring<WT, BM>::ring : BM * Out<SWIGLU>::ld * 2;
+}
+
+// A tile: 64-byte rows, 16-byte chunk c of row r stored at c ^ ((r >> 2) & 3),
+// so the 8 rows an 8-lane group of a ds_read_b128 touches cover all banks.
+// A copy's lane l lands in row l/4 (of its 16), physical chunk l%4, and
+// therefore fetches logical chunk (l%4) ^ ((l/16) % 4).
+__device__ __forceinline__ int aswz_chunk(int lane) { return (lane & 3) ^ ((lane >> 4) & 3); }
+// chunk swizzles of the B tile (16-byte chunks of one K row)
+__device__ __forceinline__ int bswz16(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+__device__ __forceinline__ int bswz8(int k) { return k & 15; }
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+template <int PER, int MAXT>
+__device__ __forceinline__ void wait_tiles(int t) {
+    // wait until at most t tiles (t <= MAXT) of PER copies each are in flight
+    static_assert(MAXT <= 7, "ring depth");
+    switch (t) {
+    case 0: wait_vm<0>(); break;
+    case 1: if constexpr (MAXT >= 1) wait_vm<PER>(); break;
+    case 2: if constexpr (MAXT >= 2) wait_vm<2 * PER>(); break;
+    case 3: if constexpr (MAXT >= 3) wait_vm<3 * PER>(); break;
+    case 4: if constexpr (MAXT >= 4) wait_vm<4 * PER>(); break;
+    case 5: if constexpr (MAXT >= 5) wait_vm<5 * PER>(); break;
+    case 6: if constexpr (MAXT >= 6) wait_vm<6 * PER>(); break;
+    default: if constexpr (MAXT >= 7) wait_vm<7 * PER>(); break;
+    }
+}
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+__device__ __forceinline__ void copy16(const void *g, uint8_t *l) {
+    __builtin_amdgcn_global_load_lds((AS1 void *)g, (AS3 void *)l, 16, 0, 0);
+}
+__device__ __forceinline__ void copy4(const void *g, uint8_t *l) {
+    __builtin_amdgcn_global_load_lds((AS1 void *)g, (AS3 void *)l, 4, 0, 0);
+}
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+    return (uint32_t)(uintptr_t)(const AS3 uint8_t *)p;
+}
+// Transposing LDS reads, issued as plain instructions: the builtins carry no
+// memory operand, which makes the compiler drain every outstanding global->LDS
+// copy before them. The results are only valid after wait_lds(); fence()
+// then hands them to the compiler as fresh values.
+__device__ __forceinline__ u32x2 ds_tr16(uint32_t addr) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+__device__ __forceinline__ u32x2 ds_tr8(uint32_t addr) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+__device__ __forceinline__ void fence(u32x2 &v) { asm volatile("" : "+v"(v)); }
+
+// Map this workgroup to (row tile, column tile) of the work order; false for
+// surplus workgroups. Work order: for each group, for each band of gn column
+// tiles, the group's row tiles x the band's column tiles (column fastest).
+// XCD x (workgroup id mod 8) takes the contiguous run [x*per, (x+1)*per).
+__device__ __forceinline__ bool pick_tile(const GemmProblem &p, int nN, int bm, int &mt, int &nt) {
+    const int n_tiles = p.tiles ? *p.n_tiles : (p.M + bm - 1) / bm;
+    const int n_work = n_tiles * nN;
+    const int per = (n_work + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    if (slot >= per) return false;
+    const int id = (blockIdx.x % kXcds) * per + slot;
+    if (id >= n_work) return false;
+    if (!p.tiles || !p.group_tile_start) {
+        mt = id % n_tiles;
+        nt = id / n_tiles;
+        return true;
+    }
+    // group holding id: largest g with starts[g] * nN <= id (binary search)
+    int lo = 0, hi = p.n_groups;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.group_tile_start[mid] * nN <= id) lo = mid;
+        else hi = mid;
+    }
+    const int t0 = p.group_tile_start[lo];
+    const int cnt = p.group_tile_start[lo + 1] - t0;  // > 0: id lies in this group
+    int gn = (kBlocksPerXcd + cnt - 1) / cnt;
+    if (gn > nN) gn = nN;
+    const int j = id - t0 * nN;
+    const int band = j / (cnt * gn);
+    const int q = j - band * cnt * gn;
+    const int width = min(gn, nN - band * gn);
+    nt = band * gn + q % width;
+    mt = t0 + q / width;
+    return true;
+}
+
+// One fragment set: the A operands of the wavefront's row blocks, the B
+// operands of its 8 column blocks and (fp8) its two block scales.
+template <int MI, bool FP8>
+struct Frags {
+    bf16x8 a[MI];
+    bf16x8 b[8];                // B operands, formed by land()
+    u32x2 raw[8][FP8 ? 1 : 2];  // transposed reads: 8 fp8, or 2 x 4 bf16, per block
+    float s0, s1;
+};
+
+template <int WT, bool SWIGLU, int BM>
+__global__ __launch_bounds__(kThreads, 1) void tiled_gemm_kernel(GemmProblem p, int nN) {
+    typedef Ring<WT, BM> R;
+    constexpr bool FP8 = R::fp8;
+    constexpr int S = R::S;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<WT, SWIGLU, BM>()];
+
+    int mt, nt;
+    if (!pick_tile(p, nN, BM, mt, nt)) return;
+    int g, row0, row_end;
+    if (p.tiles) {
+        g = p.tiles[4 * mt];
+        row0 = p.tiles[4 * mt + 1];
+        row_end = p.tiles[4 * mt + 2];
+    } else {
+        g = 0;
+        row0 = mt * BM;
+        row_end = min(row0 + BM, p.M);
+    }
+    const int n0 = nt * Out<SWIGLU>::width;
+    const bool extra = g == p.extra_group;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
+
+    // ---- copy sources (fixed over K; advanced by k0 per tile) ----
+    // A: copy q of wavefront w fills rows 16 (w nA + q) .. +15, lane -> row
+    // lane/4, 16-byte chunk lane%4. Rows past the tile's end copy a valid row
+    // (their results are never stored).
+    const uint16_t *a_src[R::nA];
+#pragma unroll
+    for (int q = 0; q < R::nA; ++q) {
+        int r = row0 + 16 * (w * R::nA + q) + (lane >> 2);
+        if (r >= row_end) r = row0;
+        long long src;
+        if (extra && p.row_src) src = r - p.extra_row0;
+        else src = p.row_src ? (long long)(p.row_src[r] / p.gk) : (long long)r;
+        a_src[q] = reinterpret_cast<const uint16_t *>(p.A) + src * p.lda + 8 * aswz_chunk(lane);
+    }
+    // B: copy q of wavefront w fills K rows of the B tile; each lane fetches
+    // the chunk that the swizzle places at its LDS position. Columns past N
+    // copy a valid chunk (their results are never stored).
+    typedef typename std::conditional<FP8, uint8_t, uint16_t>::type WE;
+    const WE *b_src[R::nB];
+    const void *B0 = extra ? p.Bx0 : p.B0;
+    const void *B1 = extra ? p.Bx1 : p.B1;
+    const long long gofs = extra ? 0 : (long long)g * p.b_stride;
+#pragma unroll
+    for (int q = 0; q < R::nB; ++q) {
+        int k, col;
+        const void *base;
+        if constexpr (FP8) {
+            k = 4 * (w * R::nB + q) + (lane >> 4);
+            const int c = (lane & 15) ^ bswz8(k);  // 16 columns per chunk
+            if (SWIGLU) { base = (c >> 3) ? B1 : B0; col = n0 + 16 * (c & 7); }
+            else { base = B0; col = n0 + 16 * c; }
+            if (col > p.N - 16) col = p.N - 16;
+        } else {
+            k = 2 * (w * R::nB + q) + (lane >> 5);
+            const int c = (lane & 31) ^ bswz16(k);  // 8 columns per chunk
+            if (SWIGLU) { base = (c >> 4) ? B1 : B0; col = n0 + 8 * (c & 15); }
+            else { base = B0; col = n0 + 8 * c; }
+            if (col > p.N - 8) col = p.N - 8;
+        }
+        b_src[q] = reinterpret_cast<const WE *>(base) + gofs + (long long)k * p.N + col;
+    }
+    // fp8 block scales: wavefront w copies its two scales (W1/W3 halves, or
+    // its W2 column block twice) for every tile; lanes 0/1 pick them
+    const float *s_src = nullptr;
+    if constexpr (FP8) {
+        const float *S0 = extra ? p.Sx0 : p.S0;
+        const float *S1 = extra ? p.Sx1 : p.S1;
+        const long long sofs = extra ? 0 : (long long)g * p.s_stride;
+        int nb;
+        const float *sb;
+        if (SWIGLU) { nb = n0 >> 7; sb = (lane & 1) ? S1 : S0; }
+        else { nb = min((n0 >> 7) + wc, (p.N >> 7) - 1); sb = S0; }
+        s_src = sb + sofs + nb;
+    }
+
+    // ---- global -> LDS copies of one K tile: item q of NC ----
+    constexpr int NC = R::nA + R::nB + (FP8 ? 1 : 0);
+    auto copy = [&](int q, int kt, int stage) {
+        uint8_t *st = lds + stage * R::stage;
+        const int k0 = kt * kBK;
+        if (q < R::nA) {
+            copy16(a_src[q] + k0, st + (w * R::nA + q) * 1024);
+        } else if (q < R::nA + R::nB) {
+            const int qb = q - R::nA;
+            copy16(b_src[qb] + (long long)k0 * p.N, st + R::a_bytes + (w * R::nB + qb) * 1024);
+        } else if constexpr (FP8) {
+            copy4(s_src + (long long)(k0 >> 7) * (p.N >> 7), st + R::a_bytes + R::b_bytes + w * 256);
+        }
+    };
+
+    // ---- fragment reads of one K tile: item r of NR (B blocks, then A row
+    // blocks, then the fp8 scales); LDS byte offsets are fixed per lane ----
+    constexpr int NBR = FP8 ? 8 : 16;
+    constexpr int NR = NBR + R::mi + (FP8 ? 1 : 0);
+    const int a_off = (wr * (BM / 2) + (lane & 15)) * 64 + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
+    const int i16 = lane & 15, gq = lane >> 4;
+    auto read = [&](Frags<R::mi, FP8> &f, int r, int stage) {
+        const uint8_t *st = lds + stage * R::stage;
+        if (r < NBR) {
+            const uint32_t bs = lds_addr(st + R::a_bytes);
+            if constexpr (FP8) {
+                const int j = r;
+                const int nb = SWIGLU ? 128 * (j >> 2) + 64 * wc + 16 * (j & 3) : 128 * wc + 16 * j;
+                const int k = 8 * gq + (i16 >> 1);
+                f.raw[j][0] = ds_tr8(bs + k * 256 + 16 * ((nb >> 4) ^ bswz8(k)) + 8 * (i16 & 1));
+            } else {
+                const int j = r >> 1, kh = r & 1;
+                const int nb = SWIGLU ? 128 * (j >> 2) + 64 * wc + 16 * (j & 3) : 128 * wc + 16 * j;
+                const int k = 8 * gq + 4 * kh + (i16 >> 2);
+                const int n = nb + 4 * (i16 & 3);
+                f.raw[j][kh] = ds_tr16(bs + k * 512 + 16 * ((n >> 3) ^ bswz16(k)) + 2 * (n & 7));
+            }
+        } else if (r < NBR + R::mi) {
+            const int m = r - NBR;
+            f.a[m] = *reinterpret_cast<const bf16x8 *>(st + a_off + m * 16 * 64);
+        } else if constexpr (FP8) {
+            const float *sc = reinterpret_cast<const float *>(st + R::a_bytes + R::b_bytes + w * 256);
+            f.s0 = sc[0];
+            f.s1 = sc[1];
+        }
+    };
+
+    // completes this wavefront's reads of f, hands the transposed reads to
+    // the compiler and forms the B operands (fp8: exact E4M3 -> bf16, scale
+    // 1; K order kept, byte e of a read being K row e)
+    auto land = [&](Frags<R::mi, FP8> &f) {
+        wait_lds();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+#pragma unroll
+            for (int h = 0; h < (FP8 ? 1 : 2); ++h) fence(f.raw[j][h]);
+            u32x4 v;
+            if constexpr (FP8) {
+                v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][0], 1.0f, false));
+                v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][0], 1.0f, true));
+                v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][1], 1.0f, false));
+                v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][1], 1.0f, true));
+            } else {
+                v[0] = f.raw[j][0][0];
+                v[1] = f.raw[j][0][1];
+                v[2] = f.raw[j][1][0];
+                v[3] = f.raw[j][1][1];
+            }
+            f.b[j] = __builtin_bit_cast(bf16x8, v);
+        }
+    };
+
+    f32x4 acc[R::mi][8];
+    f32x4 part[FP8 ? R::mi : 1][8];  // fp8: the current 128-deep K block
+#pragma unroll
+    for (int m = 0; m < R::mi; ++m)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            acc[m][j] = f32x4{};
+            if constexpr (FP8) part[m][j] = f32x4{};
+        }
+
+    // the 8 MFMAs of row block m, kept together as one scheduling group
+    auto mma_rows = [&](const Frags<R::mi, FP8> &f, int m) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (FP8) part[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[m], f.b[j], part[m][j], 0, 0, 0);
+            else acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // fp8: add the closed 128-deep K block, times its block scales
+    auto promote = [&](const Frags<R::mi, FP8> &f) {
+        if constexpr (FP8) {
+#pragma unroll
+            for (int m = 0; m < R::mi; ++m)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float s = (SWIGLU && j >= 4) ? f.s1 : f.s0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[m][j][i] += part[m][j][i] * s;
+                    part[m][j] = f32x4{};
+                }
+        }
+    };
+
+    // One K tile per step, with a fixed number of copies in flight. Step kt
+    // multiplies tile kt (fragments already in registers) row block by row
+    // block; after the first block it waits for tile kt+1 (all but the S-2
+    // newest tiles' copies), publishes it with the barrier (which also means
+    // every wavefront has finished reading the stage tile kt came from), and
+    // spreads over the remaining blocks the copies of tile kt+S into that
+    // stage and the fragment reads of tile kt+1, so the matrix cores stay
+    // busy while they issue. Past the last tile the copies repeat the last
+    // tile into stages nobody reads, keeping the counts fixed; the read after
+    // the last tile is discarded.
+    const int nk = p.K / kBK;
+    Frags<R::mi, FP8> fa, fb;
+#pragma unroll
+    for (int t = 0; t < S; ++t)
+#pragma unroll
+        for (int q = 0; q < NC; ++q) copy(q, min(t, nk - 1), t);
+    wait_vm<(S - 1) * R::per_tile>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read(fa, r, 0);
+    land(fa);
+    int stage = 0;  // kt % S
+    for (int kt = 0; kt < nk; ++kt) {
+        const int nstage = stage + 1 == S ? 0 : stage + 1;
+        const int src = min(kt + S, nk - 1);
+        mma_rows(fa, 0);
+        wait_vm<(S - 2) * R::per_tile>();
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int c = 0; c < R::mi - 1; ++c) {
+#pragma unroll
+            for (int q = c * NC / (R::mi - 1); q < (c + 1) * NC / (R::mi - 1); ++q) copy(q, src, stage);
+#pragma unroll
+            for (int r = c * NR / (R::mi - 1); r < (c + 1) * NR / (R::mi - 1); ++r) read(fb, r, nstage);
+            mma_rows(fa, c + 1);
+        }
+        if constexpr (FP8)
+            if ((kt & 3) == 3) promote(fa);
+        land(fb);
+        fa = fb;
+        stage = nstage;
+    }
+
+    // ---- epilogue: stage the bf16 tile in LDS, then 16-byte row stores ----
+    constexpr int LD = Out<SWIGLU>::ld;
+    __syncthreads();  // every wavefront is done with the ring
+    uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);
+#pragma unroll
+    for (int m = 0; m < R::mi; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wr * (BM / 2) + m * 16 + 4 * (lane >> 4) + i;
+            if (SWIGLU) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v = silu_f32(acc[m][j][i]) * acc[m][j + 4][i];
+                    Cs[r * LD + 64 * wc + 16 * j + i16] = __builtin_bit_cast(uint16_t, (__bf16)v);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    Cs[r * LD + 128 * wc + 16 * j + i16] = __builtin_bit_cast(uint16_t, (__bf16)acc[m][j][i]);
+            }
+        }
+    __syncthreads();
+    constexpr int W = Out<SWIGLU>::width;
+    constexpr int chunks_per_row = W / 8;
+    uint16_t *Cg = reinterpret_cast<uint16_t *>(p.C);
+    for (int idx = tid; idx < BM * chunks_per_row; idx += kThreads) {
+        const int r = idx / chunks_per_row, cc = idx % chunks_per_row;
+        const int row = row0 + r, col = n0 + 8 * cc;
+        if (row < row_end && col < p.N)
+            *reinterpret_cast<u32x4 *>(Cg + (long long)row * p.ldc + col) =
+                *reinterpret_cast<const u32x4 *>(Cs + r * LD + 8 * cc);
+    }
+}
+
+template <int WT, bool SWIGLU, int BM>
+inline hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
+    const int W = Out<SWIGLU>::width;
+    const int nN = (p.N + W - 1) / W;
+    const long long mt_cap = p.tiles ? p.max_tiles : (p.M + BM - 1) / BM;
+    long long blocks = mt_cap * nN;
+    blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((tiled_gemm_kernel<WT, SWIGLU, BM>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p, nN);
+    return hipGetLastError();
+}
+
+template <int WT, int BM>
+inline hipError_t launch_bm(const GemmProblem &p, bool swiglu, hipStream_t s) {
+    return swiglu ? launch_t<WT, true, BM>(p, s) : launch_t<WT, false, BM>(p, s);
+}
+
+}  // namespace tiled
+
+// per-height launchers (one translation unit each)
+hipError_t launch_tiled_bm128(const GemmProblem &p, WType wt, bool swiglu, hipStream_t s);
+hipError_t launch_tiled_bm256(const GemmProblem &p, WType wt, bool swiglu, hipStream_t s);
+
+}  // namespace moe
