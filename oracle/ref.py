@@ -83,6 +83,60 @@ def dequant_blocks(codes, scales, block: int = 128) -> np.ndarray:
     return (q * s[:, None, :, None]).reshape(R, C)
 
 
+def e4m3_encode(x) -> np.ndarray:
+    """float -> OCP E4M3 code: the representable value nearest to x, ties to
+    the code with an even mantissa (its lowest bit clear), magnitudes at or
+    above the largest finite value 448 saturating to it; the sign bit is x's
+    (so -0.0 -> 0x80). NaN -> 0x7f. From the format definition in
+    `e4m3_decode`; the decoded values are searched, nothing is computed by
+    bit manipulation.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    pos_codes = np.arange(0x7f, dtype=np.int64)          # 0x00..0x7e: the finite non-negative codes
+    pos_vals = _e4m3_table()[pos_codes]                   # ascending
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(pos_vals, a, side="left"), 0, pos_codes.size - 1)
+    lo = np.clip(hi - 1, 0, pos_codes.size - 1)
+    d_lo, d_hi = a - pos_vals[lo], pos_vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (pos_codes[hi] % 2 == 0))
+    code = np.where(pick_hi, pos_codes[hi], pos_codes[lo])
+    code = np.where(np.signbit(x), code | 0x80, code)
+    return np.where(np.isnan(x), 0x7f, code).astype(np.uint8)
+
+
+def quantize_rows_e4m3(x, group: int = 128):
+    """Activation quantisation before expert compute (page "MOE推理流程解析"
+    §三 names the choice of quantising activations before dispatch or just
+    before the expert GEMM; both give these values for per-row scales).
+
+    Per row and `group`-column block, in float32 as a kernel would compute it:
+    amax = max |x|, s = amax / 448 (s = 1 when amax = 0), q = E4M3(x / s)
+    (round to nearest even, saturating). Returns (codes uint8 [R, C], scales
+    float32 [R, C / group]).
+    """
+    x32 = np.asarray(to_f64(x), dtype=np.float32)
+    R, C = x32.shape
+    xg = x32.reshape(R, C // group, group)
+    amax = np.abs(xg).max(axis=2)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = e4m3_encode((xg / s[:, :, None]).astype(np.float32)).reshape(R, C)
+    return q, s
+
+
+def dequant_rows(codes, scales, group: int = 128) -> np.ndarray:
+    """x[r, c] = decode(code[r, c]) * scale[r, c // group], exact in float64."""
+    q = _e4m3_table()[np.asarray(codes, dtype=np.uint8)]
+    s = np.asarray(scales, dtype=np.float64)
+    R, C = q.shape
+    return (q.reshape(R, C // group, group) * s[:, :, None]).reshape(R, C)
+
+
+def _act_quant(x) -> np.ndarray:
+    """x rounded through quantize_rows_e4m3 and back (float64)."""
+    q, s = quantize_rows_e4m3(np.asarray(x, dtype=np.float64).astype(np.float32))
+    return dequant_rows(q, s)
+
+
 # ----------------------------------------------------------------------------
 # Router: page "MoE serving production quirks", memory-paradox section (linear
 # projection and softmax over all experts); page "MOE推理流程解析" §三 (top-k
@@ -178,10 +232,20 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_ffn(x, W1, W3, W2) -> np.ndarray:
-    """y = (silu(x @ W1) * (x @ W3)) @ W2 for rows x [n, H]."""
+def swiglu_ffn(x, W1, W3, W2, act_quant: bool = False) -> np.ndarray:
+    """y = (silu(x @ W1) * (x @ W3)) @ W2 for rows x [n, H].
+
+    act_quant (diagnosis only: the exact result is the reference): x and h
+    pass through E4M3 activation quantisation (`quantize_rows_e4m3`) before
+    their projections, as a W8A8 kernel computes.
+    """
     x = np.asarray(x, dtype=np.float64)
-    return (silu(x @ W1) * (x @ W3)) @ W2
+    if act_quant:
+        x = _act_quant(x)
+    h = silu(x @ W1) * (x @ W3)
+    if act_quant:
+        h = _act_quant(h)
+    return h @ W2
 
 
 def grouped_ffn(Xrows, offsets, expert) -> np.ndarray:
@@ -287,11 +351,12 @@ def forward(layer: Layer) -> dict:
                 row_src=row_src, assign_row=assign_row, Xp=Xp, Yp=Yp, S=S, Y=Y)
 
 
-def forward_tokens(layer: Layer, tokens, idx=None) -> dict:
+def forward_tokens(layer: Layer, tokens, idx=None, act_quant: bool = False) -> dict:
     """fp64 outputs for a subset of tokens only (the layer is per-token
     independent: each token's output depends on its own row, its own routing
     and the shared weights). `idx` optionally fixes the routing decision
-    (rows for the sampled tokens) instead of re-deriving it.
+    (rows for the sampled tokens) instead of re-deriving it. `act_quant`
+    mirrors activation quantisation in the expert FFNs (see swiglu_ffn).
     Returns logits, idx, w, per-token expert outputs y[t, j] and Y for the
     sampled tokens, in the given order.
     """
@@ -307,10 +372,10 @@ def forward_tokens(layer: Layer, tokens, idx=None) -> dict:
     for e in np.unique(idx):
         W1, W3, W2 = layer.expert(int(e))
         ts, js = np.nonzero(idx == e)
-        y[ts, js] = swiglu_ffn(X[ts], W1, W3, W2)
+        y[ts, js] = swiglu_ffn(X[ts], W1, W3, W2, act_quant)
     Y = np.einsum("tj,tjh->th", w, y)
     S = None
     if layer.has_shared():
-        S = swiglu_ffn(X, *layer.shared())
+        S = swiglu_ffn(X, *layer.shared(), act_quant)
         Y = Y + S
     return dict(tokens=tokens, logits=logits, idx=idx, w=w, y=y, S=S, Y=Y)
