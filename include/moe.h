@@ -71,9 +71,17 @@ typedef enum {
 
 /* Expert-FFN kernel choice. AUTO picks the row-streaming (batched GEMV) path
  * when the average rows per expert is small (decode) and the LDS-tiled
- * grouped GEMM otherwise (prefill). Both give results within the same
- * tolerance of the exact layer; the forced values exist for testing. */
-typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_TILED = 2 } moe_ffn_path;
+ * grouped GEMM otherwise (prefill); for FP8 weights the tiled choice is
+ * TILED_A8. All give results within the same tolerance of the exact layer;
+ * the forced values exist for testing and comparison.
+ *  GEMV, TILED: activations stay in act_dt; FP8 weights are decoded exactly
+ *    and each 128-deep K block is scaled (W8A16).
+ *  TILED_A8 (FP8 weights only, H and F multiples of 128): the expert inputs
+ *    (token rows, then h) are quantised to E4M3 per row and 128-column group
+ *    with scale amax/448 (page "MOE推理流程解析" §三: activations quantised
+ *    before the expert GEMM) and multiplied on the FP8 matrix cores (W8A8).
+ *    In moe_forward it needs Fs == 0 or Fs == F. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_TILED = 2, MOE_PATH_TILED_A8 = 3 } moe_ffn_path;
 
 /* Static string for a status code (host memory, never NULL). */
 const char *moe_status_string(moe_status s);
@@ -145,6 +153,21 @@ moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M
                            void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * E4M3 activation quantisation (the W8A8 path's input step; page
+ * "MOE推理流程解析" §三: activations may be quantised before dispatch or
+ * before the expert GEMM). For output row r (input row row_src[r] / gk, or r
+ * when row_src is NULL) and each 128-column group c:
+ *   s = amax / 448 over the group's |x| (s = 1 when amax = 0),
+ *   Q[r, j] = E4M3(x[j] / s) rounded to nearest, ties to even, saturating
+ *   at +-448;  S[r, c] = s.
+ * All arithmetic fp32 (correctly rounded division). X [*, ldx] bf16 with
+ * ldx >= C and ldx % 8 == 0; C a multiple of 128; Q [R, C] uint8 codes,
+ * S [R, C/128] fp32. Deterministic, bit-exact.
+ * ------------------------------------------------------------------------- */
+moe_status moe_quantize_e4m3_rows(const void *X, moe_dtype x_dt, long long ldx, const int32_t *row_src,
+                                  int gk, int R, int C, uint8_t *Q, float *S, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Combine / unpermute:
  *   Y[t, :] = sum_{j<k} topk_w[t,j] * Yp[assign_row[t*k+j], :]  (+ S[t, :])
  * summed in fp32 in ascending j, then S added with weight 1, then rounded to
@@ -184,10 +207,10 @@ enum {
     MOE_EV_START = 0,
     MOE_EV_ROUTE,          /* router GEMM + top-k done */
     MOE_EV_PERMUTE,        /* counts / offsets / permutation done */
-    MOE_EV_SCHEDULE,       /* tile list built */
+    MOE_EV_SCHEDULE,       /* tile list built (and, on TILED_A8, X quantised) */
     MOE_EV_GATE_UP,        /* routed gate/up GEMM + SwiGLU done */
     MOE_EV_SHARED_GATE_UP, /* shared expert gate/up done (no-op without one) */
-    MOE_EV_DOWN,           /* routed down projection done */
+    MOE_EV_DOWN,           /* routed down projection done (TILED_A8: h quantised first) */
     MOE_EV_SHARED_DOWN,    /* shared expert down projection done */
     MOE_EV_COMBINE,        /* combine done: Y written */
     MOE_N_EVENTS

@@ -8,8 +8,8 @@ Python binding, with torch providing device memory and streams.
 """
 from ._lib import (
     LIB_PATH, MOE_N_EVENTS, STAGES, MoEError, MoELayer, StageEvents, combine, grouped_ffn, lib,
-    permute, route,
+    permute, quantize_e4m3_rows, route,
 )
 
 __all__ = ["LIB_PATH", "MOE_N_EVENTS", "STAGES", "MoEError", "MoELayer", "StageEvents", "combine",
-           "grouped_ffn", "lib", "permute", "route"]
+           "grouped_ffn", "lib", "permute", "quantize_e4m3_rows", "route"]

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
-PATHS = {"auto": 0, "gemv": 1, "tiled": 2}
+PATHS = {"auto": 0, "gemv": 1, "tiled": 2, "tiled_a8": 3}
 
 # Every function include/moe.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -31,6 +31,7 @@ SIGNATURES = {
     "moe_grouped_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_grouped_ffn": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _P, _I,
                              _P, _SZ, _P]),
+    "moe_quantize_e4m3_rows": (_I, [_P, _I, ctypes.c_longlong, _P, _I, _I, _I, _P, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _I, _P, _P]),
     "moe_forward_workspace_bytes": (_SZ, [_P, _I]),
     "moe_forward": (_I, [_P, _P, _I, _P, _P, _SZ, _P, _P, _P, _P, _P, _P]),
@@ -175,6 +176,21 @@ def grouped_ffn(Xin, offsets, W1, W3, W2, S1=None, S3=None, S2=None, row_src=Non
         _ptr(Xin), _ptr(row_src), k, M, _ptr(offsets), G, H, F, _ptr(W1), _ptr(W3), _ptr(W2), wdt,
         _ptr(S1), _ptr(S3), _ptr(S2), adt, _ptr(Yp), p, _ptr(ws), nbytes, _stream()))
     return Yp
+
+
+def quantize_e4m3_rows(X, row_src=None, k: int = 1, R: int | None = None):
+    """E4M3 codes [R, C] (uint8) and fp32 scales [R, C/128] of bf16 rows
+    X[row_src[r] // k] (X[r] without row_src), per 128-column group."""
+    _dev(X, row_src)
+    if row_src is not None:
+        _i32(row_src)
+    R = (row_src.numel() if row_src is not None else X.shape[0]) if R is None else R
+    C = X.shape[1]
+    Q = torch.empty((R, C), dtype=torch.uint8, device=X.device)
+    S = torch.empty((R, C // 128), dtype=torch.float32, device=X.device)
+    _check("moe_quantize_e4m3_rows", lib().moe_quantize_e4m3_rows(
+        _ptr(X), act_dtype(X), X.stride(0), _ptr(row_src), k, R, C, _ptr(Q), _ptr(S), _stream()))
+    return Q, S
 
 
 def combine(Yp, assign_row, topk_w, S=None):

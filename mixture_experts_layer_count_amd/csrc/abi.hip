@@ -59,18 +59,33 @@ moe_status check_ffn_dims(int H, int F, moe_dtype w_dt) {
 // ---------------------------------------------------------------------------
 struct FfnPlan {
     bool tiled;
+    bool a8;      // tiled with E4M3 activations (W8A8)
     int bm;
     int ksplit2;  // split-K of the down projection (row-streaming path)
     int kchunk2;
 };
 
-FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path) {
+bool path_ok(moe_ffn_path path) {
+    return path == MOE_PATH_AUTO || path == MOE_PATH_GEMV || path == MOE_PATH_TILED || path == MOE_PATH_TILED_A8;
+}
+
+// a8_ok: the caller can run the W8A8 form (AUTO picks it for FP8 weights
+// whenever it picks the tiled path).
+FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path, bool a8_ok = true) {
     FfnPlan p{};
     const WType wt = wtype(w_dt);
     const bool can_tile = tiled_gemm_supports(wt, F, H) && tiled_gemm_supports(wt, H, F);
-    if (path == MOE_PATH_TILED) p.tiled = can_tile;
-    else if (path == MOE_PATH_GEMV) p.tiled = false;
-    else p.tiled = can_tile && (long long)M >= 48LL * G;
+    const bool can_a8 = a8_ok && w_dt == MOE_FP8_E4M3 && tiled_a8_supports(F, H) && tiled_a8_supports(H, F);
+    if (path == MOE_PATH_TILED_A8) {
+        p.tiled = p.a8 = can_a8;
+    } else if (path == MOE_PATH_TILED) {
+        p.tiled = can_tile;
+    } else if (path == MOE_PATH_GEMV) {
+        p.tiled = false;
+    } else {
+        p.tiled = can_tile && (long long)M >= 48LL * G;
+        p.a8 = p.tiled && can_a8;
+    }
     p.bm = p.tiled ? tiled_gemm_bm(wt, M, G) : kGemvBM;
     p.ksplit2 = 1;
     p.kchunk2 = F;
@@ -93,6 +108,8 @@ struct FfnWs {
     int32_t *tiles, *n_tiles, *group_tile_start;
     void *h;     // [rows][hw] SwiGLU activations
     void *part;  // Yp: [ksplit][rows][H] fp32 (row-streaming) or [rows][H] act_dt (tiled)
+    uint8_t *xq, *hq;  // W8A8: E4M3 codes of the expert inputs [xrows][H] and of h [rows][hw]
+    float *xs, *hs;    // and their per-row 128-column scales
 };
 
 // Weights of the optional extra group: the always-on shared expert run in
@@ -105,8 +122,9 @@ struct ExtraGroup {
 
 long long max_tiles_for(long long rows, int groups, int bm) { return (rows + bm - 1) / bm + groups; }
 
+// xrows: rows of quantised expert input (W8A8 only).
 size_t ffn_ws_carve(Carver &c, FfnWs &w, const FfnPlan &p, int rows, int groups, int H, int hw,
-                    moe_dtype act_dt) {
+                    moe_dtype act_dt, int xrows) {
     const long long max_tiles = max_tiles_for(rows, groups, p.bm);
     w.tiles = static_cast<int32_t *>(c.take(sizeof(int32_t) * 4 * max_tiles));
     w.n_tiles = static_cast<int32_t *>(c.take(sizeof(int32_t)));
@@ -114,6 +132,12 @@ size_t ffn_ws_carve(Carver &c, FfnWs &w, const FfnPlan &p, int rows, int groups,
     w.h = c.take(dt_size(act_dt) * (size_t)rows * hw);
     w.part = p.tiled ? c.take(dt_size(act_dt) * (size_t)rows * H)
                      : c.take(sizeof(float) * (size_t)p.ksplit2 * rows * H);
+    if (p.a8) {
+        w.xq = static_cast<uint8_t *>(c.take((size_t)xrows * H));
+        w.xs = static_cast<float *>(c.take(sizeof(float) * (size_t)xrows * (H / 128)));
+        w.hq = static_cast<uint8_t *>(c.take((size_t)rows * hw));
+        w.hs = static_cast<float *>(c.take(sizeof(float) * (size_t)rows * (hw / 128)));
+    }
     return c.used;
 }
 
@@ -196,8 +220,17 @@ int chunk_for(int K, int nsplit, moe_dtype w_dt) {
 
 hipError_t run_gemm(const FfnPlan &p, const GemmProblem &g, WType wt, bool swiglu, bool out_bf16,
                     hipStream_t s) {
+    if (p.a8) return out_bf16 ? launch_tiled_a8(g, swiglu, s) : hipErrorInvalidValue;
     return p.tiled ? launch_tiled_gemm(g, wt, swiglu, out_bf16, p.bm, s)
                    : launch_stream_gemm(g, wt, swiglu, out_bf16, s);
+}
+
+// W8A8 operands: A holds E4M3 codes of rows of `width` values with scales As.
+void set_a8(GemmProblem &g, const uint8_t *q, const float *sc, int width) {
+    g.A = q;
+    g.lda = width;
+    g.As = sc;
+    g.as_ld = width / 128;
 }
 
 }  // namespace
@@ -323,11 +356,15 @@ moe_status moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *co
 size_t moe_grouped_ffn_workspace_bytes(int M, int G, int H, int F, moe_dtype act_dt,
                                        moe_dtype w_dt, moe_ffn_path path) {
     if (M < 0 || G < 1 || H < 1 || F < 1) return 0;
-    FfnPlan p = plan_ffn(M, G, H, F, w_dt, path);
+    const FfnPlan p = plan_ffn(M, G, H, F, w_dt, path);
     Carver c(nullptr);
     FfnWs w{};
-    p.tiled = false;  // the fp32 partial buffer is the larger of the two formats
-    return ffn_ws_carve(c, w, p, M, G, H, F, act_dt);
+    size_t bytes = ffn_ws_carve(c, w, p, M, G, H, F, act_dt, M);
+    FfnPlan q = p;  // the fp32 partials of the row-streaming form can be larger
+    q.tiled = q.a8 = false;
+    Carver c2(nullptr);
+    const size_t b2 = ffn_ws_carve(c2, w, q, M, G, H, F, act_dt, M);
+    return bytes > b2 ? bytes : b2;
 }
 
 moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M,
@@ -339,26 +376,39 @@ moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M
     if (!pair_ok(act_dt, w_dt)) return MOE_ERR_UNSUPPORTED;
     moe_status st = check_ffn_dims(H, F, w_dt);
     if (st != MOE_OK) return st;
-    if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_TILED)
-        return MOE_ERR_INVALID_ARG;
+    if (!path_ok(path)) return MOE_ERR_INVALID_ARG;
+    if (path == MOE_PATH_TILED_A8 && w_dt != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
     if (M == 0) return MOE_OK;
     if (!Xin || !offsets || !W1 || !W3 || !W2 || !Yp) return MOE_ERR_INVALID_ARG;
     const bool fp8 = w_dt == MOE_FP8_E4M3;
     if (fp8 != (S1 != nullptr) || fp8 != (S3 != nullptr) || fp8 != (S2 != nullptr))
         return MOE_ERR_INVALID_ARG;
     const FfnPlan p = plan_ffn(M, G, H, F, w_dt, path);
-    if (path == MOE_PATH_TILED && !p.tiled) return MOE_ERR_UNSUPPORTED;
+    if ((path == MOE_PATH_TILED || path == MOE_PATH_TILED_A8) && !p.tiled) return MOE_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < moe_grouped_ffn_workspace_bytes(M, G, H, F, act_dt, w_dt, path))
         return MOE_ERR_WORKSPACE_TOO_SMALL;
     Carver c(ws);
     FfnWs w{};
-    ffn_ws_carve(c, w, p, M, G, H, F, act_dt);
+    ffn_ws_carve(c, w, p, M, G, H, F, act_dt, M);
     const WType wt = wtype(w_dt);
     const bool bf = act_dt == MOE_BF16;
     const int max_tiles = (int)max_tiles_for(M, G, p.bm);
     const ExtraGroup none{};
 
     MOE_TRY(launch_build_tiles(offsets, G, 0, p.bm, w.tiles, w.n_tiles, w.group_tile_start, stream));
+    if (p.a8) {
+        // E4M3 input rows (gathered here), gate/up, E4M3 h, down
+        MOE_TRY(launch_quant_rows(Xin, H, row_src, k, M, H, w.xq, w.xs, stream));
+        GemmProblem g1 = gate_up_problem(nullptr, nullptr, 1, &w, G, max_tiles, M, H, F, W1, W3, S1, S3, none, M,
+                                         w.h);
+        set_a8(g1, w.xq, w.xs, H);
+        MOE_TRY(run_gemm(p, g1, wt, true, true, stream));
+        MOE_TRY(launch_quant_rows(w.h, F, nullptr, 1, M, F, w.hq, w.hs, stream));
+        GemmProblem g2 = down_problem(nullptr, &w, G, max_tiles, M, H, F, W2, S2, none, M, Yp, 0, 1, F);
+        set_a8(g2, w.hq, w.hs, F);
+        MOE_TRY(run_gemm(p, g2, wt, false, true, stream));
+        return MOE_OK;
+    }
     GemmProblem g1 = gate_up_problem(Xin, row_src, k, &w, G, max_tiles, M, H, F, W1, W3, S1, S3, none, M, w.h);
     MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
     if (p.tiled) {
@@ -373,6 +423,16 @@ moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M
                                      act_dt, Yp, stream));
     }
     return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+moe_status moe_quantize_e4m3_rows(const void *X, moe_dtype x_dt, long long ldx, const int32_t *row_src,
+                                  int gk, int R, int C, uint8_t *Q, float *S, hipStream_t stream) {
+    if (R < 0 || C < 1 || gk < 1 || ldx < C) return MOE_ERR_INVALID_ARG;
+    if (x_dt != MOE_BF16 || C % 128 || ldx % 8) return MOE_ERR_UNSUPPORTED;
+    if (R == 0) return MOE_OK;
+    if (!X || !Q || !S) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_quant_rows(X, ldx, row_src, gk, R, C, Q, S, stream));
 }
 
 // ---------------------------------------------------------------------------
@@ -397,8 +457,9 @@ moe_status check_desc(const moe_layer_desc *d) {
     moe_status st = check_ffn_dims(d->H, d->F, d->w_dt);
     if (st != MOE_OK) return st;
     if (d->Fs > 0 && (st = check_ffn_dims(d->H, d->Fs, d->w_dt)) != MOE_OK) return st;
-    if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_GEMV && d->path != MOE_PATH_TILED)
-        return MOE_ERR_INVALID_ARG;
+    if (!path_ok(d->path)) return MOE_ERR_INVALID_ARG;
+    if (d->path == MOE_PATH_TILED_A8 && (d->w_dt != MOE_FP8_E4M3 || (d->Fs > 0 && d->Fs != d->F)))
+        return MOE_ERR_UNSUPPORTED;
     if (!d->Wg || !d->W1 || !d->W3 || !d->W2) return MOE_ERR_INVALID_ARG;
     const bool fp8 = d->w_dt == MOE_FP8_E4M3;
     if (fp8 != (d->S1 != nullptr) || fp8 != (d->S3 != nullptr) || fp8 != (d->S2 != nullptr))
@@ -434,8 +495,9 @@ ForwardWs carve_forward(const moe_layer_desc *d, int T, void *base) {
     f.assign_row = static_cast<int32_t *>(c.take(sizeof(int32_t) * (size_t)A));
     f.perm_ws = c.take(permute_ws_bytes(A, d->E));
     f.route_ws = c.take(route_ws_bytes(T, d->H, d->E));
-    f.plan = plan_ffn(A, d->E, d->H, d->F, d->w_dt, d->path);
     f.combined = d->Fs > 0 && d->Fs == d->F;
+    // W8A8 needs the shared expert (if any) inside the routed launches
+    f.plan = plan_ffn(A, d->E, d->H, d->F, d->w_dt, d->path, d->Fs == 0 || f.combined);
     if (d->Fs > 0 && !f.combined) {
         // separate shared-expert launches; one Yp buffer holds routed rows
         // then shared rows, so both use one format
@@ -449,7 +511,7 @@ ForwardWs carve_forward(const moe_layer_desc *d, int T, void *base) {
     const int rows = A + (d->Fs > 0 ? T : 0);
     const int groups = d->E + (f.combined ? 1 : 0);
     const int hw = d->F > d->Fs ? d->F : d->Fs;
-    ffn_ws_carve(c, f.ffn, f.plan, rows, groups, d->H, hw, d->act_dt);
+    ffn_ws_carve(c, f.ffn, f.plan, rows, groups, d->H, hw, d->act_dt, T);
     f.bytes = c.used;
     return f;
 }
@@ -514,9 +576,13 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     // 3. expert FFN; with `combined` the shared expert is group E of the same launches
     MOE_TRY(launch_build_tiles(f.offsets, E, ex.rows, p.bm, f.ffn.tiles, f.ffn.n_tiles, f.ffn.group_tile_start,
                                stream));
+    // W8A8: the token rows are quantised once (per-row scales, so the gather
+    // in the GEMM's loads picks the same codes as quantising gathered rows)
+    if (p.a8) MOE_TRY(launch_quant_rows(X, H, nullptr, 1, T, H, f.ffn.xq, f.ffn.xs, stream));
     MOE_TRY(mark(MOE_EV_SCHEDULE));
     GemmProblem g1 = gate_up_problem(X, f.row_src, d->k, &f.ffn, E, max_tiles, M, H, F, d->W1, d->W3, d->S1,
                                      d->S3, ex, A, f.ffn.h);
+    if (p.a8) set_a8(g1, f.ffn.xq, f.ffn.xs, H);
     MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
     MOE_TRY(mark(MOE_EV_GATE_UP));
     void *h_s = static_cast<char *>(f.ffn.h) + hb * (size_t)A * hw;
@@ -534,6 +600,10 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     if (p.tiled) {
         GemmProblem g2 = down_problem(f.ffn.h, &f.ffn, E, max_tiles, M, H, F, d->W2, d->S2, ex, A, f.ffn.part,
                                       0, 1, F);
+        if (p.a8) {
+            MOE_TRY(launch_quant_rows(f.ffn.h, hw, nullptr, 1, M, F, f.ffn.hq, f.ffn.hs, stream));
+            set_a8(g2, f.ffn.hq, f.ffn.hs, F);
+        }
         MOE_TRY(run_gemm(p, g2, wt, false, bf, stream));
         MOE_TRY(mark(MOE_EV_DOWN));
         void *Sp = static_cast<char *>(f.ffn.part) + hb * (size_t)A * H;

@@ -112,6 +112,10 @@ struct GemmProblem {
     long long c_split_stride;
     int ksplit;
     int kchunk;               // K elements per split (multiple of 32, or 128 for fp8)
+    // fp8 activations (W8A8 tiled path): A holds E4M3 codes and As their
+    // scales, [row][as_ld] with one scale per 128 K, rows mapped as A's
+    const float *As = nullptr;
+    int as_ld = 0;
 };
 
 hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,
@@ -125,6 +129,19 @@ hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool o
                              hipStream_t s);
 int tiled_gemm_bm(WType wt, long long rows, int groups);  // rows per tile for this row distribution
 bool tiled_gemm_supports(WType wt, int N, int K);
+
+// W8A8 variant of the LDS-tiled grouped GEMM (fp8 weights and fp8
+// activations with per-row 128-column scales, p.As): 128-row tiles built with
+// bm = 128; output bf16. Returns hipErrorInvalidValue for unsupported shapes.
+hipError_t launch_tiled_a8(const GemmProblem &p, bool swiglu, hipStream_t s);
+bool tiled_a8_supports(int N, int K);
+
+// E4M3 quantisation of bf16 rows: for each row and 128-column group,
+// s = amax / 448 (1 when amax is 0), q = E4M3(x / s) rounded to nearest even
+// and saturated. Output row r reads X[row_src[r] / gk] (X[r] if row_src is
+// NULL; row stride ldx elements) -> Q [R][C], S [R][C/128].
+hipError_t launch_quant_rows(const void *X, long long ldx, const int32_t *row_src, int gk, int R, int C,
+                             uint8_t *Q, float *S, hipStream_t s);
 
 // Tile list (group, row0, row_end, 0) for G groups of rows given by offsets
 // plus, when extra_rows > 0, group G = rows [offsets[G], offsets[G] +

@@ -1,0 +1,76 @@
+// E4M3 activation quantisation for the W8A8 expert GEMMs.
+//
+// Page "MOE推理流程解析" §三: activations may be quantised before dispatch
+// (fewer bytes moved) or dispatched in higher precision and quantised before
+// the expert GEMM. Scales here are per row and 128-column group, so quantising
+// the token rows once before the gather gives the same codes as quantising
+// the gathered rows.
+//
+// One 16-lane group per (row, 128-column group); each lane owns 8 consecutive
+// bf16 values (one 16-byte load). amax is reduced across the 16 lanes with
+// xor shuffles; s = amax / 448 (correctly rounded fp32 division), and each
+// value is divided by s, clamped to +-448 (the conversion gives NaN past
+// 480 rather than saturating) and rounded to nearest even by
+// v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t *X, long long ldx, const int32_t *row_src,
+                                                         int gk, int R, int C, uint8_t *Q, float *S) {
+    const long long gid = ((long long)blockIdx.x * 256 + threadIdx.x) >> 4;
+    const int sub = threadIdx.x & 15;
+    const int gpr = C >> 7;  // groups per row
+    const bool ok = gid < (long long)R * gpr;
+    const long long r = ok ? gid / gpr : 0;
+    const int gc = ok ? (int)(gid - r * gpr) : 0;
+
+    u32x4 raw = {0, 0, 0, 0};
+    if (ok) {
+        const long long xr = row_src ? (long long)(row_src[r] / gk) : r;
+        raw = *reinterpret_cast<const u32x4 *>(X + xr * ldx + 128 * gc + 8 * sub);
+    }
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_lo(raw[i]);
+        v[2 * i + 1] = bf16_hi(raw[i]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 16));
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(v[4 * h + i] / s, -448.0f), 448.0f);
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], p, true);
+        w[h] = (uint32_t)p;
+    }
+    if (!ok) return;
+    *reinterpret_cast<u32x2 *>(Q + r * C + 128 * gc + 8 * sub) = u32x2{w[0], w[1]};
+    if (sub == 0) S[r * gpr + gc] = s;
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(const void *X, long long ldx, const int32_t *row_src, int gk, int R, int C,
+                             uint8_t *Q, float *S, hipStream_t s) {
+    if (R < 0 || C < 128 || C % 128 || ldx < C || gk < 1) return hipErrorInvalidValue;
+    if (R == 0) return hipSuccess;
+    const long long threads = (long long)R * (C / 128) * 16;
+    const long long blocks = (threads + 255) / 256;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t *>(X), ldx, row_src, gk, R, C, Q, S);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -22,14 +22,14 @@ pinned by the worked example, closed forms, special cases and a brute-force
 per-token loop on small inputs.
 """
 from .ref import (
-    to_f64, e4m3_decode, e4m3_encode, quantize_rows_e4m3, dequant_rows, dequant_blocks, router_logits, softmax, select_topk,
+    to_f64, e4m3_decode, e4m3_encode, quantize_rows_e4m3, dequant_rows, round_bf16, dequant_blocks, router_logits, softmax, select_topk,
     route, routing_weights, permute, silu, swiglu_ffn, grouped_ffn, combine,
     Layer, forward, forward_tokens,
 )
 from .brute import brute_force_forward
 
 __all__ = [
-    "to_f64", "e4m3_decode", "e4m3_encode", "quantize_rows_e4m3", "dequant_rows", "dequant_blocks", "router_logits", "softmax",
+    "to_f64", "e4m3_decode", "e4m3_encode", "quantize_rows_e4m3", "dequant_rows", "round_bf16", "dequant_blocks", "router_logits", "softmax",
     "select_topk", "route", "routing_weights", "permute", "silu", "swiglu_ffn",
     "grouped_ffn", "combine", "Layer", "forward", "forward_tokens",
     "brute_force_forward",

@@ -131,6 +131,17 @@ def dequant_rows(codes, scales, group: int = 128) -> np.ndarray:
     return (q.reshape(R, C // group, group) * s[:, :, None]).reshape(R, C)
 
 
+def round_bf16(x) -> np.ndarray:
+    """float64 -> float32 -> bfloat16 value, each rounding to nearest even
+    (bfloat16: the float32 bit pattern's upper 16 bits, rounded on the lower
+    16 with ties to an even upper half). NaN stays NaN."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    out = u.astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(f), np.nan, out)
+
+
 def _act_quant(x) -> np.ndarray:
     """x rounded through quantize_rows_e4m3 and back (float64)."""
     q, s = quantize_rows_e4m3(np.asarray(x, dtype=np.float64).astype(np.float32))
@@ -237,22 +248,24 @@ def swiglu_ffn(x, W1, W3, W2, act_quant: bool = False) -> np.ndarray:
 
     act_quant (diagnosis only: the exact result is the reference): x and h
     pass through E4M3 activation quantisation (`quantize_rows_e4m3`) before
-    their projections, as a W8A8 kernel computes.
+    their projections, as a W8A8 kernel computes; h is first stored in
+    bfloat16 (the intermediate's storage precision), so its codes are decided
+    on the values the kernel quantises.
     """
     x = np.asarray(x, dtype=np.float64)
     if act_quant:
         x = _act_quant(x)
     h = silu(x @ W1) * (x @ W3)
     if act_quant:
-        h = _act_quant(h)
+        h = _act_quant(round_bf16(h))
     return h @ W2
 
 
-def grouped_ffn(Xrows, offsets, expert) -> np.ndarray:
+def grouped_ffn(Xrows, offsets, expert, act_quant: bool = False) -> np.ndarray:
     """Yp[r] = FFN_e(Xrows[r]) for the rows r of each group e.
 
     `expert(e)` returns (W1, W3, W2) as float64 arrays. Groups with no rows are
-    skipped (their weights are never touched).
+    skipped (their weights are never touched). `act_quant`: see swiglu_ffn.
     """
     Xrows = np.asarray(Xrows, dtype=np.float64)
     offsets = np.asarray(offsets)
@@ -263,7 +276,7 @@ def grouped_ffn(Xrows, offsets, expert) -> np.ndarray:
         if hi <= lo:
             continue
         W1, W3, W2 = expert(e)
-        y = swiglu_ffn(Xrows[lo:hi], W1, W3, W2)
+        y = swiglu_ffn(Xrows[lo:hi], W1, W3, W2, act_quant)
         if Yp is None:
             Yp = np.zeros((Xrows.shape[0], y.shape[1]), dtype=np.float64)
         Yp[lo:hi] = y

@@ -21,13 +21,13 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 def declared_functions():
     src = open(HEADER, encoding="utf-8").read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_expected_api():
     names = declared_functions()
     for n in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-              "moe_forward_workspace_bytes", "moe_status_string"):
+              "moe_forward_workspace_bytes", "moe_status_string", "moe_quantize_e4m3_rows"):
         assert n in names
 
 
@@ -136,3 +136,32 @@ def test_forward_validation_and_workspace():
                            None, None) == INVALID
     assert lib.moe_forward(ctypes.byref(d), FAKE, 16, FAKE, FAKE, 16, None, None, None, None, None, None) == WS_SMALL
     assert lib.moe_forward(ctypes.byref(d), None, 0, None, None, 0, None, None, None, None, None, None) == OK
+
+
+def test_quantize_validation():
+    lib = moe.lib()
+    q = lib.moe_quantize_e4m3_rows
+    # bad sizes, fp32 input, C not a multiple of 128, unaligned stride, nulls
+    assert q(FAKE, BF16, 256, None, 1, -1, 256, FAKE, FAKE, None) == INVALID
+    assert q(FAKE, BF16, 128, None, 1, 4, 256, FAKE, FAKE, None) == INVALID      # ldx < C
+    assert q(FAKE, BF16, 256, None, 0, 4, 256, FAKE, FAKE, None) == INVALID      # gk < 1
+    assert q(FAKE, F32, 256, None, 1, 4, 256, FAKE, FAKE, None) == UNSUPPORTED
+    assert q(FAKE, BF16, 200, None, 1, 4, 200, FAKE, FAKE, None) == UNSUPPORTED  # C % 128
+    assert q(FAKE, BF16, 260, None, 1, 4, 256, FAKE, FAKE, None) == UNSUPPORTED  # ldx % 8
+    assert q(None, BF16, 256, None, 1, 4, 256, FAKE, FAKE, None) == INVALID
+    assert q(None, BF16, 256, None, 1, 0, 256, None, None, None) == OK          # nothing to do
+
+
+def test_tiled_a8_path_validation():
+    lib = moe.lib()
+    # the W8A8 path is for fp8 weights only
+    assert lib.moe_grouped_ffn(FAKE, None, 1, 8, FAKE, 2, 256, 256, FAKE, FAKE, FAKE, BF16, None, None, None,
+                               BF16, FAKE, 3, FAKE, 1 << 30, None) == UNSUPPORTED
+    # path values past the last are rejected
+    assert lib.moe_grouped_ffn(FAKE, None, 1, 8, FAKE, 2, 256, 256, FAKE, FAKE, FAKE, BF16, None, None, None,
+                               BF16, FAKE, 4, FAKE, 1 << 30, None) == INVALID
+    # workspace sizes: the W8A8 plan adds the E4M3 codes and scales
+    m, g, h, f = 4096, 8, 512, 384
+    a8 = lib.moe_grouped_ffn_workspace_bytes(m, g, h, f, BF16, FP8, 3)
+    w8a16 = lib.moe_grouped_ffn_workspace_bytes(m, g, h, f, BF16, FP8, 2)
+    assert a8 >= w8a16 > 0

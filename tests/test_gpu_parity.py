@@ -119,8 +119,23 @@ def test_permute(T, k, E, mode):
 # grouped FFN and combine
 # ----------------------------------------------------------------------------
 
-FFN_CASES = [(n, p) for n in MINI_CONFIGS for p in ("gemv", "tiled")
-             if not (p == "tiled" and MINI_CONFIGS[n].w == "f32")]
+FFN_CASES = [(n, p) for n in MINI_CONFIGS for p in ("gemv", "tiled", "tiled_a8")
+             if not (p == "tiled" and MINI_CONFIGS[n].w == "f32")
+             and not (p == "tiled_a8" and MINI_CONFIGS[n].w != "fp8")]
+# W8A8 against the oracle's mirror of the activation quantisation. The two
+# agree except where an h value lands on the other side of an E4M3 rounding
+# boundary (fp32 accumulation here, fp64 there): such a flip moves one h
+# element by a whole E4M3 step, so single outputs can move by ~1e-2 of the
+# output scale while the mean stays near the accumulation noise. The mean
+# absolute difference over max |ref| is checked; the max is checked against
+# the exact layer (tol_for).
+MIRROR_TOL = 1e-3
+
+
+def mean_rel(got, ref) -> float:
+    got = got.detach().float().cpu().numpy() if isinstance(got, torch.Tensor) else np.asarray(got)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.abs(got.astype(np.float64) - ref).mean() / max(np.abs(ref).max(), 1e-300))
 
 
 @pytest.mark.parametrize("name,path", FFN_CASES)
@@ -142,8 +157,41 @@ def test_grouped_ffn(name, path):
     Yp2 = moe.grouped_ffn(Xp_d, off_d, d["W1"], d["W3"], d["W2"], d["S1"], d["S3"], d["S2"], path=path)
     torch.cuda.synchronize()
     tol = tol_for(cfg)
-    assert rel_err(Yp, ref) <= tol
+    err = rel_err(Yp, ref)
+    say(f"    max rel err {err:.3e} (tol {tol})")
+    assert err <= tol
     assert torch.equal(Yp, Yp2)
+    if path == "tiled_a8":
+        mirror = oracle.grouped_ffn(Xp, offsets, L.expert, act_quant=True)
+        err_m = mean_rel(Yp, mirror)
+        say(f"    against the quantisation mirror: mean {err_m:.3e} (tol {MIRROR_TOL})")
+        assert err_m <= MIRROR_TOL
+
+
+@pytest.mark.parametrize("R,C,gather", [(1, 128, False), (37, 384, False), (300, 7168, False),
+                                         (520, 512, True)])
+def test_quantize_rows(R, C, gather):
+    say(f"[quant] R={R} C={C} gather={gather}")
+    g = torch.Generator(device="cpu").manual_seed(R * 7 + C)
+    T = R // 4 if gather else R
+    X = torch.randn((max(T, 1), C), generator=g).to(torch.bfloat16)
+    if C >= 256:
+        X[0, 128:256] = 0.0                      # an all-zero group: scale 1, codes 0
+        X[-1, :128] *= 1000.0                    # large values: scale follows amax
+    Xd = X.cuda()
+    row_src = None
+    if gather:
+        rs = torch.randperm(R, generator=g).to(torch.int32) % (4 * T)
+        row_src = rs.cuda()
+        Q, S = moe.quantize_e4m3_rows(Xd, row_src, k=4)
+        rows = X[(rs // 4).long()]
+    else:
+        Q, S = moe.quantize_e4m3_rows(Xd)
+        rows = X
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_rows_e4m3(rows)
+    np.testing.assert_array_equal(S.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(Q.cpu().numpy(), q_ref)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -169,7 +217,7 @@ def test_combine(dtype, shared):
 # whole layer
 # ----------------------------------------------------------------------------
 
-def _check_forward(cfg, d, layer, tokens=None):
+def _check_forward(cfg, d, layer, tokens=None, mirror=False):
     Y, logits, idx, w, counts = layer.forward(d["X"], aux=True)
     torch.cuda.synchronize()
     idx_np = _check_routing(cfg, d, logits, idx, w)
@@ -182,6 +230,11 @@ def _check_forward(cfg, d, layer, tokens=None):
     say(f"    max rel err {err:.3e} (tol {tol_for(cfg)})")
     assert err <= tol_for(cfg)
     assert torch.isfinite(Y.float()).all()
+    if mirror:
+        ref_m = oracle.forward_tokens(L, tokens, idx=idx_np[tokens], act_quant=True)
+        err_m = mean_rel(Y[torch.as_tensor(tokens, device="cuda")], ref_m["Y"])
+        say(f"    against the quantisation mirror: mean {err_m:.3e} (tol {MIRROR_TOL})")
+        assert err_m <= MIRROR_TOL
     return Y
 
 
@@ -190,7 +243,7 @@ def test_forward_mini(name, path):
     cfg = MINI_CONFIGS[name]
     say(f"[forward] {name} path={path}")
     d = screened_layer(cfg)
-    Y = _check_forward(cfg, d, moe.MoELayer(d, cfg.k, path=path))
+    Y = _check_forward(cfg, d, moe.MoELayer(d, cfg.k, path=path), mirror=path == "tiled_a8")
     Y2 = moe.MoELayer(d, cfg.k, path=path).forward(d["X"])
     torch.cuda.synchronize()
     assert torch.equal(Y, Y2)  # deterministic

@@ -93,8 +93,20 @@ def test_mirror_mode_is_the_exact_ffn_on_representable_activations():
     W3 = rng.standard_normal((128, 128)) * 0.02
     y_exact = oracle.swiglu_ffn(x, W1, W3, W2)
     y_mirror = oracle.swiglu_ffn(x, W1, W3, W2, act_quant=True)
-    # only h is rounded here (x is exact): the change is within the format's
-    # relative bound of h, propagated through W2
+    # only h is rounded here (x is exact): bf16 storage (relative 2^-8 at
+    # most) then E4M3 (2^-4 relative, or half the subnormal spacing), through W2
     h = oracle.silu(x @ W1) * (x @ W3)
-    bound = 2.0 ** -4 * np.abs(h) @ np.abs(W2) + 2.0 ** -9 * np.abs(h).max() * np.abs(W2).sum(axis=0)
+    bound = (2.0 ** -4 + 2.0 ** -7) * np.abs(h) @ np.abs(W2) + 2.0 ** -9 * np.abs(h).max() * np.abs(W2).sum(axis=0)
     assert np.all(np.abs(y_mirror - y_exact) <= bound + 1e-12)
+
+
+def test_round_bf16_matches_torch_and_ties():
+    import torch
+    rng = np.random.default_rng(8)
+    x = np.concatenate([rng.standard_normal(5000) * 10.0 ** rng.integers(-8, 8, 5000),
+                        [0.0, -0.0, 1.0, 3.0e38, -1e-40]])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_bf16(x), ref)
+    # ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 (bf16 has 7 stored bits): even -> 1
+    assert oracle.round_bf16(1.0 + 2.0 ** -8) == 1.0
+    assert oracle.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
