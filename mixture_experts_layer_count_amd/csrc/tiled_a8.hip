@@ -41,6 +41,7 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+constexpr int kA8Threads = 256;  // 2 x 2 wavefronts of 64 x 64
 constexpr int kA8BM = 128;
 constexpr int kA8BN = 128;   // B-columns per tile
 constexpr int kA8BK = 128;   // K per step = one scale block
@@ -53,8 +54,8 @@ struct RingA8 {
     static constexpr int sw_bytes = 4 * 256;        // per-wavefront weight scales
     static constexpr int stage = a_bytes + b_bytes + sa_bytes + sw_bytes;
     static constexpr int S = (kA8Budget / stage) < 8 ? (kA8Budget / stage) : 8;
-    static constexpr int nA = a_bytes / (kThreads * 16);  // 4
-    static constexpr int nB = b_bytes / (kThreads * 16);  // 4
+    static constexpr int nA = a_bytes / (kA8Threads * 16);  // 4
+    static constexpr int nB = b_bytes / (kA8Threads * 16);  // 4
     static constexpr int per_tile = nA + nB + 2;
 };
 
@@ -67,7 +68,7 @@ struct OutA8 {
 __device__ __forceinline__ int bswz_a8(int k) { return ((k >> 1) & 3) ^ (((k >> 5) & 1) << 2); }
 
 template <bool SWIGLU>
-__global__ __launch_bounds__(kThreads, 1) void tiled_a8_kernel(GemmProblem p, int nN) {
+__global__ __launch_bounds__(kA8Threads, 1) void tiled_a8_kernel(GemmProblem p, int nN) {
     typedef RingA8 R;
     constexpr int S = R::S;
     constexpr int LDS = (R::S * R::stage) > kA8BM * OutA8<SWIGLU>::ld * 2 ? R::S * R::stage
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void tiled_a8_kernel(GemmProblem p, in
     constexpr int W = OutA8<SWIGLU>::width;
     constexpr int chunks_per_row = W / 8;
     uint16_t *Cg = reinterpret_cast<uint16_t *>(p.C);
-    for (int idx = tid; idx < kA8BM * chunks_per_row; idx += kThreads) {
+    for (int idx = tid; idx < kA8BM * chunks_per_row; idx += kA8Threads) {
         const int r = idx / chunks_per_row, cc = idx % chunks_per_row;
         const int row = row0 + r, col = n0 + 8 * cc;
         if (row < row_end && col < p.N)
@@ -301,7 +302,7 @@ hipError_t launch_a8(const GemmProblem &p, hipStream_t s) {
     blocks = (blocks + kXcds - 1) / kXcds * kXcds;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((tiled_a8_kernel<SWIGLU>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p, nN);
+    hipLaunchKernelGGL((tiled_a8_kernel<SWIGLU>), dim3((unsigned)blocks), dim3(kA8Threads), 0, s, p, nN);
     return hipGetLastError();
 }
 

@@ -10,8 +10,10 @@
 // A-tile load and SwiGLU into the gate/up epilogue.
 //
 // Tile: BM rows (256, or 128 when experts hold few rows, always 128 for fp8
-// weights) x 256 B-columns x 32 deep; 256 threads = 4 wavefronts in a 2 x 2
-// grid, each owning BM/2 rows x 128 B-columns.
+// weights) x 256 B-columns x 32 deep. Wavefronts form a WR x 2 grid, each
+// owning BM/WR rows x 128 B-columns: WR = 2 (4 wavefronts, one per SIMD) for
+// 128-row tiles, WR = 4 (8 wavefronts, two per SIMD, 64 rows each) for
+// 256-row tiles.
 //  * gate/up (SWIGLU): B-columns 0..127 are W1[:, n0:n0+128] and 128..255 are
 //    W3[:, n0:n0+128]; wavefront column wc holds the W1 and W3 accumulators of
 //    output columns n0 + 64 wc .. +63, so h = silu(g) * u is formed in
@@ -68,25 +70,27 @@ namespace tiled {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
 constexpr int kBK = 32;            // K depth per tile: one MFMA step
 constexpr int kXcds = 8;
 constexpr int kBlocksPerXcd = 32;  // one workgroup per CU (LDS-bound)
 constexpr int kRingBudget = 144 * 1024;
 
-template <int WT, int BM>
+// WR: wavefront rows (2: 4 wavefronts, one per SIMD; 4: 8 wavefronts, two
+// per SIMD, each half the rows and registers)
+template <int WT, int BM, int WR = 2>
 struct Ring {
+    static constexpr int threads = 128 * WR;
     static constexpr bool fp8 = WT == W_FP8;
     static constexpr int a_bytes = BM * kBK * 2;        // 64-byte bf16 rows
     static constexpr int b_row = fp8 ? 256 : 512;       // one K row of 256 B-columns
     static constexpr int b_bytes = kBK * b_row;
-    static constexpr int s_bytes = fp8 ? 4 * 256 : 0;   // per-wavefront block-scale copies
+    static constexpr int s_bytes = fp8 ? 2 * WR * 256 : 0;  // per-wavefront block-scale copies
     static constexpr int stage = a_bytes + b_bytes + s_bytes;
     static constexpr int S = (kRingBudget / stage) < 8 ? (kRingBudget / stage) : 8;
-    static constexpr int nA = a_bytes / (kThreads * 16);  // 16-byte copies per thread per tile
-    static constexpr int nB = b_bytes / (kThreads * 16);
+    static constexpr int nA = a_bytes / (threads * 16);  // 16-byte copies per thread per tile
+    static constexpr int nB = b_bytes / (threads * 16);
     static constexpr int per_tile = nA + nB + (fp8 ? 1 : 0);  // vector-memory ops per tile
-    static constexpr int mi = BM / 32;                    // 16-row MFMA blocks per wavefront
+    static constexpr int mi = BM / (16 * WR);              // 16-row MFMA blocks per wavefront
     static constexpr int ring = S * stage;
 };
 
@@ -96,9 +100,9 @@ struct Out {
     static constexpr int ld = width + 8;              // LDS staging row stride (elements)
 };
 
-template <int WT, bool SWIGLU, int BM>
+template <int WT, bool SWIGLU, int BM, int WR>
 constexpr int lds_bytes() {
-    return Ring<WT, BM>::ring > BM * Out<SWIGLU>::ld * 2 ? Ring<WT, BM>::ring : BM * Out<SWIGLU>::ld * 2;
+    return Ring<WT, BM, WR>::ring > BM * Out<SWIGLU>::ld * 2 ? Ring<WT, BM, WR>::ring : BM * Out<SWIGLU>::ld * 2;
 }
 
 // A tile: 64-byte rows, 16-byte chunk c of row r stored at c ^ ((r >> 2) & 3),
@@ -205,12 +209,13 @@ struct Frags {
     float s0, s1;
 };
 
-template <int WT, bool SWIGLU, int BM>
-__global__ __launch_bounds__(kThreads, 1) void tiled_gemm_kernel(GemmProblem p, int nN) {
-    typedef Ring<WT, BM> R;
+template <int WT, bool SWIGLU, int BM, int WR>
+__global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, int nN) {
+    typedef Ring<WT, BM, WR> R;
+    constexpr int kT = R::threads;
     constexpr bool FP8 = R::fp8;
     constexpr int S = R::S;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<WT, SWIGLU, BM>()];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<WT, SWIGLU, BM, WR>()];
 
     int mt, nt;
     if (!pick_tile(p, nN, BM, mt, nt)) return;
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void tiled_gemm_kernel(GemmProblem p, 
     // blocks, then the fp8 scales); LDS byte offsets are fixed per lane ----
     constexpr int NBR = FP8 ? 8 : 16;
     constexpr int NR = NBR + R::mi + (FP8 ? 1 : 0);
-    const int a_off = (wr * (BM / 2) + (lane & 15)) * 64 + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
+    const int a_off = (wr * (BM / WR) + (lane & 15)) * 64 + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
     const int i16 = lane & 15, gq = lane >> 4;
     auto read = [&](Frags<R::mi, FP8> &f, int r, int stage) {
         const uint8_t *st = lds + stage * R::stage;
@@ -443,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void tiled_gemm_kernel(GemmProblem p, 
     for (int m = 0; m < R::mi; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = wr * (BM / 2) + m * 16 + 4 * (lane >> 4) + i;
+            const int r = wr * (BM / WR) + m * 16 + 4 * (lane >> 4) + i;
             if (SWIGLU) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void tiled_gemm_kernel(GemmProblem p, 
     constexpr int W = Out<SWIGLU>::width;
     constexpr int chunks_per_row = W / 8;
     uint16_t *Cg = reinterpret_cast<uint16_t *>(p.C);
-    for (int idx = tid; idx < BM * chunks_per_row; idx += kThreads) {
+    for (int idx = tid; idx < BM * chunks_per_row; idx += kT) {
         const int r = idx / chunks_per_row, cc = idx % chunks_per_row;
         const int row = row0 + r, col = n0 + 8 * cc;
         if (row < row_end && col < p.N)
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void tiled_gemm_kernel(GemmProblem p, 
     }
 }
 
-template <int WT, bool SWIGLU, int BM>
+template <int WT, bool SWIGLU, int BM, int WR = 2>
 inline hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
     const int W = Out<SWIGLU>::width;
     const int nN = (p.N + W - 1) / W;
@@ -478,13 +483,14 @@ inline hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
     blocks = (blocks + kXcds - 1) / kXcds * kXcds;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((tiled_gemm_kernel<WT, SWIGLU, BM>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p, nN);
+    hipLaunchKernelGGL((tiled_gemm_kernel<WT, SWIGLU, BM, WR>), dim3((unsigned)blocks), dim3(128 * WR), 0, s, p,
+                       nN);
     return hipGetLastError();
 }
 
-template <int WT, int BM>
+template <int WT, int BM, int WR = 2>
 inline hipError_t launch_bm(const GemmProblem &p, bool swiglu, hipStream_t s) {
-    return swiglu ? launch_t<WT, true, BM>(p, s) : launch_t<WT, false, BM>(p, s);
+    return swiglu ? launch_t<WT, true, BM, WR>(p, s) : launch_t<WT, false, BM, WR>(p, s);
 }
 
 }  // namespace tiled

@@ -60,6 +60,8 @@ MINI_CONFIGS = {
         LayerConfig("mini_bf16_decode", T=13, H=544, F=672, E=8, k=2, seed=2),
         LayerConfig("mini_bf16_prefill", T=700, H=512, F=384, E=8, k=2, zipf_s=1.1, seed=3),
         LayerConfig("mini_bf16_wide", T=300, H=256, F=192, E=64, k=8, seed=4),
+        # enough rows per expert for 256-row tiles, ragged in rows, N and K
+        LayerConfig("mini_bf16_tall", T=1536, H=640, F=416, E=8, k=2, zipf_s=1.1, seed=7),
         LayerConfig("mini_fp8_decode", T=20, H=384, F=256, E=16, k=4, Fs=256, w="fp8", seed=5),
         LayerConfig("mini_fp8_prefill", T=520, H=512, F=384, E=16, k=4, Fs=384, w="fp8", seed=6),
     ]
