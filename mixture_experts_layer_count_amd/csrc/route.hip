@@ -7,8 +7,9 @@
 // grouped GEMM (one group, fp32 accumulation).
 //
 // One wavefront per token. Each lane holds E/64 logits in registers; k rounds
-// of a 64-lane butterfly argmax (ties to the lower expert index) pick the
-// experts best first. The renormalised weight of the j-th pick equals the
+// of a 64-lane argmax over 64-bit ranking keys (ties to the lower expert
+// index; DPP inside 16-lane rows, two shuffles across them) pick the experts
+// best first. The renormalised weight of the j-th pick equals the
 // softmax over the k kept logits, exp(l_j - l_0) / sum_j' exp(l_j' - l_0),
 // because the full softmax's denominator cancels.
 #include <math.h>
@@ -20,9 +21,41 @@ namespace {
 
 constexpr int kWaves = 4;
 
-// true if (va, ia) ranks before (vb, ib): larger value, then lower index
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+// Ranking key of (logit, expert): the logit's bits made monotonic as an
+// unsigned integer in the high word, the complemented expert index in the low
+// word, so a larger key means a larger logit, then the lower index. Every
+// real key is above 0, which marks taken entries. (NaN logits are ranked as
+// -inf before they get here.)
+__device__ __forceinline__ unsigned long long rank_key(float v, int e) {
+    uint32_t b = __float_as_uint(v);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((unsigned long long)b << 32) | (uint32_t)(~e);
+}
+__device__ __forceinline__ unsigned long long kmax(unsigned long long a, unsigned long long b) {
+    return a > b ? a : b;
+}
+// the key of another lane of the same 16-lane row (DPP: no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_key(unsigned long long x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xf, 0xf, false);
+    return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long xor_key(unsigned long long x, int d) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, d, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), d, 64);
+    return ((unsigned long long)hi << 32) | lo;
+}
+// wavefront-wide maximum key, in every lane: quad permutations and row
+// rotations inside each 16-lane row, then two exchanges across rows
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long x) {
+    x = kmax(x, dpp_key<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = kmax(x, dpp_key<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = kmax(x, dpp_key<0x124>(x));  // row_ror:4
+    x = kmax(x, dpp_key<0x128>(x));  // row_ror:8
+    x = kmax(x, xor_key(x, 16));
+    x = kmax(x, xor_key(x, 32));
+    return x;
 }
 
 template <int NPER>
@@ -36,64 +69,48 @@ __global__ __launch_bounds__(kWaves * 64) void topk_kernel(const float *part, in
     const float *prow = part + (long long)t * E;
     float *row = logits + (long long)t * E;
 
-    float v[NPER];   // logit used for ranking (NaN -> -inf)
-    float raw[NPER]; // logit as stored
-    bool taken[NPER];
+    float raw[NPER];              // logit as stored
+    unsigned long long key[NPER];  // ranking key (0 once taken)
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
         const int e = lane + 64 * i;
         float x = -INFINITY;
         if (e < E) {
-            // fixed-order sum of the split-K partials; loads issued in
-            // batches of 8 so their latencies overlap
+            // fixed-order sum of the split-K partials (at most 16, loaded
+            // together so their latencies overlap)
             x = 0.0f;
-            for (int s0 = 0; s0 < nsplit; s0 += 8) {
-                float v[8];
+            for (int s0 = 0; s0 < nsplit; s0 += 16) {
+                float v[16];
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
+                for (int u = 0; u < 16; ++u)
                     v[u] = (s0 + u < nsplit) ? prow[(long long)(s0 + u) * split_stride + e] : 0.0f;
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
+                for (int u = 0; u < 16; ++u)
                     if (s0 + u < nsplit) x = (s0 + u == 0) ? v[u] : x + v[u];
             }
             if (bias) x += bias[e];
             row[e] = x;
         }
         raw[i] = x;
-        v[i] = (x != x) ? -INFINITY : x;
-        taken[i] = e >= E;
+        key[i] = e < E ? rank_key((x != x) ? -INFINITY : x, e) : 0ull;
     }
 
     float sel_val = 0.0f;  // lane j < k keeps the j-th pick
     int sel_idx = 0;
     for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-        float braw = 0.0f;
+        unsigned long long best = 0;
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) best = kmax(best, key[i]);
+        best = wave_max_key(best);
+        // every lane now holds the same best key; its owner marks it taken
+        const int bi = __builtin_amdgcn_readfirstlane((int)~(uint32_t)best);
+        float r = raw[0];
 #pragma unroll
         for (int i = 0; i < NPER; ++i) {
-            const int e = lane + 64 * i;
-            if (!taken[i] && better(v[i], e, bv, bi)) {
-                bv = v[i];
-                bi = e;
-                braw = raw[i];
-            }
+            if (lane + 64 * i == bi) key[i] = 0ull;
+            if (i == (bi >> 6)) r = raw[i];
         }
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float ov = __shfl_xor(bv, d, 64);
-            const int oi = __shfl_xor(bi, d, 64);
-            const float oraw = __shfl_xor(braw, d, 64);
-            if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-                braw = oraw;
-            }
-        }
-        // every lane now agrees on (bv, bi); its owner marks it taken
-#pragma unroll
-        for (int i = 0; i < NPER; ++i)
-            if (lane + 64 * i == bi) taken[i] = true;
+        const float braw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), bi & 63));
         if (lane == j) {
             sel_val = braw;
             sel_idx = bi;

@@ -28,7 +28,7 @@
 namespace moe {
 namespace {
 
-constexpr int kWaves = 4;   // wavefronts per block
+constexpr int kWaves = 4;   // wavefronts per block (at most)
 constexpr int kBM = 16;     // rows per tile
 constexpr int kVec = 4;     // weight columns per lane
 constexpr int kNS = 16 * kVec;  // columns per wavefront slice
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p,
     constexpr int kDepth = ring_depth<WT, SWIGLU>();
 
     const int lane = threadIdx.x & 63;
-    const long long wave = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const long long wave = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int mt = (int)(wave / n_slices);
     const int ns = (int)(wave - (long long)mt * n_slices);
     const int split = blockIdx.y;
@@ -298,12 +298,14 @@ hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
     const int n_slices = (p.N + kNS - 1) / kNS;
     const long long mtiles = p.tiles ? (long long)p.max_tiles : (long long)((p.M + kBM - 1) / kBM);
     const long long waves = mtiles * n_slices;
-    const long long blocks = (waves + kWaves - 1) / kWaves;
+    // 2 wavefronts per block when there are few (balances the blocks over
+    // the CUs; measured 7% faster on 112 experts x 12 slices), else 4
+    const int wpb = waves < 2048 ? 2 : kWaves;
+    const long long blocks = (waves + wpb - 1) / wpb;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 grid((unsigned)blocks, (unsigned)p.ksplit);
-    hipLaunchKernelGGL((stream_gemm_kernel<WT, SWIGLU, OUT_BF16>), grid, dim3(kWaves * 64), 0, s, p,
-                       n_slices);
+    hipLaunchKernelGGL((stream_gemm_kernel<WT, SWIGLU, OUT_BF16>), grid, dim3(wpb * 64), 0, s, p, n_slices);
     return hipGetLastError();
 }
 
