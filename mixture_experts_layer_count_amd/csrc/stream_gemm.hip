@@ -5,21 +5,21 @@
 // in effect a batched GEMV and needs its own tile strategy; page
 // "MOE推理流程解析" §二: grouped GEMM runs every expert's row block in one
 // launch). Each wavefront owns one (expert row tile of 16 rows, 64-column
-// slice of the weight) pair and streams that slice of the expert's weights
+// (fp8: 128-column) slice of the weight) pair and streams that slice of the expert's weights
 // from HBM exactly once, over its K range. Only experts that received rows
 // produce tiles, so untouched experts' weights are never read.
 //
 // MI355X mapping:
-//  * the weight matrices are stored [K][N] (N contiguous). A lane loads VEC
-//    consecutive columns from 8 consecutive K rows; v_perm packs them into
+//  * the weight matrices are stored [K][N] (N contiguous). A lane loads 4
+//    (fp8: 8) consecutive columns from 8 consecutive K rows; v_perm packs them into
 //    K-contiguous bf16 pairs, which is exactly the B operand layout of
 //    v_mfma_f32_16x16x32_bf16 (no LDS round trip).
 //  * the token rows (<= 16, zero-padded) are the A operand, read directly in
 //    their natural K-contiguous layout, gathered through row_src.
-//  * fp8 E4M3 weights are decoded to bf16 in registers
-//    (v_cvt_scalef32_pk_bf16_fp8, scale 1: exact), multiplied on the bf16
-//    MFMA, and each 128-deep K block's partial sum is multiplied by its fp32
-//    block scale before it joins the accumulator.
+//  * fp8 E4M3 weights are loaded 8 columns (8 bytes) a lane, decoded to bf16
+//    in registers (v_cvt_scalef32_pk_bf16_fp8, scale 1: exact) and multiplied
+//    on the bf16 MFMA; each 32-deep step's product joins the accumulator times
+//    the fp32 block scale of its 128x128 block.
 //  * f32 weights use v_mfma_f32_16x16x4_f32 with no transpose.
 //  * a ring of register stages keeps the weight, token and scale loads of
 //    the next K steps in flight while the current step is multiplied.
@@ -30,8 +30,10 @@ namespace {
 
 constexpr int kWaves = 4;   // wavefronts per block (at most)
 constexpr int kBM = 16;     // rows per tile
-constexpr int kVec = 4;     // weight columns per lane
-constexpr int kNS = 16 * kVec;  // columns per wavefront slice
+// weight columns per lane: 8 for fp8 (8-byte loads, the same bytes per load
+// instruction as bf16), else 4; a wavefront slice is 16 lanes wide
+template <int WT> constexpr int vec_of() { return WT == W_FP8 ? 8 : 4; }
+template <int WT> constexpr int slice_of() { return 16 * vec_of<WT>(); }
 
 template <int WT> struct WTraits;
 template <> struct WTraits<W_BF16> {
@@ -41,7 +43,7 @@ template <> struct WTraits<W_BF16> {
 };
 template <> struct WTraits<W_FP8> {
     typedef uint8_t elem;
-    typedef uint32_t raw;  // 4 columns
+    typedef u32x2 raw;  // 8 columns
     typedef uint16_t act;
 };
 template <> struct WTraits<W_F32> {
@@ -83,40 +85,50 @@ __device__ __forceinline__ void load_rows(typename WTraits<WT>::raw (&r)[8],
     }
 }
 
-// One K step (32 deep) of acc[c] += A * B[:, c] for the wave's 4 column tiles.
+// One K step (32 deep) of acc[c] += A * B[:, c] for the wave's column tiles
+// (fp8: times the step's 128x128 block scale s).
 template <int WT>
-__device__ __forceinline__ void mma_step(f32x4 (&acc)[kVec], const typename WTraits<WT>::raw (&r)[8],
-                                         const void *afrag);
+__device__ __forceinline__ void mma_step(f32x4 (&acc)[vec_of<WT>()], const typename WTraits<WT>::raw (&r)[8],
+                                         const void *afrag, float s);
 
 template <>
-__device__ __forceinline__ void mma_step<W_BF16>(f32x4 (&acc)[kVec], const u32x2 (&r)[8],
-                                                 const void *afrag) {
+__device__ __forceinline__ void mma_step<W_BF16>(f32x4 (&acc)[4], const u32x2 (&r)[8], const void *afrag,
+                                                 float) {
     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(afrag);
 #pragma unroll
-    for (int c = 0; c < kVec; ++c)
+    for (int c = 0; c < 4; ++c)
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, column_frag(r, c), acc[c], 0, 0, 0);
 }
 
+// fp8: each step's product starts from zero and joins the accumulator times
+// the block scale, so no per-block partial sums are kept (their registers go
+// to a deeper load ring instead)
 template <>
-__device__ __forceinline__ void mma_step<W_FP8>(f32x4 (&acc)[kVec], const uint32_t (&q)[8],
-                                                const void *afrag) {
+__device__ __forceinline__ void mma_step<W_FP8>(f32x4 (&acc)[8], const u32x2 (&q)[8], const void *afrag,
+                                                float s) {
     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(afrag);
-    u32x2 r[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = fp8x4_to_bf16x4(q[i]);
+    for (int h = 0; h < 2; ++h) {
+        u32x2 r[8];
 #pragma unroll
-    for (int c = 0; c < kVec; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, column_frag(r, c), acc[c], 0, 0, 0);
+        for (int i = 0; i < 8; ++i) r[i] = fp8x4_to_bf16x4(h ? q[i].y : q[i].x);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, column_frag(r, c), f32x4{}, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[4 * h + c][i] = fmaf(t[i], s, acc[4 * h + c][i]);
+        }
+    }
 }
 
 template <>
-__device__ __forceinline__ void mma_step<W_F32>(f32x4 (&acc)[kVec], const f32x4 (&r)[8],
-                                                const void *afrag) {
+__device__ __forceinline__ void mma_step<W_F32>(f32x4 (&acc)[4], const f32x4 (&r)[8], const void *afrag,
+                                                float) {
     const float *a = reinterpret_cast<const float *>(afrag);
 #pragma unroll
     for (int s = 0; s < 8; ++s)
 #pragma unroll
-        for (int c = 0; c < kVec; ++c)
+        for (int c = 0; c < 4; ++c)
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], r[s][c], acc[c], 0, 0, 0);
 }
 
@@ -142,10 +154,10 @@ __device__ __forceinline__ void load_a(AFrag<WT> &f, const typename WTraits<WT>:
 }
 
 // K steps held in the register ring (kDepth - 1 in flight while one is
-// multiplied), the deepest that keeps two wavefronts per SIMD: the
-// single-matrix down projection has registers to spare; fp8 gate/up stages
-// are larger after decoding.
-template <int WT, bool SWIGLU> constexpr int ring_depth() { return !SWIGLU ? 4 : (WT == W_FP8 ? 2 : 3); }
+// multiplied), chosen by measurement: 3 for bf16 gate/up (two wavefronts per
+// SIMD), 4 for the single-matrix bf16 down projection; fp8 steps are twice as
+// wide (8 columns a lane), best at 2 for gate/up and 3 for down.
+template <int WT, bool SWIGLU> constexpr int ring_depth() { return !SWIGLU ? (WT == W_FP8 ? 3 : 4) : (WT == W_FP8 ? 2 : 3); }
 
 // One K step's operands for one lane: weight rows of both matrices, the token
 // fragment and (fp8) the block scales of the step's 128-deep K block.
@@ -183,7 +195,8 @@ __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p,
     }
 
     const int kg = lane >> 4;
-    const int col = ns * kNS + kVec * (lane & 15);
+    constexpr int KV = vec_of<WT>();
+    const int col = ns * slice_of<WT>() + KV * (lane & 15);
     const bool colok = col < p.N;
     const int kbeg = split * p.kchunk;
     const int kend = min(p.K, kbeg + p.kchunk);
@@ -221,38 +234,16 @@ __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p,
         }
     };
 
-    f32x4 acc0[kVec], acc1[kVec];
-    f32x4 tmp0[kVec], tmp1[kVec];  // fp8: current 128-deep K block
+    f32x4 acc0[KV], acc1[KV];
 #pragma unroll
-    for (int c = 0; c < kVec; ++c) {
+    for (int c = 0; c < KV; ++c) {
         acc0[c] = f32x4{};
         acc1[c] = f32x4{};
-        tmp0[c] = f32x4{};
-        tmp1[c] = f32x4{};
     }
 
-    auto consume = [&](Stage<WT, SWIGLU> &st, int step) {
-        if constexpr (WT == W_FP8) {
-            mma_step<WT>(tmp0, st.w0, &st.a);
-            if constexpr (SWIGLU) mma_step<WT>(tmp1, st.w1, &st.a);
-            const int k0 = kbeg + step * 32;
-            if ((k0 & 127) == 96 || step + 1 == nsteps) {
-                // end of a 128-deep scale block: acc += block partial * scale
-#pragma unroll
-                for (int c = 0; c < kVec; ++c) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc0[c][i] = fmaf(tmp0[c][i], st.s0, acc0[c][i]);
-                        if (SWIGLU) acc1[c][i] = fmaf(tmp1[c][i], st.s1, acc1[c][i]);
-                    }
-                    tmp0[c] = f32x4{};
-                    tmp1[c] = f32x4{};
-                }
-            }
-        } else {
-            mma_step<WT>(acc0, st.w0, &st.a);
-            if constexpr (SWIGLU) mma_step<WT>(acc1, st.w1, &st.a);
-        }
+    auto consume = [&](Stage<WT, SWIGLU> &st, int) {
+        mma_step<WT>(acc0, st.w0, &st.a, st.s0);
+        if constexpr (SWIGLU) mma_step<WT>(acc1, st.w1, &st.a, st.s1);
     };
 
     // ring of kDepth stages: step j lives in slot j % kDepth
@@ -277,25 +268,28 @@ __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p,
     for (int i = 0; i < 4; ++i) {
         const int row = row0 + 4 * kg + i;
         if (row >= row_end) continue;
-        float v[kVec];
+        float v[KV];
 #pragma unroll
-        for (int c = 0; c < kVec; ++c)
+        for (int c = 0; c < KV; ++c)
             v[c] = SWIGLU ? silu_f32(acc0[c][i]) * acc1[c][i] : acc0[c][i];
         const long long off = (long long)split * p.c_split_stride + (long long)row * p.ldc + col;
-        if (OUT_BF16) {
-            u32x2 o;
-            o.x = pack_bf16x2(v[0], v[1]);
-            o.y = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<u32x2 *>(Cb + off * 2) = o;
-        } else {
-            *reinterpret_cast<f32x4 *>(Cb + off * 4) = f32x4{v[0], v[1], v[2], v[3]};
+#pragma unroll
+        for (int h = 0; h < KV / 4; ++h) {
+            if (OUT_BF16) {
+                u32x2 o;
+                o.x = pack_bf16x2(v[4 * h], v[4 * h + 1]);
+                o.y = pack_bf16x2(v[4 * h + 2], v[4 * h + 3]);
+                *reinterpret_cast<u32x2 *>(Cb + (off + 4 * h) * 2) = o;
+            } else {
+                *reinterpret_cast<f32x4 *>(Cb + (off + 4 * h) * 4) = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+            }
         }
     }
 }
 
 template <int WT, bool SWIGLU, bool OUT_BF16>
 hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
-    const int n_slices = (p.N + kNS - 1) / kNS;
+    const int n_slices = (p.N + slice_of<WT>() - 1) / slice_of<WT>();
     const long long mtiles = p.tiles ? (long long)p.max_tiles : (long long)((p.M + kBM - 1) / kBM);
     const long long waves = mtiles * n_slices;
     // 2 wavefronts per block when there are few (balances the blocks over
@@ -316,7 +310,7 @@ hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool 
     // an extra group needs its own weights (and scales for fp8)
     if (p.extra_group >= 0 && (!p.Bx0 || (swiglu && !p.Bx1) || (wt == W_FP8 && (!p.Sx0 || (swiglu && !p.Sx1)))))
         return hipErrorInvalidValue;
-    if (p.K % 32 || p.N % kVec || p.kchunk % 32 || p.ksplit < 1) return hipErrorInvalidValue;
+    if (p.K % 32 || p.N % 4 || p.kchunk % 32 || p.ksplit < 1) return hipErrorInvalidValue;
     if (wt == W_FP8 && (p.K % 128 || p.N % 128 || p.kchunk % 128)) return hipErrorInvalidValue;
     switch (wt) {
     case W_BF16:
