@@ -6,8 +6,9 @@
 //
 // Y[t] = sum_{j<k} w[t,j] * (sum_s Yp_s[assign_row[t*k+j]]) (+ sum_s S_s[t]),
 // accumulated in fp32 in ascending j (and ascending split s), then rounded
-// once to the output dtype. Each thread owns 4 consecutive columns of one
-// token row; rows are read with 8-byte (bf16) or 16-byte (f32) vectors.
+// once to the output dtype. Each thread owns 8 (or, when H is not a multiple
+// of 8, 4) consecutive columns of one token row; the rows and weights of up
+// to 8 contributions are fetched before their row loads are issued together.
 #include "common.h"
 
 namespace moe {
@@ -39,32 +40,83 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t *p, f32x4 v) {
     *reinterpret_cast<u32x2 *>(p) = o;
 }
 
-template <typename InT, typename OutT>
+// V = 4 or 8 consecutive columns per thread (two 4-column halves)
+template <typename InT, int V>
+struct Vec {
+    f32x4 h[V / 4];
+};
+template <typename InT, int V>
+__device__ __forceinline__ Vec<InT, V> loadv(const InT *p) {
+    Vec<InT, V> r;
+    if constexpr (V == 8 && sizeof(InT) == 2) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+        r.h[0] = f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
+        r.h[1] = f32x4{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
+    } else {
+#pragma unroll
+        for (int i = 0; i < V / 4; ++i) r.h[i] = load4<InT>(p + 4 * i);
+    }
+    return r;
+}
+
+template <typename InT, typename OutT, int V>
 __global__ __launch_bounds__(256) void combine_kernel(const InT *Yp, const InT *S,
                                                       long long split_stride, int nsplit,
                                                       const int32_t *assign_row, const float *w,
                                                       int T, int k, int H, OutT *Y) {
     const int t = blockIdx.y;
-    const int col = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int col = (blockIdx.x * 256 + threadIdx.x) * V;
     if (t >= T || col >= H) return;
-    f32x4 acc = f32x4{};
-    for (int j = 0; j < k; ++j) {
-        const long long a = (long long)t * k + j;
-        const long long row = assign_row[a];
-        const float wj = w[a];
-        f32x4 y = load4<InT>(Yp + row * H + col);
-        for (int s = 1; s < nsplit; ++s) y += load4<InT>(Yp + s * split_stride + row * H + col);
-        acc[0] = fmaf(wj, y[0], acc[0]);
-        acc[1] = fmaf(wj, y[1], acc[1]);
-        acc[2] = fmaf(wj, y[2], acc[2]);
-        acc[3] = fmaf(wj, y[3], acc[3]);
+    f32x4 acc[V / 4];
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) acc[i] = f32x4{};
+    // up to 8 contributions at a time: their rows and weights first, then all
+    // their loads, so the latencies overlap; then the weighted sum in j order
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        long long row[8];
+        float wj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j0 + u < k) {
+                const long long a = (long long)t * k + j0 + u;
+                row[u] = assign_row[a];
+                wj[u] = w[a];
+            }
+        }
+        Vec<InT, V> y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j0 + u < k) {
+                y[u] = loadv<InT, V>(Yp + row[u] * H + col);
+                for (int s = 1; s < nsplit; ++s) {
+                    const Vec<InT, V> z = loadv<InT, V>(Yp + s * split_stride + row[u] * H + col);
+#pragma unroll
+                    for (int i = 0; i < V / 4; ++i) y[u].h[i] += z.h[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j0 + u < k) {
+#pragma unroll
+                for (int i = 0; i < V / 4; ++i)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[i][c] = fmaf(wj[u], y[u].h[i][c], acc[i][c]);
+            }
+        }
     }
     if (S) {
-        f32x4 y = load4<InT>(S + (long long)t * H + col);
-        for (int s = 1; s < nsplit; ++s) y += load4<InT>(S + s * split_stride + (long long)t * H + col);
-        acc += y;
+        Vec<InT, V> y = loadv<InT, V>(S + (long long)t * H + col);
+        for (int s = 1; s < nsplit; ++s) {
+            const Vec<InT, V> z = loadv<InT, V>(S + s * split_stride + (long long)t * H + col);
+#pragma unroll
+            for (int i = 0; i < V / 4; ++i) y.h[i] += z.h[i];
+        }
+#pragma unroll
+        for (int i = 0; i < V / 4; ++i) acc[i] += y.h[i];
     }
-    store4<OutT>(Y + (long long)t * H + col, acc);
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) store4<OutT>(Y + (long long)t * H + col + 4 * i, acc[i]);
 }
 
 template <typename OutT>
@@ -84,10 +136,18 @@ hipError_t launch_combine(const void *Yp, const void *S, long long split_stride,
                           int k, int H, moe_dtype out_dt, void *Y, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     if (H % 4 || nsplit < 1 || T > 65535) return hipErrorInvalidValue;
-    const dim3 grid((H / 4 + 255) / 256, T), block(256);
-#define MOE_COMBINE(IT, OT)                                                                         \
-    hipLaunchKernelGGL((combine_kernel<IT, OT>), grid, block, 0, s, (const IT *)Yp, (const IT *)S, \
-                       split_stride, nsplit, assign_row, w, T, k, H, (OT *)Y)
+    // 8 columns a thread (16-byte bf16 loads) when H allows, else 4
+    const bool v8 = H % 8 == 0;
+    const dim3 grid(v8 ? (H / 8 + 255) / 256 : (H / 4 + 255) / 256, T), block(256);
+#define MOE_COMBINE(IT, OT)                                                                               \
+    do {                                                                                                  \
+        if (v8)                                                                                           \
+            hipLaunchKernelGGL((combine_kernel<IT, OT, 8>), grid, block, 0, s, (const IT *)Yp,             \
+                               (const IT *)S, split_stride, nsplit, assign_row, w, T, k, H, (OT *)Y);    \
+        else                                                                                              \
+            hipLaunchKernelGGL((combine_kernel<IT, OT, 4>), grid, block, 0, s, (const IT *)Yp,             \
+                               (const IT *)S, split_stride, nsplit, assign_row, w, T, k, H, (OT *)Y);    \
+    } while (0)
     if (in_dt == MOE_F32 && out_dt == MOE_F32) MOE_COMBINE(float, float);
     else if (in_dt == MOE_F32 && out_dt == MOE_BF16) MOE_COMBINE(float, uint16_t);
     else if (in_dt == MOE_BF16 && out_dt == MOE_BF16) MOE_COMBINE(uint16_t, uint16_t);

@@ -92,26 +92,63 @@ __global__ __launch_bounds__(kChunk) void permute_rank_kernel(
     }
 }
 
+// Per-chunk counts -> each chunk's first row in its expert block. The 1024
+// threads split into P = 1024 / E groups; thread (group s, expert e) owns a
+// contiguous run of chunks of expert e. Pass 1 sums the run (loads in
+// batches of 16, so their latencies overlap), the runs and the experts are
+// scanned in LDS, and pass 2 rewrites the run's counts as exclusive prefixes.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t *chunk_counts, int nchunks,
                                                             int E, int32_t *counts,
                                                             int32_t *offsets) {
+    __shared__ int run_sum[1024];
+    __shared__ int expert_off[1024];
     __shared__ int scan_lds[16];
     const int tid = threadIdx.x;
-    int total = 0;
-    if (tid < E) {
-        for (int c = 0; c < nchunks; ++c) {
-            const long long i = (long long)c * E + tid;
-            const int v = chunk_counts[i];
-            chunk_counts[i] = total;
+    const int P = 1024 / E;
+    const int e = tid % E, sg = tid / E;
+    const bool act = sg < P;
+    const int per = (nchunks + P - 1) / P;
+    const int c0 = act ? min(nchunks, sg * per) : 0;
+    const int c1 = act ? min(nchunks, c0 + per) : 0;
+
+    int sum = 0;
+    for (int c = c0; c < c1; c += 16) {
+        int v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = c + u < c1 ? chunk_counts[(long long)(c + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) sum += v[u];
+    }
+    run_sum[tid] = sum;
+    __syncthreads();
+    int before = 0, total = 0;
+    if (act) {
+        for (int g = 0; g < P; ++g) {
+            const int v = run_sum[g * E + e];
+            if (g < sg) before += v;
             total += v;
         }
     }
     int all = 0;
-    const int off = block_exclusive_scan(tid < E ? total : 0, scan_lds, &all);
-    if (tid < E) {
-        counts[tid] = total;
-        offsets[tid] = off;
-        for (int c = 0; c < nchunks; ++c) chunk_counts[(long long)c * E + tid] += off;
+    const int off = block_exclusive_scan(act && sg == 0 ? total : 0, scan_lds, &all);
+    if (act && sg == 0) expert_off[e] = off;
+    __syncthreads();
+    if (act) {
+        int run = expert_off[e] + before;
+        for (int c = c0; c < c1; c += 16) {
+            int v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = c + u < c1 ? chunk_counts[(long long)(c + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (c + u < c1) chunk_counts[(long long)(c + u) * E + e] = run;
+                run += v[u];
+            }
+        }
+        if (sg == 0) {
+            counts[e] = total;
+            offsets[e] = off;
+        }
     }
     if (tid == 0) offsets[E] = all;
 }
