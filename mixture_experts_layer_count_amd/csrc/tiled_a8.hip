@@ -29,7 +29,10 @@
 // copies in flight, one barrier per K step, the next step's fragments read
 // between the MFMA groups of the current one.
 //  * A tile: 128-byte rows (128 codes), 16-byte chunk c of row r stored at
-//    c ^ (r & 7); an operand is 32 consecutive codes (two ds_read_b128).
+//    c ^ ((r >> 1) & 7), so the 16 rows one 16-lane pass of a ds_read_b128
+//    reads hit 16 distinct 16-byte bank groups (with r & 7, rows r and r + 8
+//    collided: measured 2-way conflicts); an operand is 32 consecutive codes
+//    (two ds_read_b128).
 //  * B tile: [K][N] layout, BN-byte rows, 16-byte chunk c of row k stored at
 //    c ^ swz(k), so that the 16 rows that two 16-lane groups of a
 //    ds_read_b64_tr_b8 read land in distinct banks; an operand is four
@@ -119,12 +122,13 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
 
     // ---- copy sources ----
     // A: copy q of wavefront w fills rows 8 (w nA + q) .. +7; lane -> row
-    // lane/8, physical chunk lane%8, i.e. logical chunk (lane%8) ^ (row & 7)
+    // lane/8, physical chunk lane%8, i.e. logical chunk (lane%8) ^ ((row >> 1) & 7)
     const uint8_t *a_src[R::nA];
 #pragma unroll
     for (int q = 0; q < R::nA; ++q) {
         const long long src = src_row(row0 + 8 * (w * R::nA + q) + (lane >> 3));
-        a_src[q] = reinterpret_cast<const uint8_t *>(p.A) + src * p.lda + 16 * ((lane & 7) ^ ((lane >> 3) & 7));
+        const int trow = 8 * (w * R::nA + q) + (lane >> 3);  // row within the tile
+        a_src[q] = reinterpret_cast<const uint8_t *>(p.A) + src * p.lda + 16 * ((lane & 7) ^ ((trow >> 1) & 7));
     }
     // B: copy q of wavefront w fills 1024 / BN K rows; lane -> row
     // lane / lanes_per_row, physical chunk lane % lanes_per_row holding data
@@ -200,8 +204,8 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
             const int m = r - 16;
             const int row = a_row + 16 * m;
             const uint8_t *base = st + row * 128;
-            const u32x4 lo = *reinterpret_cast<const u32x4 *>(base + 16 * ((2 * gq) ^ (row & 7)));
-            const u32x4 hi = *reinterpret_cast<const u32x4 *>(base + 16 * ((2 * gq + 1) ^ (row & 7)));
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(base + 16 * ((2 * gq) ^ ((row >> 1) & 7)));
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(base + 16 * ((2 * gq + 1) ^ ((row >> 1) & 7)));
             f.a[m] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         } else {
             const float *sc = reinterpret_cast<const float *>(st + R::a_bytes + R::b_bytes + 2 * 256);
@@ -263,13 +267,16 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     for (int r = 0; r < NR; ++r) read(fa, r, 0);
     land(fa);
     int stage = 0;
-    for (int kt = 0; kt < nk; ++kt) {
+    // one K step: multiply tile kt (in cur) while copying tile kt + S and
+    // reading tile kt + 1 into nxt; two steps per loop trip swap the roles of
+    // the fragment sets, so they are never copied
+    auto step = [&](Frag &cur, Frag &nxt, int kt) {
         const int nstage = stage + 1 == S ? 0 : stage + 1;
         const int src = min(kt + S, nk - 1);
         // the row scales of tile kt, before the barrier lets its stage refill
         f32x4 sa[4];
         read_sa(sa, stage);
-        mma_rows(fa, sa[0], 0);
+        mma_rows(cur, sa[0], 0);
         wait_vm<(S - 2) * R::per_tile>();
         wait_lds();  // the scale reads are done before anyone refills the stage
         __builtin_amdgcn_s_barrier();
@@ -278,13 +285,18 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
 #pragma unroll
             for (int q = c * NC / 3; q < (c + 1) * NC / 3; ++q) copy(q, src, stage);
 #pragma unroll
-            for (int r = c * NR / 3; r < (c + 1) * NR / 3; ++r) read(fb, r, nstage);
-            mma_rows(fa, sa[c + 1], c + 1);
+            for (int r = c * NR / 3; r < (c + 1) * NR / 3; ++r) read(nxt, r, nstage);
+            mma_rows(cur, sa[c + 1], c + 1);
         }
-        land(fb);
-        fa = fb;
+        land(nxt);
         stage = nstage;
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        step(fa, fb, kt);
+        step(fb, fa, kt + 1);
     }
+    if (kt < nk) step(fa, fb, kt);
 
     // ---- epilogue: bf16 tile through LDS, 16-byte row stores ----
     constexpr int LD = O::ld;
