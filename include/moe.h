@@ -79,7 +79,8 @@ typedef enum {
  *  TILED_A8 (FP8 weights only, H and F multiples of 128): the expert inputs
  *    (token rows, then h) are quantised to E4M3 per row and 128-column group
  *    with scale amax/448 (page "MOE推理流程解析" §三: activations quantised
- *    before the expert GEMM) and multiplied on the FP8 matrix cores (W8A8).
+ *    before the expert GEMM) and multiplied on the FP8 matrix cores (W8A8);
+ *    h is quantised inside the gate/up GEMM, from its bf16 values.
  *    In moe_forward it needs Fs == 0 or Fs == F. */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_TILED = 2, MOE_PATH_TILED_A8 = 3 } moe_ffn_path;
 
@@ -208,9 +209,9 @@ enum {
     MOE_EV_ROUTE,          /* router GEMM + top-k done */
     MOE_EV_PERMUTE,        /* counts / offsets / permutation done */
     MOE_EV_SCHEDULE,       /* tile list built (and, on TILED_A8, X quantised) */
-    MOE_EV_GATE_UP,        /* routed gate/up GEMM + SwiGLU done */
+    MOE_EV_GATE_UP,        /* routed gate/up GEMM + SwiGLU done (TILED_A8: h written as E4M3) */
     MOE_EV_SHARED_GATE_UP, /* shared expert gate/up done (no-op without one) */
-    MOE_EV_DOWN,           /* routed down projection done (TILED_A8: h quantised first) */
+    MOE_EV_DOWN,           /* routed down projection done */
     MOE_EV_SHARED_DOWN,    /* shared expert down projection done */
     MOE_EV_COMBINE,        /* combine done: Y written */
     MOE_N_EVENTS

@@ -397,13 +397,14 @@ moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M
 
     MOE_TRY(launch_build_tiles(offsets, G, 0, p.bm, w.tiles, w.n_tiles, w.group_tile_start, stream));
     if (p.a8) {
-        // E4M3 input rows (gathered here), gate/up, E4M3 h, down
+        // E4M3 input rows (gathered here), gate/up writing E4M3 h, down
         MOE_TRY(launch_quant_rows(Xin, H, row_src, k, M, H, w.xq, w.xs, stream));
         GemmProblem g1 = gate_up_problem(nullptr, nullptr, 1, &w, G, max_tiles, M, H, F, W1, W3, S1, S3, none, M,
                                          w.h);
         set_a8(g1, w.xq, w.xs, H);
+        g1.Cq = w.hq;
+        g1.Cqs = w.hs;
         MOE_TRY(run_gemm(p, g1, wt, true, true, stream));
-        MOE_TRY(launch_quant_rows(w.h, F, nullptr, 1, M, F, w.hq, w.hs, stream));
         GemmProblem g2 = down_problem(nullptr, &w, G, max_tiles, M, H, F, W2, S2, none, M, Yp, 0, 1, F);
         set_a8(g2, w.hq, w.hs, F);
         MOE_TRY(run_gemm(p, g2, wt, false, true, stream));
@@ -582,7 +583,11 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     MOE_TRY(mark(MOE_EV_SCHEDULE));
     GemmProblem g1 = gate_up_problem(X, f.row_src, d->k, &f.ffn, E, max_tiles, M, H, F, d->W1, d->W3, d->S1,
                                      d->S3, ex, A, f.ffn.h);
-    if (p.a8) set_a8(g1, f.ffn.xq, f.ffn.xs, H);
+    if (p.a8) {
+        set_a8(g1, f.ffn.xq, f.ffn.xs, H);
+        g1.Cq = f.ffn.hq;  // h leaves the gate/up GEMM as E4M3 codes
+        g1.Cqs = f.ffn.hs;
+    }
     MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
     MOE_TRY(mark(MOE_EV_GATE_UP));
     void *h_s = static_cast<char *>(f.ffn.h) + hb * (size_t)A * hw;
@@ -600,10 +605,7 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     if (p.tiled) {
         GemmProblem g2 = down_problem(f.ffn.h, &f.ffn, E, max_tiles, M, H, F, d->W2, d->S2, ex, A, f.ffn.part,
                                       0, 1, F);
-        if (p.a8) {
-            MOE_TRY(launch_quant_rows(f.ffn.h, hw, nullptr, 1, M, F, f.ffn.hq, f.ffn.hs, stream));
-            set_a8(g2, f.ffn.hq, f.ffn.hs, F);
-        }
+        if (p.a8) set_a8(g2, f.ffn.hq, f.ffn.hs, F);
         MOE_TRY(run_gemm(p, g2, wt, false, bf, stream));
         MOE_TRY(mark(MOE_EV_DOWN));
         void *Sp = static_cast<char *>(f.ffn.part) + hb * (size_t)A * H;

@@ -116,6 +116,11 @@ struct GemmProblem {
     // scales, [row][as_ld] with one scale per 128 K, rows mapped as A's
     const float *As = nullptr;
     int as_ld = 0;
+    // W8A8 gate/up: when Cq is set, h is written as E4M3 codes (Cq, ldc bytes
+    // a row) with one fp32 scale per row and 128 columns (Cqs, ldc / 128 a
+    // row) instead of bf16 to C
+    uint8_t *Cq = nullptr;
+    float *Cqs = nullptr;
 };
 
 hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,

@@ -320,6 +320,50 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
             }
         }
     __syncthreads();
+    if constexpr (SWIGLU && O::width == 128 && R::threads == 4 * kA8BM) {
+        if (p.Cq) {
+            // E4M3 codes of h instead of h: the tile's 128 columns are exactly
+            // one 128-column scale group, so each row's scale is complete here.
+            // Same arithmetic as the stand-alone row quantiser (scale
+            // amax / 448 of the bf16 values, clamp to +-448, round to nearest
+            // even); 4 threads a row, 32 columns each
+            const int r = tid >> 2, part = tid & 3;
+            float v[32];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const u32x4 raw = *reinterpret_cast<const u32x4 *>(Cs + r * LD + 32 * part + 8 * c);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[8 * c + 2 * i] = bf16_lo(raw[i]);
+                    v[8 * c + 2 * i + 1] = bf16_hi(raw[i]);
+                }
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 4));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 4));
+            const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+            uint32_t qw[8];
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+                float q[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(v[4 * h + i] / sc, -448.0f), 448.0f);
+                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+                pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], pk, true);
+                qw[h] = (uint32_t)pk;
+            }
+            const int row = row0 + r;
+            if (row < row_end) {
+                uint8_t *dst = p.Cq + (long long)row * p.ldc + n0 + 32 * part;
+                *reinterpret_cast<u32x4 *>(dst) = u32x4{qw[0], qw[1], qw[2], qw[3]};
+                *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{qw[4], qw[5], qw[6], qw[7]};
+                if (part == 0) p.Cqs[(long long)row * (p.ldc >> 7) + (n0 >> 7)] = sc;
+            }
+            return;
+        }
+    }
     constexpr int W = O::width;
     constexpr int chunks_per_row = W / 8;
     uint16_t *Cg = reinterpret_cast<uint16_t *>(p.C);
@@ -351,6 +395,9 @@ hipError_t launch_a8(const GemmProblem &p, hipStream_t s) {
 bool tiled_a8_supports(int N, int K) { return N >= 128 && N % 128 == 0 && K >= 128 && K % 128 == 0; }
 
 hipError_t launch_tiled_a8(const GemmProblem &p, bool swiglu, hipStream_t s) {
+    // quantised h output: gate/up only, with whole 128-column scale groups
+    if (p.Cq && (!swiglu || !p.Cqs || p.ldc % 128 || tiled::OutA8<true, tiled::kA8WC>::width != 128))
+        return hipErrorInvalidValue;
     if (p.extra_group >= 0 && (!p.Bx0 || !p.Sx0 || (swiglu && (!p.Bx1 || !p.Sx1)))) return hipErrorInvalidValue;
     if (!p.As || p.as_ld < p.K / 128 || p.ksplit != 1 || !tiled_a8_supports(p.N, p.K) || !p.S0 ||
         (swiglu && (!p.B1 || !p.S1)))
