@@ -251,13 +251,28 @@ const char *moe_status_string(moe_status s) {
 // ---------------------------------------------------------------------------
 namespace {
 
-// Split of the router's sum over h: enough wavefronts (16 rows x 64 experts
-// each) to keep the gate and token reads in flight, at least 4 K steps each.
+// The router GEMM: for many bf16 tokens (and at least 16 experts) the
+// LDS-tiled GEMM with 128-row tiles, split over h into at most 256
+// workgroups (one round on the CUs) of at least 8 K steps; otherwise the row-streaming form, split so that
+// enough wavefronts (16 rows x 64 experts each) keep the gate and token reads
+// in flight, at least 4 K steps each.
 struct RoutePlan {
     int ksplit, kchunk;
+    bool tiled;
 };
 
-RoutePlan plan_route(int T, int H, int E) {
+RoutePlan plan_route(int T, int H, int E, moe_dtype x_dt) {
+    if (x_dt == MOE_BF16 && T >= 512 && tiled_f32_supports(T, E, H, 1, H)) {
+        const long long tiles = (long long)((T + 127) / 128) * ((E + 255) / 256);
+        long long ks = 256 / tiles;  // one workgroup per CU, one round
+        long long max_ks = H / 256 > 0 ? H / 256 : 1;
+        if (max_ks > 16) max_ks = 16;
+        if (ks > max_ks) ks = max_ks;
+        if (ks < 1) ks = 1;
+        int chunk = (int)((H + ks - 1) / ks);
+        chunk = (chunk + 31) / 32 * 32;
+        return RoutePlan{(H + chunk - 1) / chunk, chunk, true};
+    }
     long long base = (long long)((T + 15) / 16) * ((E + 63) / 64);
     if (base < 1) base = 1;
     long long ks = (4096 + base - 1) / base;
@@ -267,18 +282,25 @@ RoutePlan plan_route(int T, int H, int E) {
     if (ks < 1) ks = 1;
     int chunk = (int)((H + ks - 1) / ks);
     chunk = (chunk + 31) / 32 * 32;
-    return RoutePlan{(H + chunk - 1) / chunk, chunk};
+    return RoutePlan{(H + chunk - 1) / chunk, chunk, false};
 }
 
+// split-K partials of the router; the larger of the two forms' needs, so the
+// size does not depend on the token dtype
 size_t route_ws_bytes(int T, int H, int E) {
-    const RoutePlan r = plan_route(T, H, E);
-    return r.ksplit > 1 ? (size_t)r.ksplit * T * E * sizeof(float) : 0;
+    size_t need = 0;
+    for (moe_dtype dt : {MOE_BF16, MOE_F32}) {
+        const RoutePlan r = plan_route(T, H, E, dt);
+        const size_t b = r.ksplit > 1 ? (size_t)r.ksplit * T * E * sizeof(float) : 0;
+        if (b > need) need = b;
+    }
+    return need;
 }
 
 moe_status route_impl(const void *X, moe_dtype x_dt, const void *Wg, const float *gate_bias, int T, int H,
                       int E, int k, float *logits, int32_t *topk_idx, float *topk_w, void *ws,
                       hipStream_t stream) {
-    const RoutePlan r = plan_route(T, H, E);
+    const RoutePlan r = plan_route(T, H, E, x_dt);
     float *part = r.ksplit > 1 ? static_cast<float *>(ws) : logits;
     GemmProblem g{};
     g.extra_group = -1;
@@ -294,7 +316,8 @@ moe_status route_impl(const void *X, moe_dtype x_dt, const void *Wg, const float
     g.c_split_stride = (long long)T * E;
     g.ksplit = r.ksplit;
     g.kchunk = r.kchunk;
-    MOE_TRY(launch_stream_gemm(g, x_dt == MOE_F32 ? W_F32 : W_BF16, false, false, stream));
+    if (r.tiled) MOE_TRY(launch_tiled_f32(g, stream));
+    else MOE_TRY(launch_stream_gemm(g, x_dt == MOE_F32 ? W_F32 : W_BF16, false, false, stream));
     return hip_status(launch_topk(part, r.ksplit, (long long)T * E, gate_bias, T, E, k, logits, topk_idx,
                                   topk_w, stream));
 }

@@ -126,6 +126,11 @@ struct GemmProblem {
 hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,
                               hipStream_t s);
 
+// Plain bf16 GEMM of M rows (no tile list, no gather) with fp32 output and
+// split-K over blockIdx.y (C + s c_split_stride); every split non-empty.
+bool tiled_f32_supports(int M, int N, int K, int ksplit, int kchunk);
+hipError_t launch_tiled_f32(const GemmProblem &p, hipStream_t s);
+
 // LDS-tiled grouped GEMM (many rows per group). Same problem statement;
 // ksplit must be 1; bm (rows per tile) must be tiled_gemm_bm(wt, rows, groups) and
 // the tile list must have been built with it. Returns hipErrorInvalidValue

@@ -209,8 +209,12 @@ struct Frags {
     float s0, s1;
 };
 
-template <int WT, bool SWIGLU, int BM, int WR>
+// F32OUT (plain GEMM only): fp32 output straight from the accumulators, and
+// split-K: blockIdx.y = split s multiplies K range [s kchunk, (s+1) kchunk)
+// into C + s c_split_stride (every split must be non-empty).
+template <int WT, bool SWIGLU, int BM, int WR, bool F32OUT = false>
 __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, int nN) {
+    static_assert(!(F32OUT && SWIGLU), "fp32 output is for the plain GEMM");
     typedef Ring<WT, BM, WR> R;
     constexpr int kT = R::threads;
     constexpr bool FP8 = R::fp8;
@@ -219,6 +223,8 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
 
     int mt, nt;
     if (!pick_tile(p, nN, BM, mt, nt)) return;
+    const int split = F32OUT ? (int)blockIdx.y : 0;
+    const int kbase = F32OUT ? split * p.kchunk : 0;  // first K of this split
     int g, row0, row_end;
     if (p.tiles) {
         g = p.tiles[4 * mt];
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     constexpr int NC = R::nA + R::nB + (FP8 ? 1 : 0);
     auto copy = [&](int q, int kt, int stage) {
         uint8_t *st = lds + stage * R::stage;
-        const int k0 = kt * kBK;
+        const int k0 = kbase + kt * kBK;
         if (q < R::nA) {
             copy16(a_src[q] + k0, st + (w * R::nA + q) * 1024);
         } else if (q < R::nA + R::nB) {
@@ -407,7 +413,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     // busy while they issue. Past the last tile the copies repeat the last
     // tile into stages nobody reads, keeping the counts fixed; the read after
     // the last tile is discarded.
-    const int nk = p.K / kBK;
+    const int nk = F32OUT ? (min(p.K, kbase + p.kchunk) - kbase) / kBK : p.K / kBK;
     Frags<R::mi, FP8> fa, fb;
 #pragma unroll
     for (int t = 0; t < S; ++t)
@@ -440,6 +446,25 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
         stage = nstage;
     }
 
+    if constexpr (F32OUT) {
+        wait_vm<0>();  // the last (discarded) copies land before the LDS is released
+        // lane holds rows 4 (lane / 16) + i of each 16-row block, column
+        // lane % 16 of each 16-column block: 64-byte row segments
+        float *Cf = reinterpret_cast<float *>(p.C) + (long long)split * p.c_split_stride;
+#pragma unroll
+        for (int m = 0; m < R::mi; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = row0 + wr * (BM / WR) + m * 16 + 4 * (lane >> 4) + i;
+                if (row >= row_end) continue;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int col = n0 + 128 * wc + 16 * j + i16;
+                    if (col < p.N) Cf[(long long)row * p.ldc + col] = acc[m][j][i];
+                }
+            }
+        return;
+    }
     // ---- epilogue: stage the bf16 tile in LDS, then 16-byte row stores ----
     constexpr int LD = Out<SWIGLU>::ld;
     __syncthreads();  // every wavefront is done with the ring
@@ -474,7 +499,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     }
 }
 
-template <int WT, bool SWIGLU, int BM, int WR = 2>
+template <int WT, bool SWIGLU, int BM, int WR = 2, bool F32OUT = false>
 inline hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
     const int W = Out<SWIGLU>::width;
     const int nN = (p.N + W - 1) / W;
@@ -483,8 +508,8 @@ inline hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
     blocks = (blocks + kXcds - 1) / kXcds * kXcds;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((tiled_gemm_kernel<WT, SWIGLU, BM, WR>), dim3((unsigned)blocks), dim3(128 * WR), 0, s, p,
-                       nN);
+    hipLaunchKernelGGL((tiled_gemm_kernel<WT, SWIGLU, BM, WR, F32OUT>),
+                       dim3((unsigned)blocks, F32OUT ? (unsigned)p.ksplit : 1u), dim3(128 * WR), 0, s, p, nN);
     return hipGetLastError();
 }
 

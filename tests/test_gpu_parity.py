@@ -67,10 +67,15 @@ def test_route_worked_example():
     np.testing.assert_allclose(w.cpu().numpy(), exp_w, atol=1e-6)
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 4, 1), (33, 8, 8), (70, 256, 8), (5, 1024, 64), (129, 64, 1)])
-def test_route_shapes(T, E, k):
-    cfg = LayerConfig(f"route_{T}_{E}_{k}", T=T, H=256, F=32, E=E, k=k, w_std=0.2, seed=T + E)
-    say(f"[route] T={T} E={E} k={k}")
+@pytest.mark.parametrize("T,E,k,H", [
+    (1, 4, 1, 256), (33, 8, 8, 256), (70, 256, 8, 256), (5, 1024, 64, 256), (129, 64, 1, 256),
+    # 512 tokens and more: the tiled router GEMM (128-row tiles, split over H),
+    # with ragged rows, fewer experts than one 256-column tile, and K splits
+    (600, 64, 4, 1024), (777, 40, 2, 512), (1100, 256, 8, 2048), (4096, 16, 2, 256),
+])
+def test_route_shapes(T, E, k, H):
+    cfg = LayerConfig(f"route_{T}_{E}_{k}_{H}", T=T, H=H, F=32, E=E, k=k, w_std=0.2, seed=T + E)
+    say(f"[route] T={T} E={E} k={k} H={H}")
     d = screened_layer(cfg, experts=False)
     logits, idx, w = moe.route(d["X"], d["Wg"], k)
     torch.cuda.synchronize()
@@ -196,9 +201,12 @@ def test_quantize_rows(R, C, gather):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("shared", [False, True])
-def test_combine(dtype, shared):
-    T, k, H = 300, 4, 1024
-    say(f"[combine] {dtype} shared={shared}")
+@pytest.mark.parametrize("k,H", [(4, 1024), (10, 100), (1, 8)])
+def test_combine(dtype, shared, k, H):
+    # (10, 100): more than 8 contributions a token (two batches, the second
+    # partial) and a row width that is not a multiple of 8 (4 columns a thread)
+    T = 300
+    say(f"[combine] {dtype} shared={shared} k={k} H={H}")
     rng = np.random.default_rng(7)
     idx = np.argsort(rng.random((T, 16)), axis=1)[:, :k]
     _, _, _, assign_row = oracle.permute(idx, 16)
