@@ -36,7 +36,13 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 # sources of the gate/up kernel each path launches (the traffic record is
 # void once any of them changes)
 KERNEL_SOURCES = {"stream": ("stream_gemm.hip", "common.h"),
-                  "tiled": ("tiled_gemm_kernel.h", "tiled_gemm_bm128.hip", "tiled_gemm_bm256.hip", "common.h")}
+                  "tiled": ("tiled_gemm_kernel.h", "tiled_gemm_bm128.hip", "tiled_gemm_bm256.hip", "common.h"),
+                  "a8": ("tiled_a8.hip", "tiled_gemm_kernel.h", "common.h")}
+
+
+def kernel_family(name: str) -> str:
+    """Source family of a gate/up kernel's (demangled) name."""
+    return "stream" if "stream_gemm" in name else ("a8" if "tiled_a8" in name else "tiled")
 
 
 def kernel_source_hash(path: str) -> str:
@@ -56,8 +62,7 @@ def measured_traffic(workload: str, kernel: str):
         return None
     with open(path, encoding="utf-8") as fh:
         rec = json.load(fh)
-    path = "stream" if "stream_gemm" in rec.get("kernel", "") else "tiled"
-    if rec.get("kernel_source_hash") != kernel_source_hash(path):
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel_family(rec.get("kernel", ""))):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -91,7 +96,7 @@ def cpu_baseline(cfg, d, k: int) -> dict:
                       f"{platform.processor() or 'host'}"}
 
 
-GATE_UP_KERNEL = re.compile(r"(stream|tiled)_gemm_kernel<[^,]+, true")
+GATE_UP_KERNEL = re.compile(r"(stream|tiled)_gemm_kernel<[^,]+, true|tiled_a8_kernel<true")
 
 
 def _pmc_means(run_dir: str, counter: str) -> dict:
@@ -133,7 +138,7 @@ def record_traffic(args) -> int:
     wk, nw = write[name]
     rec = {
         "workload": args.workload, "kernel": name,
-        "kernel_source_hash": kernel_source_hash("stream" if "stream_gemm" in name else "tiled"),
+        "kernel_source_hash": kernel_source_hash(kernel_family(name)),
         "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
         "dispatches": [nf, nw], "calibration_bytes": nbytes,
         "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4),
@@ -175,7 +180,7 @@ def summarize_trace(args) -> int:
             rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e3,
                          float(r["Percentage"])))
     print(f"# rocprofv3 kernel trace: {args.workload}\n")
-    print("Command, from the repository root:\n\n```\n" + " ".join(args.commands) + "\n```\n")
+    print("Commands, from the repository root R:\n\n```\n" + "\n".join(args.commands) + "\n```\n")
     print("| kernel | calls | avg (us) | total (us) | % of GPU time |\n|---|---:|---:|---:|---:|")
     for name, calls, avg, tot, pct in rows:
         print(f"| `{name}` | {calls} | {avg:.2f} | {tot:.1f} | {pct:.1f} |")
