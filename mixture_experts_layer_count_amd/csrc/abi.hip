@@ -86,7 +86,7 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path, 
         p.tiled = can_tile && (long long)M >= 48LL * G;
         p.a8 = p.tiled && can_a8;
     }
-    p.bm = p.tiled ? tiled_gemm_bm(wt, M, G) : kGemvBM;
+    p.bm = p.a8 ? tiled_a8_bm(M, G) : p.tiled ? tiled_gemm_bm(wt, M, G) : kGemvBM;
     p.ksplit2 = 1;
     p.kchunk2 = F;
     if (!p.tiled) {
@@ -220,7 +220,7 @@ int chunk_for(int K, int nsplit, moe_dtype w_dt) {
 
 hipError_t run_gemm(const FfnPlan &p, const GemmProblem &g, WType wt, bool swiglu, bool out_bf16,
                     hipStream_t s) {
-    if (p.a8) return out_bf16 ? launch_tiled_a8(g, swiglu, s) : hipErrorInvalidValue;
+    if (p.a8) return out_bf16 ? launch_tiled_a8(g, swiglu, p.bm, s) : hipErrorInvalidValue;
     return p.tiled ? launch_tiled_gemm(g, wt, swiglu, out_bf16, p.bm, s)
                    : launch_stream_gemm(g, wt, swiglu, out_bf16, s);
 }

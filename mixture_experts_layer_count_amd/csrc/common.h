@@ -143,7 +143,8 @@ bool tiled_gemm_supports(WType wt, int N, int K);
 // W8A8 variant of the LDS-tiled grouped GEMM (fp8 weights and fp8
 // activations with per-row 128-column scales, p.As): 128-row tiles built with
 // bm = 128; output bf16. Returns hipErrorInvalidValue for unsupported shapes.
-hipError_t launch_tiled_a8(const GemmProblem &p, bool swiglu, hipStream_t s);
+hipError_t launch_tiled_a8(const GemmProblem &p, bool swiglu, int bm, hipStream_t s);
+int tiled_a8_bm(long long rows, int groups);  // rows per W8A8 tile (128 or 160)
 bool tiled_a8_supports(int N, int K);
 
 // E4M3 quantisation of bf16 rows: for each row and 128-column group,

@@ -54,23 +54,27 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // DeepSeek-V3 prefill layer
 constexpr int kA8WC = 4;
 
-constexpr int kA8BM = 128;
 constexpr int kA8BK = 128;   // K per step = one scale block
-constexpr int kA8Budget = 156 * 1024;
+constexpr int kA8Budget = 160 * 1024;
 
-template <int WC>
+// BM rows (128 or 160: 2 wavefront rows of BM/2) x BN B-columns
+template <int WC, int BM>
 struct RingA8 {
     static constexpr int threads = 128 * WC;        // 2 x WC wavefronts
     static constexpr int BN = 64 * WC;              // B-columns per tile
-    static constexpr int a_bytes = kA8BM * kA8BK;   // 16 KB
+    static constexpr int mi = BM / 32;              // 16-row blocks per wavefront
+    static constexpr int a_bytes = BM * kA8BK;
     static constexpr int b_bytes = kA8BK * BN;
-    static constexpr int sc_bytes = 2 * WC * 256;   // one 256-byte scale slot per wavefront
+    static constexpr int nsa = (BM + 63) / 64;      // activation-scale slots (64 rows each)
+    static constexpr int sc_bytes = (nsa + 1) * 256;  // + one slot for the weight scales
     static constexpr int stage = a_bytes + b_bytes + sc_bytes;
     static constexpr int S = (kA8Budget / stage) < 8 ? (kA8Budget / stage) : 8;
-    static constexpr int nA = a_bytes / (threads * 16);
+    static constexpr int a_chunks = a_bytes / 1024;  // 1 KB copies (8 rows each)
+    static constexpr int nA = (a_chunks + 2 * WC - 1) / (2 * WC);
     static constexpr int nB = b_bytes / (threads * 16);
     static constexpr int per_tile = nA + nB + 1;
     static constexpr int lanes_per_row = BN / 16;   // 16-byte chunks per B row
+    static_assert(BM % 32 == 0 && 2 * WC >= nsa + 1, "tile shape");
 };
 
 template <bool SWIGLU, int WC>
@@ -88,16 +92,18 @@ __device__ __forceinline__ int bswz_a8(int k) {
     else return ((k >> 1) & 3) ^ (((k >> 5) & 1) << 2);
 }
 
-template <bool SWIGLU, int WC>
+template <bool SWIGLU, int WC, int BM>
 __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, int nN) {
-    typedef RingA8<WC> R;
+    typedef RingA8<WC, BM> R;
     typedef OutA8<SWIGLU, WC> O;
     constexpr int S = R::S;
-    constexpr int LDS = (R::S * R::stage) > kA8BM * O::ld * 2 ? R::S * R::stage : kA8BM * O::ld * 2;
+    constexpr int MI = R::mi;
+    constexpr int LDS = (R::S * R::stage) > BM * O::ld * 2 ? R::S * R::stage : BM * O::ld * 2;
+    static_assert(LDS <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS];
 
     int mt, nt;
-    if (!pick_tile(p, nN, kA8BM, mt, nt)) return;
+    if (!pick_tile(p, nN, BM, mt, nt)) return;
     int g, row0, row_end;
     if (p.tiles) {
         g = p.tiles[4 * mt];
@@ -105,8 +111,8 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
         row_end = p.tiles[4 * mt + 2];
     } else {
         g = 0;
-        row0 = mt * kA8BM;
-        row_end = min(row0 + kA8BM, p.M);
+        row0 = mt * BM;
+        row_end = min(row0 + BM, p.M);
     }
     const int n0 = nt * O::width;
     const bool extra = g == p.extra_group;
@@ -121,13 +127,17 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     };
 
     // ---- copy sources ----
-    // A: copy q of wavefront w fills rows 8 (w nA + q) .. +7; lane -> row
-    // lane/8, physical chunk lane%8, i.e. logical chunk (lane%8) ^ ((row >> 1) & 7)
+    // A: copy q of wavefront w fills chunk a_chunk(q) (rows 8 chunk .. +7);
+    // lane -> row lane/8, physical chunk lane%8, i.e. logical chunk
+    // (lane%8) ^ ((row >> 1) & 7). When the chunks do not divide evenly, the
+    // surplus copies repeat the last chunk (same bytes to the same place), so
+    // every wavefront issues the same number of copies.
+    auto a_chunk = [&](int q) { return min(w + 2 * WC * q, R::a_chunks - 1); };
     const uint8_t *a_src[R::nA];
 #pragma unroll
     for (int q = 0; q < R::nA; ++q) {
-        const long long src = src_row(row0 + 8 * (w * R::nA + q) + (lane >> 3));
-        const int trow = 8 * (w * R::nA + q) + (lane >> 3);  // row within the tile
+        const int trow = 8 * a_chunk(q) + (lane >> 3);  // row within the tile
+        const long long src = src_row(row0 + trow);
         a_src[q] = reinterpret_cast<const uint8_t *>(p.A) + src * p.lda + 16 * ((lane & 7) ^ ((trow >> 1) & 7));
     }
     // B: copy q of wavefront w fills 1024 / BN K rows; lane -> row
@@ -149,13 +159,15 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
         if (col > p.N - 16) col = p.N - 16;
         b_src[q] = reinterpret_cast<const uint8_t *>(base) + gofs + (long long)k * p.N + col;
     }
-    // scale copy of wavefront w (one 4-byte copy per lane and stage):
-    // w = 0, 1: the A scales of rows 64 w .. +63; w >= 2: the weight block
-    // scales, lanes 0 / 1 giving W1 / W3 of block n0 / 128 (gate/up) or W2
-    // blocks n0 / 128 and n0 / 128 + 1 (down); only wavefront 2's slot is read
+    // scale copy of wavefront w (one 4-byte copy per lane and stage) into
+    // slot min(w, nsa): w < nsa: the A scales of rows 64 w .. +63; w >= nsa:
+    // the weight block scales (the same copy into the same slot), lanes 0 / 1
+    // giving W1 / W3 of block n0 / 128 (gate/up) or W2 blocks n0 / 128 and
+    // n0 / 128 + 1 (down)
     const float *sc_src;
     long long sc_step;  // elements per K block
-    if (w < 2) {
+    const int sc_slot = min(w, R::nsa);
+    if (w < R::nsa) {
         sc_src = p.As + src_row(row0 + 64 * w + lane) * p.as_ld;
         sc_step = 1;
     } else {
@@ -172,26 +184,26 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
         uint8_t *st = lds + stage * R::stage;
         const int k0 = kt * kA8BK;
         if (q < R::nA) {
-            copy16(a_src[q] + k0, st + (w * R::nA + q) * 1024);
+            copy16(a_src[q] + k0, st + a_chunk(q) * 1024);
         } else if (q < R::nA + R::nB) {
             const int qb = q - R::nA;
             copy16(b_src[qb] + (long long)k0 * p.N, st + R::a_bytes + (w * R::nB + qb) * 1024);
         } else {
-            copy4(sc_src + (long long)kt * sc_step, st + R::a_bytes + R::b_bytes + w * 256);
+            copy4(sc_src + (long long)kt * sc_step, st + R::a_bytes + R::b_bytes + sc_slot * 256);
         }
     };
 
     // ---- fragment reads: B blocks (4 transposing reads each), then A row
     // blocks (two 16-byte reads each), then the weight scales ----
     struct Frag {
-        i32x8 a[4];
+        i32x8 a[MI];
         i32x8 b[4];
         float s0, s1;
     };
     u32x2 raw[4][4];  // transposed reads of the set being loaded
-    constexpr int NR = 16 + 4 + 1;
+    constexpr int NR = 16 + MI + 1;
     const int i16 = lane & 15, gq = lane >> 4;
-    const int a_row = wr * 64 + i16;  // + 16 m
+    const int a_row = wr * (BM / 2) + i16;  // + 16 m
     auto read = [&](Frag &f, int r, int stage) {
         const uint8_t *st = lds + stage * R::stage;
         if (r < 16) {
@@ -200,7 +212,7 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
             const int k = 32 * gq + 8 * t + (i16 >> 1);
             raw[j][t] = ds_tr8(lds_addr(st + R::a_bytes) + k * R::BN + 16 * ((nb >> 4) ^ bswz_a8<WC>(k)) +
                                8 * (i16 & 1));
-        } else if (r < 20) {
+        } else if (r < 16 + MI) {
             const int m = r - 16;
             const int row = a_row + 16 * m;
             const uint8_t *base = st + row * 128;
@@ -208,7 +220,7 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(base + 16 * ((2 * gq + 1) ^ ((row >> 1) & 7)));
             f.a[m] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         } else {
-            const float *sc = reinterpret_cast<const float *>(st + R::a_bytes + R::b_bytes + 2 * 256);
+            const float *sc = reinterpret_cast<const float *>(st + R::a_bytes + R::b_bytes + R::nsa * 256);
             if (SWIGLU) {
                 f.s0 = sc[0];
                 f.s1 = sc[1];
@@ -228,9 +240,9 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
         }
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[MI][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < MI; ++m)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{};
 
@@ -249,10 +261,10 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
         __builtin_amdgcn_sched_barrier(0);
     };
     // this lane's four row scales (rows 4 (lane/16) + i of row block m)
-    auto read_sa = [&](f32x4 (&sa)[4], int stage) {
+    auto read_sa = [&](f32x4 (&sa)[MI], int stage) {
         const float *sc = reinterpret_cast<const float *>(lds + stage * R::stage + R::a_bytes + R::b_bytes);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) sa[m] = *reinterpret_cast<const f32x4 *>(sc + wr * 64 + 16 * m + 4 * gq);
+        for (int m = 0; m < MI; ++m) sa[m] = *reinterpret_cast<const f32x4 *>(sc + wr * (BM / 2) + 16 * m + 4 * gq);
     };
 
     const int nk = p.K / kA8BK;
@@ -274,18 +286,18 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
         const int nstage = stage + 1 == S ? 0 : stage + 1;
         const int src = min(kt + S, nk - 1);
         // the row scales of tile kt, before the barrier lets its stage refill
-        f32x4 sa[4];
+        f32x4 sa[MI];
         read_sa(sa, stage);
         mma_rows(cur, sa[0], 0);
         wait_vm<(S - 2) * R::per_tile>();
         wait_lds();  // the scale reads are done before anyone refills the stage
         __builtin_amdgcn_s_barrier();
 #pragma unroll
-        for (int c = 0; c < 3; ++c) {
+        for (int c = 0; c < MI - 1; ++c) {
 #pragma unroll
-            for (int q = c * NC / 3; q < (c + 1) * NC / 3; ++q) copy(q, src, stage);
+            for (int q = c * NC / (MI - 1); q < (c + 1) * NC / (MI - 1); ++q) copy(q, src, stage);
 #pragma unroll
-            for (int r = c * NR / 3; r < (c + 1) * NR / 3; ++r) read(nxt, r, nstage);
+            for (int r = c * NR / (MI - 1); r < (c + 1) * NR / (MI - 1); ++r) read(nxt, r, nstage);
             mma_rows(cur, sa[c + 1], c + 1);
         }
         land(nxt);
@@ -303,10 +315,10 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     __syncthreads();
     uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < MI; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = wr * 64 + m * 16 + 4 * gq + i;
+            const int r = wr * (BM / 2) + m * 16 + 4 * gq + i;
             if (SWIGLU) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
@@ -320,14 +332,15 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
             }
         }
     __syncthreads();
-    if constexpr (SWIGLU && O::width == 128 && R::threads == 4 * kA8BM) {
+    if constexpr (SWIGLU && O::width == 128) {
         if (p.Cq) {
             // E4M3 codes of h instead of h: the tile's 128 columns are exactly
             // one 128-column scale group, so each row's scale is complete here.
             // Same arithmetic as the stand-alone row quantiser (scale
             // amax / 448 of the bf16 values, clamp to +-448, round to nearest
-            // even); 4 threads a row, 32 columns each
-            const int r = tid >> 2, part = tid & 3;
+            // even); 4 adjacent threads a row, 32 columns each
+            const int part = tid & 3;
+            for (int r = tid >> 2; r < BM; r += R::threads / 4) {
             float v[32];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -361,13 +374,14 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
                 *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{qw[4], qw[5], qw[6], qw[7]};
                 if (part == 0) p.Cqs[(long long)row * (p.ldc >> 7) + (n0 >> 7)] = sc;
             }
+            }
             return;
         }
     }
     constexpr int W = O::width;
     constexpr int chunks_per_row = W / 8;
     uint16_t *Cg = reinterpret_cast<uint16_t *>(p.C);
-    for (int idx = tid; idx < kA8BM * chunks_per_row; idx += R::threads) {
+    for (int idx = tid; idx < BM * chunks_per_row; idx += R::threads) {
         const int r = idx / chunks_per_row, cc = idx % chunks_per_row;
         const int row = row0 + r, col = n0 + 8 * cc;
         if (row < row_end && col < p.N)
@@ -376,16 +390,16 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     }
 }
 
-template <bool SWIGLU, int WC>
+template <bool SWIGLU, int WC, int BM>
 hipError_t launch_a8(const GemmProblem &p, hipStream_t s) {
     const int W = OutA8<SWIGLU, WC>::width;
     const int nN = (p.N + W - 1) / W;
-    const long long mt_cap = p.tiles ? p.max_tiles : (p.M + kA8BM - 1) / kA8BM;
+    const long long mt_cap = p.tiles ? p.max_tiles : (p.M + BM - 1) / BM;
     long long blocks = mt_cap * nN;
     blocks = (blocks + kXcds - 1) / kXcds * kXcds;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((tiled_a8_kernel<SWIGLU, WC>), dim3((unsigned)blocks), dim3(128 * WC), 0, s, p, nN);
+    hipLaunchKernelGGL((tiled_a8_kernel<SWIGLU, WC, BM>), dim3((unsigned)blocks), dim3(128 * WC), 0, s, p, nN);
     return hipGetLastError();
 }
 
@@ -394,7 +408,11 @@ hipError_t launch_a8(const GemmProblem &p, hipStream_t s) {
 
 bool tiled_a8_supports(int N, int K) { return N >= 128 && N % 128 == 0 && K >= 128 && K % 128 == 0; }
 
-hipError_t launch_tiled_a8(const GemmProblem &p, bool swiglu, hipStream_t s) {
+// 160-row tiles: with up to 160 rows per expert (the DeepSeek-shaped prefill
+// has 93..161) every expert is one tile, so its weights are read once
+int tiled_a8_bm(long long, int) { return 160; }
+
+hipError_t launch_tiled_a8(const GemmProblem &p, bool swiglu, int bm, hipStream_t s) {
     // quantised h output: gate/up only, with whole 128-column scale groups
     if (p.Cq && (!swiglu || !p.Cqs || p.ldc % 128 || tiled::OutA8<true, tiled::kA8WC>::width != 128))
         return hipErrorInvalidValue;
@@ -402,7 +420,11 @@ hipError_t launch_tiled_a8(const GemmProblem &p, bool swiglu, hipStream_t s) {
     if (!p.As || p.as_ld < p.K / 128 || p.ksplit != 1 || !tiled_a8_supports(p.N, p.K) || !p.S0 ||
         (swiglu && (!p.B1 || !p.S1)))
         return hipErrorInvalidValue;
-    return swiglu ? tiled::launch_a8<true, tiled::kA8WC>(p, s) : tiled::launch_a8<false, tiled::kA8WC>(p, s);
+    if (bm == 160)
+        return swiglu ? tiled::launch_a8<true, tiled::kA8WC, 160>(p, s) : tiled::launch_a8<false, tiled::kA8WC, 160>(p, s);
+    if (bm == 128)
+        return swiglu ? tiled::launch_a8<true, tiled::kA8WC, 128>(p, s) : tiled::launch_a8<false, tiled::kA8WC, 128>(p, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace moe
