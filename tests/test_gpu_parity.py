@@ -173,6 +173,43 @@ def test_grouped_ffn(name, path):
         assert err_m <= MIRROR_TOL
 
 
+# Group sizes on both sides of every tile height (128, 160, 256 rows), with
+# empty groups; the rows are pre-permuted token rows drawn by the generator.
+EDGE_SIZES = {
+    "mini_fp8_prefill": [0, 1, 159, 160, 161, 0, 320, 7, 128, 129, 255, 256, 257, 0, 33, 2],
+    "mini_bf16_prefill": [1, 255, 256, 257, 0, 513, 129, 127],  # 1538 rows: 256-row tiles
+}
+EDGE_CASES = [("mini_fp8_prefill", "tiled_a8"), ("mini_fp8_prefill", "tiled"), ("mini_fp8_prefill", "gemv"),
+              ("mini_bf16_prefill", "tiled"), ("mini_bf16_prefill", "gemv")]
+
+
+@pytest.mark.parametrize("name,path", EDGE_CASES)
+def test_grouped_ffn_tile_edges(name, path):
+    import dataclasses
+    from synth import make_layer
+    cfg = MINI_CONFIGS[name]
+    sizes = EDGE_SIZES[name]
+    assert len(sizes) == cfg.E
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(offsets[-1])
+    say(f"[ffn edges] {name} path={path} sizes={sizes}")
+    d = screened_layer(cfg)
+    L = oracle.Layer(d, cfg.k)
+    Xp = make_layer(dataclasses.replace(cfg, name=cfg.name + "_edges", T=M), device="cuda", experts=False)["X"]
+    Yp = moe.grouped_ffn(Xp, _to_dev_i32(offsets), d["W1"], d["W3"], d["W2"], d["S1"], d["S3"], d["S2"], path=path)
+    torch.cuda.synchronize()
+    Xp64 = oracle.to_f64(Xp)
+    ref = oracle.grouped_ffn(Xp64, offsets, L.expert)
+    tol = tol_for(cfg)
+    err = rel_err(Yp, ref)
+    say(f"    max rel err {err:.3e} (tol {tol})")
+    assert err <= tol
+    if path == "tiled_a8":
+        err_m = mean_rel(Yp, oracle.grouped_ffn(Xp64, offsets, L.expert, act_quant=True))
+        say(f"    against the quantisation mirror: mean {err_m:.3e} (tol {MIRROR_TOL})")
+        assert err_m <= MIRROR_TOL
+
+
 @pytest.mark.parametrize("R,C,gather", [(1, 128, False), (37, 384, False), (300, 7168, False),
                                          (520, 512, True)])
 def test_quantize_rows(R, C, gather):
