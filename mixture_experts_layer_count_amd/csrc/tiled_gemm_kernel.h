@@ -179,15 +179,12 @@ __device__ __forceinline__ bool pick_tile(const GemmProblem &p, int nN, int bm, 
         nt = id / n_tiles;
         return true;
     }
-    // group holding id: largest g with starts[g] * nN <= id (binary search)
-    int lo = 0, hi = p.n_groups;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.group_tile_start[mid] * nN <= id) lo = mid;
-        else hi = mid;
-    }
-    const int t0 = p.group_tile_start[lo];
-    const int cnt = p.group_tile_start[lo + 1] - t0;  // > 0: id lies in this group
+    // group holding id: a group's items are [start * nN, next start * nN), so
+    // tile id / nN belongs to it, and the tile's record names the group (two
+    // dependent loads instead of a search over the group starts)
+    const int grp = p.tiles[4 * (id / nN)];
+    const int t0 = p.group_tile_start[grp];
+    const int cnt = p.group_tile_start[grp + 1] - t0;  // > 0: id lies in this group
     int gn = (kBlocksPerXcd + cnt - 1) / cnt;
     if (gn > nN) gn = nN;
     const int j = id - t0 * nN;
