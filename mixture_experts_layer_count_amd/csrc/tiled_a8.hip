@@ -16,13 +16,15 @@
 // a 16x16 output tile (fresh accumulator), which is then added to the result
 // times sa * sw: the scales never meet a partial sum of another block.
 //
-// Tile: 128 rows x BN B-columns x 128 deep, BN = 64 WC; 2 x WC wavefronts in
-// a 2 x WC grid, each 64 rows x 64 B-columns (4 x 4 MFMA tiles). WC = 4 (8
-// wavefronts, two per SIMD, BN = 256) halves the re-reads of the activation
-// rows against WC = 2 and lets one wavefront's copies overlap the other's
-// matrix-core work.
+// Tile: BM rows x BN B-columns x 128 deep, BN = 64 WC; 2 x WC wavefronts in
+// a 2 x WC grid, each BM/2 rows x 64 B-columns. Used: WC = 4 (8 wavefronts,
+// two per SIMD, BN = 256: half the activation re-reads of BN = 128, and one
+// wavefront's copies overlap the other's matrix-core work) and BM = 160 (5 x 4
+// MFMA tiles a wavefront: an expert with up to 160 rows is one tile, so its
+// weights are read once).
 //  * gate/up (SWIGLU): B-columns 0..BN/2-1 are W1[:, n0:n0+BN/2], the rest
-//    W3[:, n0:n0+BN/2]; output columns n0..n0+BN/2-1 (h, bf16).
+//    W3[:, n0:n0+BN/2]; output columns n0..n0+BN/2-1: h as bf16, or as E4M3
+//    codes with one scale per row (the BN/2 = 128 columns are one scale group).
 //  * down (PLAIN): B-columns are W2[:, n0:n0+BN].
 // Pipeline as in the bf16 ring kernel (tiled_gemm_kernel.h): global -> LDS
 // copies (global_load_lds) into a ring of S stages with a fixed count of
@@ -30,18 +32,19 @@
 // between the MFMA groups of the current one.
 //  * A tile: 128-byte rows (128 codes), 16-byte chunk c of row r stored at
 //    c ^ ((r >> 1) & 7), so the 16 rows one 16-lane pass of a ds_read_b128
-//    reads hit 16 distinct 16-byte bank groups (with r & 7, rows r and r + 8
-//    collided: measured 2-way conflicts); an operand is 32 consecutive codes
-//    (two ds_read_b128).
+//    reads hit 16 distinct 16-byte bank groups of the 64 banks (with r & 7,
+//    rows r and r + 8 share one); an operand is 32 consecutive codes (two
+//    ds_read_b128).
 //  * B tile: [K][N] layout, BN-byte rows, 16-byte chunk c of row k stored at
 //    c ^ swz(k), so that the 16 rows that two 16-lane groups of a
 //    ds_read_b64_tr_b8 read land in distinct banks; an operand is four
 //    transposing reads (8 K rows each) of the lane's column.
 //  * the activation scales of the tile's rows ride along with each stage
 //    (gathered through row_src like the rows), and so do the weight block
-//    scales: one 4-byte copy per wavefront and stage (slots: rows 0..63,
-//    rows 64..127, the two weight scales, then unused slots), which keeps
-//    every wavefront's count of copies per stage equal.
+//    scales: one 4-byte copy per wavefront and stage (slots of 64 rows' scales,
+//    then one slot for the two weight scales that every further wavefront
+//    fills with the same copy), which keeps every wavefront's count of copies
+//    per stage equal.
 #include "tiled_gemm_kernel.h"
 
 namespace moe {
