@@ -14,6 +14,7 @@ recorded by libmoe on its own stream around that kernel, in every timed step.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import csv
 import glob
 import hashlib
@@ -188,6 +189,69 @@ def summarize_trace(args) -> int:
     return 0
 
 
+SWEEP_T = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192]
+
+
+def t_sweep(args) -> int:
+    """Token-count sweep of one model shape: the same layer (weights drawn
+    once at the largest T) at T = 1 .. 8192 tokens, each row-streaming (gemv)
+    and tiled path timed, plus the path AUTO takes. Reports ms per layer,
+    tokens/s, the experts the batch touches and their weight bytes' share of
+    the HBM peak (decode view) and the FFN flops' share of the dtype's MFMA
+    peak (prefill view)."""
+    import torch
+    import mixture_experts_layer_count_amd as moe
+    from synth import get_config, make_layer
+
+    base = get_config(args.sweep)
+    Ts = [t for t in SWEEP_T if t <= args.sweep_max_t]
+    cfg = dataclasses.replace(base, name=f"{base.name}_sweep", T=max(Ts))
+    d = make_layer(cfg, device="cuda")
+    paths = ["gemv", "tiled"] + (["tiled_a8"] if cfg.w == "fp8" else [])
+    layers = {p: moe.MoELayer(d, cfg.k, path=p) for p in paths + ["auto"]}
+    wb = weight_bytes(cfg)
+    rows = []
+    for T in Ts:
+        X = d["X"][:T].contiguous()
+        Y = torch.empty_like(X)
+        _, _, _, _, counts = layers["auto"].forward(X, Y, aux=True)
+        torch.cuda.synchronize()
+        touched = int((counts > 0).sum().item())
+        w_bytes = touched * 3 * cfg.H * cfg.F * wb + 3 * cfg.H * cfg.Fs * wb + cfg.H * cfg.E * 2
+        flops = 6.0 * T * cfg.k * cfg.H * cfg.F + 6.0 * T * cfg.H * cfg.Fs
+        rec = {"T": T, "touched_experts": touched}
+        steps = max(3, min(args.steps, int(2e4 // max(T, 1)) or 3))
+        for name in paths + ["auto"]:
+            layer = layers[name]
+            for _ in range(2):
+                layer.forward(X, Y)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                layer.forward(X, Y)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / steps
+            # AUTO takes the tiled form from 15 rows per expert (W8A8 for fp8)
+            a8 = name == "tiled_a8" or (name == "auto" and cfg.w == "fp8" and T * cfg.k >= 15 * cfg.E)
+            rec[name] = {"ms": round(ms, 4), "tokens_per_s": round(T / ms * 1e3, 1),
+                         "hbm_frac": round(w_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                         "mfma_frac": round(flops / (ms * 1e-3) /
+                                            (MFMA_PEAK_TFLOPS["fp8" if a8 else "bf16"] * 1e12), 4)}
+        best = min(paths, key=lambda n: rec[n]["ms"])
+        rec["fastest"] = best
+        rows.append(rec)
+        print(json.dumps(rec), flush=True)
+    print(f"\n| T | touched experts | " + " | ".join(f"{p} ms" for p in paths) +
+          " | auto ms | fastest | auto tokens/s | auto HBM frac | auto MFMA frac |")
+    print("|" + "---:|" * (len(paths) + 3) + "---|---:|---:|---:|")
+    for r in rows:
+        a = r["auto"]
+        print(f"| {r['T']} | {r['touched_experts']} | " + " | ".join(f"{r[p]['ms']:.4f}" for p in paths) +
+              f" | {a['ms']:.4f} | {r['fastest']} | {a['tokens_per_s']:.0f} | {a['hbm_frac']:.3f} | "
+              f"{a['mfma_frac']:.3f} |")
+    return 0
+
+
 COPY_CALIBRATION_BYTES = 1 << 30
 
 
@@ -219,6 +283,9 @@ def main() -> int:
     ap.add_argument("--calib-fetch")
     ap.add_argument("--calib-write")
     ap.add_argument("--commands", nargs="*", default=[])
+    ap.add_argument("--sweep", metavar="WORKLOAD",
+                    help="token-count sweep of this workload's layer shape (T = 1 .. --sweep-max-t), every path")
+    ap.add_argument("--sweep-max-t", type=int, default=8192)
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 kernel-trace run (no GPU)")
     args = ap.parse_args()
@@ -239,6 +306,8 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration()
         return 0
+    if args.sweep:
+        return t_sweep(args)
 
     import mixture_experts_layer_count_amd as moe
     from mixture_experts_layer_count_amd._lib import MOE_N_EVENTS

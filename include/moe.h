@@ -70,7 +70,7 @@ typedef enum {
 } moe_dtype;
 
 /* Expert-FFN kernel choice. AUTO picks the row-streaming (batched GEMV) path
- * when the average rows per expert is small (decode) and the LDS-tiled
+ * when the experts average fewer than 15 rows (decode) and the LDS-tiled
  * grouped GEMM otherwise (prefill); for FP8 weights the tiled choice is
  * TILED_A8. All give results within the same tolerance of the exact layer;
  * the forced values exist for testing and comparison.

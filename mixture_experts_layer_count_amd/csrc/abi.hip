@@ -83,7 +83,9 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path, 
     } else if (path == MOE_PATH_GEMV) {
         p.tiled = false;
     } else {
-        p.tiled = can_tile && (long long)M >= 48LL * G;
+        // the tiled kernels win from about 12-25 rows per group (measured by
+        // token-count sweeps of the Mixtral-, Qwen3- and DeepSeek-shaped layers)
+        p.tiled = can_tile && (long long)M >= 15LL * G;
         p.a8 = p.tiled && can_a8;
     }
     p.bm = p.a8 ? tiled_a8_bm(M, G) : p.tiled ? tiled_gemm_bm(wt, M, G) : kGemvBM;
