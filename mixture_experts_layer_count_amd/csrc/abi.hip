@@ -61,6 +61,8 @@ struct FfnPlan {
     bool tiled;
     bool a8;      // tiled with E4M3 activations (W8A8)
     int bm;
+    int ksplit1;  // split-K of gate/up (row-streaming path; 1: none)
+    int kchunk1;
     int ksplit2;  // split-K of the down projection (row-streaming path)
     int kchunk2;
 };
@@ -89,11 +91,27 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path, 
         p.a8 = p.tiled && can_a8;
     }
     p.bm = p.a8 ? tiled_a8_bm(M, G) : p.tiled ? tiled_gemm_bm(wt, M, G) : kGemvBM;
+    p.ksplit1 = 1;
+    p.kchunk1 = H;
     p.ksplit2 = 1;
     p.kchunk2 = F;
     if (!p.tiled) {
         // enough wavefronts in flight to cover HBM latency: ~2048
         const long long tiles_est = M < G ? M : G;
+        // gate/up: split over H only when its slices alone leave most SIMDs
+        // idle (few touched experts); its fp32 partials are summed and passed
+        // through SwiGLU by one small pass
+        const int slice = w_dt == MOE_FP8_E4M3 ? 128 : 64;
+        const long long waves1 = tiles_est * ((F + slice - 1) / slice);
+        if (waves1 < 1024) {
+            int ks1 = (int)((2048 + waves1 - 1) / (waves1 > 0 ? waves1 : 1));
+            ks1 = ks1 < 1 ? 1 : ks1 > 8 ? 8 : ks1;
+            const int gran1 = w_dt == MOE_FP8_E4M3 ? 128 : 32;
+            int chunk1 = (H + ks1 - 1) / ks1;
+            chunk1 = (chunk1 + gran1 - 1) / gran1 * gran1;
+            p.kchunk1 = chunk1;
+            p.ksplit1 = (H + chunk1 - 1) / chunk1;
+        }
         const long long waves = tiles_est * ((H + 63) / 64);
         int ks = (int)((2048 + waves - 1) / (waves > 0 ? waves : 1));
         ks = ks < 1 ? 1 : ks > 8 ? 8 : ks;
@@ -110,6 +128,7 @@ struct FfnWs {
     int32_t *tiles, *n_tiles, *group_tile_start;
     void *h;     // [rows][hw] SwiGLU activations
     void *part;  // Yp: [ksplit][rows][H] fp32 (row-streaming) or [rows][H] act_dt (tiled)
+    float *part1;  // gate/up split-K partials [ksplit1][rows][2 hw] (g then u), or null
     uint8_t *xq, *hq;  // W8A8: E4M3 codes of the expert inputs [xrows][H] and of h [rows][hw]
     float *xs, *hs;    // and their per-row 128-column scales
 };
@@ -134,6 +153,8 @@ size_t ffn_ws_carve(Carver &c, FfnWs &w, const FfnPlan &p, int rows, int groups,
     w.h = c.take(dt_size(act_dt) * (size_t)rows * hw);
     w.part = p.tiled ? c.take(dt_size(act_dt) * (size_t)rows * H)
                      : c.take(sizeof(float) * (size_t)p.ksplit2 * rows * H);
+    w.part1 = p.ksplit1 > 1 ? static_cast<float *>(c.take(sizeof(float) * (size_t)p.ksplit1 * rows * 2 * hw))
+                            : nullptr;
     if (p.a8) {
         w.xq = static_cast<uint8_t *>(c.take((size_t)xrows * H));
         w.xs = static_cast<float *>(c.take(sizeof(float) * (size_t)xrows * (H / 128)));
@@ -225,6 +246,23 @@ hipError_t run_gemm(const FfnPlan &p, const GemmProblem &g, WType wt, bool swigl
     if (p.a8) return out_bf16 ? launch_tiled_a8(g, swiglu, p.bm, s) : hipErrorInvalidValue;
     return p.tiled ? launch_tiled_gemm(g, wt, swiglu, out_bf16, p.bm, s)
                    : launch_stream_gemm(g, wt, swiglu, out_bf16, s);
+}
+
+// Row-streaming gate/up into h (rows x F, row stride F). With a split plan
+// the GEMM writes fp32 partials of x W1 and x W3 and one pass sums them in
+// fixed order and applies SwiGLU.
+hipError_t run_gate_up_rows(const FfnPlan &p, GemmProblem g, const FfnWs &w, int rows, int F, WType wt,
+                            moe_dtype act_dt, hipStream_t s) {
+    if (p.ksplit1 <= 1) return launch_stream_gemm(g, wt, true, act_dt == MOE_BF16, s);
+    void *h = g.C;
+    g.C = w.part1;
+    g.ldc = 2 * F;
+    g.c_split_stride = (long long)rows * 2 * F;
+    g.ksplit = p.ksplit1;
+    g.kchunk = p.kchunk1;
+    hipError_t e = launch_stream_gemm(g, wt, true, act_dt == MOE_BF16, s);
+    if (e != hipSuccess) return e;
+    return launch_swiglu_splits(w.part1, g.c_split_stride, p.ksplit1, rows, F, act_dt, h, s);
 }
 
 // W8A8 operands: A holds E4M3 codes of rows of `width` values with scales As.
@@ -436,7 +474,8 @@ moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M
         return MOE_OK;
     }
     GemmProblem g1 = gate_up_problem(Xin, row_src, k, &w, G, max_tiles, M, H, F, W1, W3, S1, S3, none, M, w.h);
-    MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
+    if (p.tiled) MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
+    else MOE_TRY(run_gate_up_rows(p, g1, w, M, F, wt, act_dt, stream));
     if (p.tiled) {
         GemmProblem g2 = down_problem(w.h, &w, G, max_tiles, M, H, F, W2, S2, none, M, Yp, 0, 1, F);
         MOE_TRY(run_gemm(p, g2, wt, false, bf, stream));
@@ -533,6 +572,8 @@ ForwardWs carve_forward(const moe_layer_desc *d, int T, void *base) {
             f.plan_s = plan_ffn(T, 1, d->H, d->Fs, d->w_dt, MOE_PATH_GEMV);
         }
         if (!f.plan.tiled && f.plan_s.ksplit2 > f.plan.ksplit2) f.plan.ksplit2 = f.plan_s.ksplit2;
+        f.plan_s.ksplit1 = 1;  // the separate shared-expert gate/up is not split
+        f.plan_s.kchunk1 = d->H;
     }
     const int rows = A + (d->Fs > 0 ? T : 0);
     const int groups = d->E + (f.combined ? 1 : 0);
@@ -613,7 +654,8 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
         g1.Cq = f.ffn.hq;  // h leaves the gate/up GEMM as E4M3 codes
         g1.Cqs = f.ffn.hs;
     }
-    MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
+    if (p.tiled) MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
+    else MOE_TRY(run_gate_up_rows(p, g1, f.ffn, M, F, wt, d->act_dt, stream));
     MOE_TRY(mark(MOE_EV_GATE_UP));
     void *h_s = static_cast<char *>(f.ffn.h) + hb * (size_t)A * hw;
     const ExtraGroup none{};

@@ -129,7 +129,46 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float *part, l
     store4<OutT>(out + 4 * i, v);
 }
 
+// h[r, c] = silu(sum_s G_s[r, c]) * sum_s U_s[r, c], sums in ascending s;
+// part holds per split s the rows [M][2N] with G in columns [0, N) and U in
+// [N, 2N)
+template <typename OutT>
+__global__ __launch_bounds__(256) void swiglu_splits_kernel(const float *part, long long split_stride, int nsplit,
+                                                            int M, int N, OutT *out) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // 4-column group
+    const int n4 = N / 4;
+    if (i >= (long long)M * n4) return;
+    const long long r = i / n4;
+    const int c = 4 * (int)(i - r * n4);
+    const float *p0 = part + r * 2 * N + c;
+    f32x4 g = *reinterpret_cast<const f32x4 *>(p0);
+    f32x4 u = *reinterpret_cast<const f32x4 *>(p0 + N);
+    for (int s = 1; s < nsplit; ++s) {
+        g += *reinterpret_cast<const f32x4 *>(p0 + s * split_stride);
+        u += *reinterpret_cast<const f32x4 *>(p0 + s * split_stride + N);
+    }
+    store4<OutT>(out + r * N + c, f32x4{silu_f32(g[0]) * u[0], silu_f32(g[1]) * u[1], silu_f32(g[2]) * u[2],
+                                        silu_f32(g[3]) * u[3]});
+}
+
 }  // namespace
+
+hipError_t launch_swiglu_splits(const float *part, long long split_stride, int nsplit, int M, int N,
+                                moe_dtype out_dt, void *out, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    if (N % 4 || nsplit < 1) return hipErrorInvalidValue;
+    const long long n = (long long)M * (N / 4);
+    const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    if (out_dt == MOE_F32)
+        hipLaunchKernelGGL(swiglu_splits_kernel<float>, grid, block, 0, s, part, split_stride, nsplit, M, N,
+                           (float *)out);
+    else if (out_dt == MOE_BF16)
+        hipLaunchKernelGGL(swiglu_splits_kernel<uint16_t>, grid, block, 0, s, part, split_stride, nsplit, M, N,
+                           (uint16_t *)out);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(const void *Yp, const void *S, long long split_stride, int nsplit,
                           moe_dtype in_dt, const int32_t *assign_row, const float *w, int T,

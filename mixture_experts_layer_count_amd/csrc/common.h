@@ -125,6 +125,9 @@ struct GemmProblem {
 
 hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,
                               hipStream_t s);
+// h = silu(sum of G partials) * (sum of U partials), rows [M][2N] per split
+hipError_t launch_swiglu_splits(const float *part, long long split_stride, int nsplit, int M, int N,
+                                moe_dtype out_dt, void *out, hipStream_t s);
 
 // Plain bf16 GEMM of M rows (no tile list, no gather) with fp32 output and
 // split-K over blockIdx.y (C + s c_split_stride); every split non-empty.

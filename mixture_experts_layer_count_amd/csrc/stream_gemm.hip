@@ -263,6 +263,27 @@ __global__ __launch_bounds__(kWaves * 64) void stream_gemm_kernel(GemmProblem p,
 
     // epilogue: lane holds C[row0 + 4*(lane>>4) + i][col + c]
     if (!colok) return;
+    if constexpr (SWIGLU) {
+        if (p.ksplit > 1) {
+            // split gate/up: fp32 partials of x W1 (columns [0, N)) and x W3
+            // (columns [N, 2N)) of this K range; SwiGLU follows the sum
+            float *Cf = reinterpret_cast<float *>(p.C) + (long long)split * p.c_split_stride;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = row0 + 4 * kg + i;
+                if (row >= row_end) continue;
+                float *dst = Cf + (long long)row * p.ldc + col;
+#pragma unroll
+                for (int h = 0; h < KV / 4; ++h) {
+                    *reinterpret_cast<f32x4 *>(dst + 4 * h) =
+                        f32x4{acc0[4 * h][i], acc0[4 * h + 1][i], acc0[4 * h + 2][i], acc0[4 * h + 3][i]};
+                    *reinterpret_cast<f32x4 *>(dst + p.N + 4 * h) =
+                        f32x4{acc1[4 * h][i], acc1[4 * h + 1][i], acc1[4 * h + 2][i], acc1[4 * h + 3][i]};
+                }
+            }
+            return;
+        }
+    }
     char *Cb = reinterpret_cast<char *>(p.C);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
