@@ -95,8 +95,14 @@ __device__ __forceinline__ int bswz_a8(int k) {
     else return ((k >> 1) & 3) ^ (((k >> 5) & 1) << 2);
 }
 
-template <bool SWIGLU, int WC, int BM>
-__global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, int nN) {
+// MULTI (plain GEMM only): a workgroup multiplies up to `per_wg`
+// consecutive column tiles of its row tile with one copy ring: the ring runs
+// on across the tile boundary, so only the first tile waits for it to fill,
+// and each finished tile is stored from the accumulators while the next
+// tile's first stages are already in flight.
+template <bool SWIGLU, int WC, int BM, bool MULTI>
+__global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, int nG, int nN, int per_wg) {
+    static_assert(!(MULTI && SWIGLU), "multi-tile workgroups are for the plain GEMM");
     typedef RingA8<WC, BM> R;
     typedef OutA8<SWIGLU, WC> O;
     constexpr int S = R::S;
@@ -105,8 +111,10 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     static_assert(LDS <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS];
 
-    int mt, nt;
-    if (!pick_tile(p, nN, BM, mt, nt)) return;
+    int mt, ng;
+    if (!pick_tile(p, nG, BM, mt, ng)) return;
+    // column tiles of this workgroup: ng * per_wg .. + ntiles - 1
+    const int ntiles = MULTI ? min(per_wg, nN - ng * per_wg) : 1;
     int g, row0, row_end;
     if (p.tiles) {
         g = p.tiles[4 * mt];
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
         row0 = mt * BM;
         row_end = min(row0 + BM, p.M);
     }
-    const int n0 = nt * O::width;
+    const int n0 = (MULTI ? ng * per_wg : ng) * O::width;  // first tile's first column
     const bool extra = g == p.extra_group;
 
     const int tid = threadIdx.x;
@@ -146,7 +154,8 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     // B: copy q of wavefront w fills 1024 / BN K rows; lane -> row
     // lane / lanes_per_row, physical chunk lane % lanes_per_row holding data
     // chunk (physical ^ swizzle)
-    const uint8_t *b_src[R::nB];
+    const uint8_t *b_src[R::nB];  // MULTI: the row start; the column is added per copy
+    int b_col[MULTI ? R::nB : 1];
     const void *B0 = extra ? p.Bx0 : p.B0;
     const void *B1 = extra ? p.Bx1 : p.B1;
     const long long gofs = extra ? 0 : (long long)g * p.b_stride;
@@ -159,8 +168,13 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
         int col;
         if (SWIGLU) { base = c >= LPR / 2 ? B1 : B0; col = n0 + 16 * (c % (LPR / 2)); }
         else { base = B0; col = n0 + 16 * c; }
-        if (col > p.N - 16) col = p.N - 16;
-        b_src[q] = reinterpret_cast<const uint8_t *>(base) + gofs + (long long)k * p.N + col;
+        if constexpr (MULTI) {
+            b_col[q] = col;
+            b_src[q] = reinterpret_cast<const uint8_t *>(base) + gofs + (long long)k * p.N;
+        } else {
+            if (col > p.N - 16) col = p.N - 16;
+            b_src[q] = reinterpret_cast<const uint8_t *>(base) + gofs + (long long)k * p.N + col;
+        }
     }
     // scale copy of wavefront w (one 4-byte copy per lane and stage) into
     // slot min(w, nsa): w < nsa: the A scales of rows 64 w .. +63; w >= nsa:
@@ -169,6 +183,9 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     // n0 / 128 + 1 (down)
     const float *sc_src;
     long long sc_step;  // elements per K block
+    // MULTI: weight-scale block of column tile u: min(sc_off + sc_du u, sc_max)
+    // (all zero for the activation-scale copies)
+    int sc_off = 0, sc_du = 0, sc_max = 0;
     const int sc_slot = min(w, R::nsa);
     if (w < R::nsa) {
         sc_src = p.As + src_row(row0 + 64 * w + lane) * p.as_ld;
@@ -178,21 +195,38 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
         const float *S1 = extra ? p.Sx1 : p.S1;
         const long long sofs = extra ? 0 : (long long)g * p.s_stride;
         if (SWIGLU) sc_src = ((lane & 1) ? S1 : S0) + sofs + (n0 >> 7);
+        else if (MULTI) {
+            sc_src = S0 + sofs;
+            sc_off = (n0 >> 7) + (lane & 1);
+            sc_du = O::width >> 7;
+            sc_max = (p.N >> 7) - 1;
+        }
         else sc_src = S0 + sofs + min((n0 >> 7) + (lane & 1), (p.N >> 7) - 1);
         sc_step = p.N >> 7;
     }
 
+    const int nk = p.K / kA8BK;
     constexpr int NC = R::per_tile;
-    auto copy = [&](int q, int kt, int stage) {
+    // the copies of global step gs: K step kt of column tile u
+    auto copy = [&](int q, int gs, int stage) {
         uint8_t *st = lds + stage * R::stage;
+        const int u = MULTI ? gs / nk : 0;
+        const int kt = gs - u * nk;
         const int k0 = kt * kA8BK;
         if (q < R::nA) {
             copy16(a_src[q] + k0, st + a_chunk(q) * 1024);
         } else if (q < R::nA + R::nB) {
             const int qb = q - R::nA;
-            copy16(b_src[qb] + (long long)k0 * p.N, st + R::a_bytes + (w * R::nB + qb) * 1024);
+            if constexpr (MULTI) {
+                const int col = min(b_col[qb] + u * O::width, p.N - 16);
+                copy16(b_src[qb] + (long long)k0 * p.N + col, st + R::a_bytes + (w * R::nB + qb) * 1024);
+            } else {
+                copy16(b_src[qb] + (long long)k0 * p.N, st + R::a_bytes + (w * R::nB + qb) * 1024);
+            }
         } else {
-            copy4(sc_src + (long long)kt * sc_step, st + R::a_bytes + R::b_bytes + sc_slot * 256);
+            const float *src = sc_src + (long long)kt * sc_step;
+            if (MULTI) src += min(sc_off + sc_du * u, sc_max);
+            copy4(src, st + R::a_bytes + R::b_bytes + sc_slot * 256);
         }
     };
 
@@ -250,46 +284,71 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
         for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{};
 
     // row block m of the current step: 4 MFMAs (one 128-deep block each),
-    // added with scale sa[row] * sw[half]
-    auto mma_rows = [&](const Frag &f, const f32x4 &sa, int m) {
+    // added with scale sa[row] * sw[half]. The weights are the first operand,
+    // so a lane's four results are one row (16 m + lane % 16 of the
+    // wavefront's rows) and four adjacent columns (16 j + 4 (lane / 16) + i):
+    // one row scale per lane, and 8-byte output writes
+    auto mma_rows = [&](const Frag &f, float sa, int m) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const f32x4 t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.a[m], f.b[j], f32x4{0, 0, 0, 0},
+            const f32x4 t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[m], f32x4{0, 0, 0, 0},
                                                                             0, 0, 0, 0, 0, 0);
-            const float sw = (SWIGLU && j >= 2) ? f.s1 : f.s0;
+            const float sc = sa * ((SWIGLU && j >= 2) ? f.s1 : f.s0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(t[i], sa[i] * sw, acc[m][j][i]);
+            for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(t[i], sc, acc[m][j][i]);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    // this lane's four row scales (rows 4 (lane/16) + i of row block m)
-    auto read_sa = [&](f32x4 (&sa)[MI], int stage) {
+    // this lane's row scale in each row block
+    auto read_sa = [&](float (&sa)[MI], int stage) {
         const float *sc = reinterpret_cast<const float *>(lds + stage * R::stage + R::a_bytes + R::b_bytes);
 #pragma unroll
-        for (int m = 0; m < MI; ++m) sa[m] = *reinterpret_cast<const f32x4 *>(sc + wr * (BM / 2) + 16 * m + 4 * gq);
+        for (int m = 0; m < MI; ++m) sa[m] = sc[wr * (BM / 2) + 16 * m + i16];
     };
 
-    const int nk = p.K / kA8BK;
     Frag fa, fb;
+    const int total = ntiles * nk;  // global K steps of this workgroup
 #pragma unroll
     for (int t = 0; t < S; ++t)
 #pragma unroll
-        for (int q = 0; q < NC; ++q) copy(q, min(t, nk - 1), t);
+        for (int q = 0; q < NC; ++q) copy(q, min(t, total - 1), t);
     wait_vm<(S - 1) * R::per_tile>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int r = 0; r < NR; ++r) read(fa, r, 0);
     land(fa);
     int stage = 0;
-    // one K step: multiply tile kt (in cur) while copying tile kt + S and
-    // reading tile kt + 1 into nxt; two steps per loop trip swap the roles of
+    // MULTI: column tile u's bf16 results straight from the accumulators: a
+    // lane holds four adjacent columns of one row, so each store is 8 bytes
+    // and one instruction covers 32 contiguous bytes of 16 rows (the four
+    // stores of j fill the wavefront's 128-byte row segments)
+    auto tile_out = [&](int u) {
+        uint16_t *Cg = reinterpret_cast<uint16_t *>(p.C);
+        const int cbase = n0 + u * O::width + 64 * wc + 4 * gq;
+#pragma unroll
+        for (int m = 0; m < MI; ++m) {
+            const int row = row0 + wr * (BM / 2) + 16 * m + i16;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = cbase + 16 * j;
+                if (row < row_end && col < p.N)
+                    *reinterpret_cast<u32x2 *>(Cg + (long long)row * p.ldc + col) =
+                        u32x2{pack_bf16x2(acc[m][j][0], acc[m][j][1]), pack_bf16x2(acc[m][j][2], acc[m][j][3])};
+                acc[m][j] = f32x4{};
+            }
+        }
+    };
+    // one K step: multiply step gs (in cur) while copying step gs + S and
+    // reading step gs + 1 into nxt; two steps per loop trip swap the roles of
     // the fragment sets, so they are never copied
-    auto step = [&](Frag &cur, Frag &nxt, int kt) {
+    // gs: the global K step; MULTI: the last K step of a column tile stores
+    // the tile and clears the accumulators for the next one
+    auto step = [&](Frag &cur, Frag &nxt, int gs) {
         const int nstage = stage + 1 == S ? 0 : stage + 1;
-        const int src = min(kt + S, nk - 1);
-        // the row scales of tile kt, before the barrier lets its stage refill
-        f32x4 sa[MI];
+        const int src = min(gs + S, total - 1);
+        // the row scales of step gs, before the barrier lets its stage refill
+        float sa[MI];
         read_sa(sa, stage);
         mma_rows(cur, sa[0], 0);
         wait_vm<(S - 2) * R::per_tile>();
@@ -304,8 +363,18 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
             mma_rows(cur, sa[c + 1], c + 1);
         }
         land(nxt);
+        if (MULTI && gs % nk == nk - 1) tile_out(gs / nk);
         stage = nstage;
     };
+    if constexpr (MULTI) {
+        // nk is even, so a column tile's last step is always the second of a pair
+        for (int gs = 0; gs < total; gs += 2) {
+            step(fa, fb, gs);
+            step(fb, fa, gs + 1);
+        }
+        wait_vm<0>();  // the clamped copies of the last steps land before the workgroup ends
+        return;
+    }
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
         step(fa, fb, kt);
@@ -314,26 +383,29 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     if (kt < nk) step(fa, fb, kt);
 
     // ---- epilogue: bf16 tile through LDS, 16-byte row stores ----
+    if constexpr (MULTI) return;
     constexpr int LD = O::ld;
     __syncthreads();
     uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);
 #pragma unroll
-    for (int m = 0; m < MI; ++m)
+    for (int m = 0; m < MI; ++m) {
+        const int r = wr * (BM / 2) + m * 16 + i16;
+        if (SWIGLU) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wr * (BM / 2) + m * 16 + 4 * gq + i;
-            if (SWIGLU) {
+            for (int j = 0; j < 2; ++j) {
+                float v[4];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float v = silu_f32(acc[m][j][i]) * acc[m][j + 2][i];
-                    Cs[r * LD + 32 * wc + 16 * j + i16] = __builtin_bit_cast(uint16_t, (__bf16)v);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    Cs[r * LD + 64 * wc + 16 * j + i16] = __builtin_bit_cast(uint16_t, (__bf16)acc[m][j][i]);
+                for (int i = 0; i < 4; ++i) v[i] = silu_f32(acc[m][j][i]) * acc[m][j + 2][i];
+                *reinterpret_cast<u32x2 *>(Cs + r * LD + 32 * wc + 16 * j + 4 * gq) =
+                    u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x2 *>(Cs + r * LD + 64 * wc + 16 * j + 4 * gq) =
+                    u32x2{pack_bf16x2(acc[m][j][0], acc[m][j][1]), pack_bf16x2(acc[m][j][2], acc[m][j][3])};
         }
+    }
     __syncthreads();
     if constexpr (SWIGLU && O::width == 128) {
         if (p.Cq) {
@@ -393,16 +465,31 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     }
 }
 
+// column tiles per workgroup of the plain GEMM (when K / 128 is even)
+constexpr int kA8TilesPerWg = 4;
+
 template <bool SWIGLU, int WC, int BM>
 hipError_t launch_a8(const GemmProblem &p, hipStream_t s) {
     const int W = OutA8<SWIGLU, WC>::width;
     const int nN = (p.N + W - 1) / W;
+    const int nk = p.K / kA8BK;
+    const bool multi = !SWIGLU && nk % 2 == 0 && kA8TilesPerWg > 1 && nN > 1;
+    const int per_wg = multi ? kA8TilesPerWg : 1;
+    const int nG = (nN + per_wg - 1) / per_wg;
     const long long mt_cap = p.tiles ? p.max_tiles : (p.M + BM - 1) / BM;
-    long long blocks = mt_cap * nN;
+    long long blocks = mt_cap * nG;
     blocks = (blocks + kXcds - 1) / kXcds * kXcds;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((tiled_a8_kernel<SWIGLU, WC, BM>), dim3((unsigned)blocks), dim3(128 * WC), 0, s, p, nN);
+    if constexpr (!SWIGLU) {
+        if (multi) {
+            hipLaunchKernelGGL((tiled_a8_kernel<false, WC, BM, true>), dim3((unsigned)blocks), dim3(128 * WC), 0, s, p,
+                               nG, nN, per_wg);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((tiled_a8_kernel<SWIGLU, WC, BM, false>), dim3((unsigned)blocks), dim3(128 * WC), 0, s, p, nG,
+                       nN, 1);
     return hipGetLastError();
 }
 

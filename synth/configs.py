@@ -64,6 +64,9 @@ MINI_CONFIGS = {
         LayerConfig("mini_bf16_tall", T=1536, H=640, F=416, E=8, k=2, zipf_s=1.1, seed=7),
         LayerConfig("mini_fp8_decode", T=20, H=384, F=256, E=16, k=4, Fs=256, w="fp8", seed=5),
         LayerConfig("mini_fp8_prefill", T=520, H=512, F=384, E=16, k=4, Fs=384, w="fp8", seed=6),
+        # down projection over several 256-column tiles (H = 11 x 128: a
+        # half tile at the end) with an even count of 128-deep K blocks
+        LayerConfig("mini_fp8_wide", T=640, H=1408, F=512, E=16, k=4, Fs=512, w="fp8", seed=8),
     ]
 }
 

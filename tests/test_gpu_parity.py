@@ -178,8 +178,10 @@ def test_grouped_ffn(name, path):
 EDGE_SIZES = {
     "mini_fp8_prefill": [0, 1, 159, 160, 161, 0, 320, 7, 128, 129, 255, 256, 257, 0, 33, 2],
     "mini_bf16_prefill": [1, 255, 256, 257, 0, 513, 129, 127],  # 1538 rows: 256-row tiles
+    "mini_fp8_wide": [0, 1, 159, 160, 161, 0, 320, 7, 128, 129, 255, 256, 257, 0, 33, 2],
 }
-EDGE_CASES = [("mini_fp8_prefill", "tiled_a8"), ("mini_fp8_prefill", "tiled"), ("mini_fp8_prefill", "gemv"),
+EDGE_CASES = [("mini_fp8_prefill", "tiled_a8"), ("mini_fp8_wide", "tiled_a8"), ("mini_fp8_prefill", "tiled"),
+              ("mini_fp8_prefill", "gemv"),
               ("mini_bf16_prefill", "tiled"), ("mini_bf16_prefill", "gemv")]
 
 
