@@ -236,7 +236,11 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     const bool extra = g == p.extra_group;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), wr = w >> 1, wc = w & 1;
+    // 16-row blocks of this wavefront that hold rows of the group; a
+    // wavefront with none (in a short last tile of an expert) skips its MFMAs
+    // (its accumulators stay zero and are never stored)
+    const int nblk = min(max((row_end - row0 - wr * (BM / WR) + 15) >> 4, 0), R::mi);
 
     // ---- copy sources (fixed over K; advanced by k0 per tile) ----
     // A: copy q of wavefront w fills rows 16 (w nA + q) .. +15, lane -> row
@@ -376,12 +380,16 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
         }
 
     // the 8 MFMAs of row block m, kept together as one scheduling group
-    auto mma_rows = [&](const Frags<R::mi, FP8> &f, int m) {
+    // (row blocks m >= ACT, past the group's end, issue none)
+    auto mma_rows = [&](const Frags<R::mi, FP8> &f, int m, auto act) {
+        constexpr int ACT = decltype(act)::value;
         __builtin_amdgcn_sched_barrier(0);
+        if (m < ACT) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if constexpr (FP8) part[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[m], f.b[j], part[m][j], 0, 0, 0);
-            else acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (FP8) part[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[m], f.b[j], part[m][j], 0, 0, 0);
+                else acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -421,27 +429,35 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
 #pragma unroll
     for (int r = 0; r < NR; ++r) read(fa, r, 0);
     land(fa);
-    int stage = 0;  // kt % S
-    for (int kt = 0; kt < nk; ++kt) {
-        const int nstage = stage + 1 == S ? 0 : stage + 1;
-        const int src = min(kt + S, nk - 1);
-        mma_rows(fa, 0);
-        wait_vm<(S - 2) * R::per_tile>();
-        __builtin_amdgcn_s_barrier();
+    // Two copies of the loop: all row blocks active, or none (a wavefront
+    // whose rows all lie past the group's end). Neither copy branches; both
+    // issue the same copies, reads, waits and barriers, and only the MFMAs
+    // differ. (Copies for 1..3 active blocks made the compiler spill.)
+    auto kloop = [&](auto act) {
+        int stage = 0;  // kt % S
+        for (int kt = 0; kt < nk; ++kt) {
+            const int nstage = stage + 1 == S ? 0 : stage + 1;
+            const int src = min(kt + S, nk - 1);
+            mma_rows(fa, 0, act);
+            wait_vm<(S - 2) * R::per_tile>();
+            __builtin_amdgcn_s_barrier();
 #pragma unroll
-        for (int c = 0; c < R::mi - 1; ++c) {
+            for (int c = 0; c < R::mi - 1; ++c) {
 #pragma unroll
-            for (int q = c * NC / (R::mi - 1); q < (c + 1) * NC / (R::mi - 1); ++q) copy(q, src, stage);
+                for (int q = c * NC / (R::mi - 1); q < (c + 1) * NC / (R::mi - 1); ++q) copy(q, src, stage);
 #pragma unroll
-            for (int r = c * NR / (R::mi - 1); r < (c + 1) * NR / (R::mi - 1); ++r) read(fb, r, nstage);
-            mma_rows(fa, c + 1);
+                for (int r = c * NR / (R::mi - 1); r < (c + 1) * NR / (R::mi - 1); ++r) read(fb, r, nstage);
+                mma_rows(fa, c + 1, act);
+            }
+            if constexpr (FP8)
+                if ((kt & 3) == 3) promote(fa);
+            land(fb);
+            fa = fb;
+            stage = nstage;
         }
-        if constexpr (FP8)
-            if ((kt & 3) == 3) promote(fa);
-        land(fb);
-        fa = fb;
-        stage = nstage;
-    }
+    };
+    if (nblk == 0) kloop(std::integral_constant<int, 0>{});
+    else kloop(std::integral_constant<int, R::mi>{});
 
     if constexpr (F32OUT) {
         wait_vm<0>();  // the last (discarded) copies land before the LDS is released
