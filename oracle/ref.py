@@ -346,6 +346,11 @@ class Layer:
     def has_shared(self) -> bool:
         return self.d.get("Ws1") is not None
 
+    def shared_is_fp8(self) -> bool:
+        """The shared expert is stored as E4M3 codes with block scales (it may
+        instead be bf16 beside fp8 routed experts)."""
+        return self.d.get("Ss1") is not None
+
     def shared(self):
         return (self._mat("Ws1", "Ss1"), self._mat("Ws3", "Ss3"), self._mat("Ws2", "Ss2"))
 
@@ -389,6 +394,8 @@ def forward_tokens(layer: Layer, tokens, idx=None, act_quant: bool = False) -> d
     Y = np.einsum("tj,tjh->th", w, y)
     S = None
     if layer.has_shared():
-        S = swiglu_ffn(X, *layer.shared(), act_quant)
+        # activation quantisation belongs to the W8A8 form of fp8 experts: a
+        # bf16 shared expert is mirrored without it
+        S = swiglu_ffn(X, *layer.shared(), act_quant and layer.shared_is_fp8())
         Y = Y + S
     return dict(tokens=tokens, logits=logits, idx=idx, w=w, y=y, S=S, Y=Y)

@@ -110,3 +110,31 @@ def test_round_bf16_matches_torch_and_ties():
     # ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 (bf16 has 7 stored bits): even -> 1
     assert oracle.round_bf16(1.0 + 2.0 ** -8) == 1.0
     assert oracle.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+
+
+def test_mirror_quantises_only_fp8_shared_experts():
+    # activation quantisation is part of the W8A8 form of E4M3 experts: the
+    # mirror applies it to an E4M3 shared expert and leaves a bf16 one exact
+    rng = np.random.default_rng(9)
+    T, H, F, E = 3, 128, 128, 2
+    X = rng.standard_normal((T, H)).astype(np.float32)
+    ones = np.ones((E, 1, 1), dtype=np.float32)
+    codes = [rng.integers(0x20, 0x38, size=(E, H, F)).astype(np.uint8) for _ in range(3)]
+    routed = dict(X=X, Wg=(rng.standard_normal((H, E)) * 0.02).astype(np.float32), gate_bias=None,
+                  W1=codes[0], W3=codes[1], W2=codes[2], S1=ones, S3=ones, S2=ones)
+    shared_codes = [rng.integers(0x20, 0x38, size=(H, F)).astype(np.uint8) for _ in range(3)]
+    one = np.ones((1, 1), dtype=np.float32)
+    shared_vals = [oracle.dequant_blocks(c, one) for c in shared_codes]
+    d_bf16 = dict(routed, Ws1=shared_vals[0].astype(np.float32), Ws3=shared_vals[1].astype(np.float32),
+                  Ws2=shared_vals[2].astype(np.float32), Ss1=None, Ss3=None, Ss2=None)
+    d_fp8 = dict(routed, Ws1=shared_codes[0], Ws3=shared_codes[1], Ws2=shared_codes[2], Ss1=one, Ss3=one, Ss2=one)
+    x64 = X.astype(np.float64)
+    exact = oracle.swiglu_ffn(x64, *shared_vals)
+    mirrored = oracle.swiglu_ffn(x64, *shared_vals, act_quant=True)
+    assert not np.array_equal(exact, mirrored)  # the two readings differ on these inputs
+    out_bf16 = oracle.forward_tokens(oracle.Layer(d_bf16, 1), np.arange(T), act_quant=True)
+    out_fp8 = oracle.forward_tokens(oracle.Layer(d_fp8, 1), np.arange(T), act_quant=True)
+    assert np.array_equal(out_bf16["S"], exact)
+    assert np.array_equal(out_fp8["S"], mirrored)
+    # the routed part is mirrored the same way in both
+    assert np.array_equal(out_bf16["y"], out_fp8["y"])
