@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s at 1 GPU + % HBM peak (decode) / % MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
-DECODE_WORKLOADS = {"toy_fp32", "mixtral_decode", "qwen3_decode", "dsv3_decode"}
+DECODE_WORKLOADS = {"toy_fp32", "mixtral_decode", "qwen3_decode", "dsv3_decode", "dsv3_decode_bf16_shared"}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 # sources of the gate/up kernel each path launches (the traffic record is
 # void once any of them changes)
@@ -68,8 +68,18 @@ def measured_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def weight_bytes(cfg) -> float:
-    return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0}[cfg.w]
+def weight_bytes(cfg, dt=None) -> float:
+    return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0}[dt or cfg.w]
+
+
+def shared_bytes(cfg) -> float:
+    """Weight (and fp8 block-scale) bytes of the shared expert."""
+    if cfg.Fs == 0:
+        return 0.0
+    b = 3 * cfg.H * cfg.Fs * weight_bytes(cfg, cfg.shared_w)
+    if cfg.shared_w == "fp8":
+        b += 3 * (cfg.H // 128) * (cfg.Fs // 128) * 4
+    return b
 
 
 def cpu_baseline(cfg, d, k: int) -> dict:
@@ -217,7 +227,7 @@ def t_sweep(args) -> int:
         _, _, _, _, counts = layers["auto"].forward(X, Y, aux=True)
         torch.cuda.synchronize()
         touched = int((counts > 0).sum().item())
-        w_bytes = touched * 3 * cfg.H * cfg.F * wb + 3 * cfg.H * cfg.Fs * wb + cfg.H * cfg.E * 2
+        w_bytes = touched * 3 * cfg.H * cfg.F * wb + shared_bytes(cfg) + cfg.H * cfg.E * 2
         flops = 6.0 * T * cfg.k * cfg.H * cfg.F + 6.0 * T * cfg.H * cfg.Fs
         rec = {"T": T, "touched_experts": touched}
         steps = max(3, min(args.steps, int(2e4 // max(T, 1)) or 3))
@@ -355,7 +365,7 @@ def main() -> int:
     if cfg.w == "fp8":
         gate_up_w += touched * 2 * (cfg.H // 128) * (cfg.F // 128) * 4
     gate_up_rows = A
-    if cfg.Fs > 0 and cfg.Fs == cfg.F:
+    if cfg.Fs > 0 and cfg.Fs == cfg.F and cfg.shared_w == cfg.w:
         # the always-on shared expert runs as one more group of the same launch
         gate_up_w += 2 * cfg.H * cfg.Fs * wb
         if cfg.w == "fp8":
@@ -385,9 +395,9 @@ def main() -> int:
     roof["algorithmic_flops"] = gate_up_flops
 
     # whole-layer view: touched expert weights (+ gate, shared expert) over the step time
-    layer_w = touched * 3 * cfg.H * cfg.F * wb + cfg.H * cfg.E * ab + 3 * cfg.H * cfg.Fs * wb
+    layer_w = touched * 3 * cfg.H * cfg.F * wb + cfg.H * cfg.E * ab + shared_bytes(cfg)
     if cfg.w == "fp8":
-        layer_w += (touched * 3 * (cfg.H // 128) * (cfg.F // 128) + 3 * (cfg.H // 128) * (cfg.Fs // 128)) * 4
+        layer_w += touched * 3 * (cfg.H // 128) * (cfg.F // 128) * 4
     layer_flops = 6.0 * A * cfg.H * cfg.F + 6.0 * cfg.T * cfg.H * cfg.Fs + 2.0 * cfg.T * cfg.H * cfg.E
 
     out = {
@@ -406,7 +416,8 @@ def main() -> int:
                   else "fp8-e4m3 weights, bf16 activations"}[cfg.w],
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
-                   "Fs": cfg.Fs, "weights": cfg.w, "activations": cfg.act, "path": args.path},
+                   "Fs": cfg.Fs, "weights": cfg.w, "shared_weights": cfg.shared_w if cfg.Fs else None,
+                   "activations": cfg.act, "path": args.path},
         "roofline": roof,
         "layer": {"touched_experts": touched, "weight_bytes": layer_w,
                   "hbm_frac": round(layer_w / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),

@@ -181,8 +181,16 @@ moe_status moe_combine(const void *Yp, const int32_t *assign_row, const float *t
 /* ---------------------------------------------------------------------------
  * Whole layer: route -> permute -> grouped FFN (+ shared expert) -> combine.
  * Weights are borrowed device pointers described by moe_layer_desc. The
- * shared expert (Fs > 0) uses Ws1, Ws3 [H, Fs], Ws2 [Fs, H] (+ Ss* scales
- * for FP8) and is added with weight 1. X [T, H] and Y [T, H] in act_dt.
+ * shared expert (Fs > 0) uses Ws1, Ws3 [H, Fs], Ws2 [Fs, H] in ws_dt (+ Ss*
+ * scales when ws_dt is FP8) and is added with weight 1. ws_dt equals w_dt,
+ * or is BF16 beside FP8 routed experts: the page "MoE-推理部署"
+ * (expert-quantisation section) notes that the shared expert, like the
+ * router, is usually kept at higher precision than the routed experts. A
+ * shared expert whose dtype or width differs from the routed experts' runs
+ * as its own one-group launches; otherwise it is one more group of the routed
+ * launches. ws_dt is ignored when Fs == 0. Unsupported pairs return
+ * MOE_ERR_UNSUPPORTED; scale pointers that do not match ws_dt return
+ * MOE_ERR_INVALID_ARG. X [T, H] and Y [T, H] in act_dt.
  * Optional outputs (NULL to skip): logits [T,E], topk_idx [T,k],
  * topk_w [T,k], counts [E]. Optional `events`: see MOE_EV_* below.
  * Workspace: moe_forward_workspace_bytes(desc, T) bytes.
@@ -197,6 +205,7 @@ typedef struct moe_layer_desc {
     const float *S1, *S3, *S2;
     const void *Ws1, *Ws3, *Ws2;
     const float *Ss1, *Ss3, *Ss2;
+    moe_dtype ws_dt;         /* shared expert weights: w_dt, or BF16 beside FP8 */
 } moe_layer_desc;
 
 /* Stage markers for moe_forward's `events` argument: events[i] is recorded on

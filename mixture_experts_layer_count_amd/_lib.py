@@ -48,6 +48,7 @@ class LayerDesc(ctypes.Structure):
         ("S1", _P), ("S3", _P), ("S2", _P),
         ("Ws1", _P), ("Ws3", _P), ("Ws2", _P),
         ("Ss1", _P), ("Ss3", _P), ("Ss2", _P),
+        ("ws_dt", _I),
     ]
 
 
@@ -224,6 +225,8 @@ class MoELayer:
         d.H, d.F, d.E, d.k, d.Fs = H, F, E, k, Fs
         d.act_dt = act_dtype(self.w["Wg"])
         d.w_dt = weight_dtype(W1)
+        # the shared expert's own dtype (bf16 beside fp8 routed experts allowed)
+        d.ws_dt = weight_dtype(self.w["Ws1"]) if Fs > 0 else d.w_dt
         d.path = PATHS[path]
         for key in self.w:
             setattr(d, key, None if self.w[key] is None else self.w[key].data_ptr())

@@ -508,7 +508,7 @@ moe_status moe_combine(const void *Yp, const int32_t *assign_row, const float *t
     if (H % 4 || T > 65535) return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
     if (!Yp || !assign_row || !topk_w || !Y) return MOE_ERR_INVALID_ARG;
-    return hip_status(launch_combine(Yp, S, 0, 1, act_dt, assign_row, topk_w, T, k, H, act_dt, Y, stream));
+    return hip_status(launch_combine(Yp, S, 0, 1, 1, act_dt, assign_row, topk_w, T, k, H, act_dt, Y, stream));
 }
 
 // ---------------------------------------------------------------------------
@@ -521,17 +521,23 @@ moe_status check_desc(const moe_layer_desc *d) {
     if (d->E > 1024 || d->k > 64 || d->E % 4) return MOE_ERR_UNSUPPORTED;
     moe_status st = check_ffn_dims(d->H, d->F, d->w_dt);
     if (st != MOE_OK) return st;
-    if (d->Fs > 0 && (st = check_ffn_dims(d->H, d->Fs, d->w_dt)) != MOE_OK) return st;
+    // the shared expert: the routed experts' dtype, or bf16 beside fp8
+    if (d->Fs > 0 && d->ws_dt != d->w_dt && !(d->w_dt == MOE_FP8_E4M3 && d->ws_dt == MOE_BF16))
+        return MOE_ERR_UNSUPPORTED;
+    if (d->Fs > 0 && (st = check_ffn_dims(d->H, d->Fs, d->ws_dt)) != MOE_OK) return st;
     if (!path_ok(d->path)) return MOE_ERR_INVALID_ARG;
-    if (d->path == MOE_PATH_TILED_A8 && (d->w_dt != MOE_FP8_E4M3 || (d->Fs > 0 && d->Fs != d->F)))
+    // W8A8 takes an fp8 shared expert only inside its routed launches
+    if (d->path == MOE_PATH_TILED_A8 &&
+        (d->w_dt != MOE_FP8_E4M3 || (d->Fs > 0 && d->ws_dt == MOE_FP8_E4M3 && d->Fs != d->F)))
         return MOE_ERR_UNSUPPORTED;
     if (!d->Wg || !d->W1 || !d->W3 || !d->W2) return MOE_ERR_INVALID_ARG;
     const bool fp8 = d->w_dt == MOE_FP8_E4M3;
     if (fp8 != (d->S1 != nullptr) || fp8 != (d->S3 != nullptr) || fp8 != (d->S2 != nullptr))
         return MOE_ERR_INVALID_ARG;
     if (d->Fs > 0) {
+        const bool sfp8 = d->ws_dt == MOE_FP8_E4M3;
         if (!d->Ws1 || !d->Ws3 || !d->Ws2) return MOE_ERR_INVALID_ARG;
-        if (fp8 != (d->Ss1 != nullptr) || fp8 != (d->Ss3 != nullptr) || fp8 != (d->Ss2 != nullptr))
+        if (sfp8 != (d->Ss1 != nullptr) || sfp8 != (d->Ss3 != nullptr) || sfp8 != (d->Ss2 != nullptr))
             return MOE_ERR_INVALID_ARG;
     }
     return MOE_OK;
@@ -543,7 +549,8 @@ struct ForwardWs {
     void *perm_ws, *route_ws;
     FfnWs ffn;
     FfnPlan plan, plan_s;
-    bool combined;  // shared expert runs as an extra group of the routed launches
+    float *part1_s;  // split-K partials of a separate shared-expert gate/up, or null
+    bool combined;   // shared expert runs as an extra group of the routed launches
     size_t bytes;
 };
 
@@ -560,25 +567,32 @@ ForwardWs carve_forward(const moe_layer_desc *d, int T, void *base) {
     f.assign_row = static_cast<int32_t *>(c.take(sizeof(int32_t) * (size_t)A));
     f.perm_ws = c.take(permute_ws_bytes(A, d->E));
     f.route_ws = c.take(route_ws_bytes(T, d->H, d->E));
-    f.combined = d->Fs > 0 && d->Fs == d->F;
-    // W8A8 needs the shared expert (if any) inside the routed launches
-    f.plan = plan_ffn(A, d->E, d->H, d->F, d->w_dt, d->path, d->Fs == 0 || f.combined);
+    f.combined = d->Fs > 0 && d->Fs == d->F && d->ws_dt == d->w_dt;
+    // W8A8 keeps an fp8 shared expert inside the routed launches (a bf16
+    // one runs on its own, on the bf16 path)
+    f.plan = plan_ffn(A, d->E, d->H, d->F, d->w_dt, d->path,
+                      d->Fs == 0 || f.combined || d->ws_dt == MOE_BF16);
     if (d->Fs > 0 && !f.combined) {
         // separate shared-expert launches; one Yp buffer holds routed rows
         // then shared rows, so both use one format
-        f.plan_s = plan_ffn(T, 1, d->H, d->Fs, d->w_dt, f.plan.tiled ? MOE_PATH_TILED : MOE_PATH_GEMV);
+        f.plan_s = plan_ffn(T, 1, d->H, d->Fs, d->ws_dt, f.plan.tiled ? MOE_PATH_TILED : MOE_PATH_GEMV);
         if (f.plan_s.tiled != f.plan.tiled) {
             f.plan = plan_ffn(A, d->E, d->H, d->F, d->w_dt, MOE_PATH_GEMV);
-            f.plan_s = plan_ffn(T, 1, d->H, d->Fs, d->w_dt, MOE_PATH_GEMV);
+            f.plan_s = plan_ffn(T, 1, d->H, d->Fs, d->ws_dt, MOE_PATH_GEMV);
         }
-        if (!f.plan.tiled && f.plan_s.ksplit2 > f.plan.ksplit2) f.plan.ksplit2 = f.plan_s.ksplit2;
-        f.plan_s.ksplit1 = 1;  // the separate shared-expert gate/up is not split
-        f.plan_s.kchunk1 = d->H;
     }
     const int rows = A + (d->Fs > 0 ? T : 0);
     const int groups = d->E + (f.combined ? 1 : 0);
     const int hw = d->F > d->Fs ? d->F : d->Fs;
-    ffn_ws_carve(c, f.ffn, f.plan, rows, groups, d->H, hw, d->act_dt, T);
+    // row-streaming: the routed and a separate shared down projection keep
+    // their own split counts; the partial buffer holds the larger count
+    FfnPlan carve = f.plan;
+    const bool separate = d->Fs > 0 && !f.combined;
+    if (separate && !f.plan.tiled && f.plan_s.ksplit2 > carve.ksplit2) carve.ksplit2 = f.plan_s.ksplit2;
+    ffn_ws_carve(c, f.ffn, carve, rows, groups, d->H, hw, d->act_dt, T);
+    f.part1_s = nullptr;
+    if (separate && !f.plan_s.tiled && f.plan_s.ksplit1 > 1)
+        f.part1_s = static_cast<float *>(c.take(sizeof(float) * (size_t)f.plan_s.ksplit1 * T * 2 * d->Fs));
     f.bytes = c.used;
     return f;
 }
@@ -612,6 +626,7 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
 
     const int A = T * d->k, H = d->H, F = d->F, E = d->E;
     const WType wt = wtype(d->w_dt);
+    const WType wts = wtype(d->Fs > 0 ? d->ws_dt : d->w_dt);  // separate shared-expert launches
     const bool bf = d->act_dt == MOE_BF16;
     const FfnPlan &p = f.plan;
     const int rows = A + (d->Fs > 0 ? T : 0);
@@ -662,12 +677,19 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     if (d->Fs > 0 && !f.combined) {
         GemmProblem gs = gate_up_problem(X, nullptr, 1, nullptr, 1, 0, T, H, d->Fs, d->Ws1, d->Ws3, d->Ss1,
                                          d->Ss3, none, 0, h_s);
-        MOE_TRY(run_gemm(f.plan_s, gs, wt, true, bf, stream));
+        if (f.plan_s.tiled) {
+            MOE_TRY(run_gemm(f.plan_s, gs, wts, true, bf, stream));
+        } else {
+            // few rows: split over H like a small routed launch (own partials)
+            FfnWs ws_s = f.ffn;
+            ws_s.part1 = f.part1_s;
+            MOE_TRY(run_gate_up_rows(f.plan_s, gs, ws_s, T, d->Fs, wts, d->act_dt, stream));
+        }
     }
     MOE_TRY(mark(MOE_EV_SHARED_GATE_UP));
     const void *S = nullptr;
     long long split_stride = 0;
-    int nsplit = 1;
+    int nsplit = 1, nsplit_s = 1;
     moe_dtype yp_dt = d->act_dt;
     if (p.tiled) {
         GemmProblem g2 = down_problem(f.ffn.h, &f.ffn, E, max_tiles, M, H, F, d->W2, d->S2, ex, A, f.ffn.part,
@@ -679,7 +701,7 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
         if (d->Fs > 0 && !f.combined) {
             GemmProblem g2s = down_problem(h_s, nullptr, 1, 0, T, H, d->Fs, d->Ws2, d->Ss2, none, 0, Sp, 0, 1,
                                            d->Fs);
-            MOE_TRY(run_gemm(f.plan_s, g2s, wt, false, bf, stream));
+            MOE_TRY(run_gemm(f.plan_s, g2s, wts, false, bf, stream));
         }
         if (d->Fs > 0) S = Sp;
     } else {
@@ -687,6 +709,7 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
         // writes zeros), so combine sums a fixed number of slices
         split_stride = (long long)rows * H;
         nsplit = p.ksplit2;
+        nsplit_s = (d->Fs > 0 && !f.combined) ? f.plan_s.ksplit2 : nsplit;
         yp_dt = MOE_F32;
         GemmProblem g2 = down_problem(f.ffn.h, &f.ffn, E, max_tiles, M, H, F, d->W2, d->S2, ex, A, f.ffn.part,
                                       split_stride, nsplit, chunk_for(F, nsplit, d->w_dt));
@@ -695,14 +718,14 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
         float *Sp = static_cast<float *>(f.ffn.part) + (size_t)A * H;
         if (d->Fs > 0 && !f.combined) {
             GemmProblem g2s = down_problem(h_s, nullptr, 1, 0, T, H, d->Fs, d->Ws2, d->Ss2, none, 0, Sp,
-                                           split_stride, nsplit, chunk_for(d->Fs, nsplit, d->w_dt));
-            MOE_TRY(run_gemm(f.plan_s, g2s, wt, false, false, stream));
+                                           split_stride, nsplit_s, chunk_for(d->Fs, nsplit_s, d->ws_dt));
+            MOE_TRY(run_gemm(f.plan_s, g2s, wts, false, false, stream));
         }
         if (d->Fs > 0) S = Sp;
     }
     MOE_TRY(mark(MOE_EV_SHARED_DOWN));
     // 4. combine
-    MOE_TRY(launch_combine(f.ffn.part, S, split_stride, nsplit, yp_dt, f.assign_row, f.w, T, d->k, H,
+    MOE_TRY(launch_combine(f.ffn.part, S, split_stride, nsplit, nsplit_s, yp_dt, f.assign_row, f.w, T, d->k, H,
                            d->act_dt, Y, stream));
     MOE_TRY(mark(MOE_EV_COMBINE));
     return MOE_OK;

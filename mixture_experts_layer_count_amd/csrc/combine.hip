@@ -5,7 +5,8 @@
 // order. §一: an always-on shared expert adds its output with weight 1.
 //
 // Y[t] = sum_{j<k} w[t,j] * (sum_s Yp_s[assign_row[t*k+j]]) (+ sum_s S_s[t]),
-// accumulated in fp32 in ascending j (and ascending split s), then rounded
+// accumulated in fp32 in ascending j (and ascending split s; the shared
+// expert's partials may have their own split count), then rounded
 // once to the output dtype. Each thread owns 8 (or, when H is not a multiple
 // of 8, 4) consecutive columns of one token row; the rows and weights of up
 // to 8 contributions are fetched before their row loads are issued together.
@@ -61,7 +62,7 @@ __device__ __forceinline__ Vec<InT, V> loadv(const InT *p) {
 
 template <typename InT, typename OutT, int V>
 __global__ __launch_bounds__(256) void combine_kernel(const InT *Yp, const InT *S,
-                                                      long long split_stride, int nsplit,
+                                                      long long split_stride, int nsplit, int nsplit_s,
                                                       const int32_t *assign_row, const float *w,
                                                       int T, int k, int H, OutT *Y) {
     const int t = blockIdx.y;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const InT *Yp, const InT *
     }
     if (S) {
         Vec<InT, V> y = loadv<InT, V>(S + (long long)t * H + col);
-        for (int s = 1; s < nsplit; ++s) {
+        for (int s = 1; s < nsplit_s; ++s) {
             const Vec<InT, V> z = loadv<InT, V>(S + s * split_stride + (long long)t * H + col);
 #pragma unroll
             for (int i = 0; i < V / 4; ++i) y.h[i] += z.h[i];
@@ -170,11 +171,11 @@ hipError_t launch_swiglu_splits(const float *part, long long split_stride, int n
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const void *Yp, const void *S, long long split_stride, int nsplit,
+hipError_t launch_combine(const void *Yp, const void *S, long long split_stride, int nsplit, int nsplit_s,
                           moe_dtype in_dt, const int32_t *assign_row, const float *w, int T,
                           int k, int H, moe_dtype out_dt, void *Y, hipStream_t s) {
     if (T <= 0) return hipSuccess;
-    if (H % 4 || nsplit < 1 || T > 65535) return hipErrorInvalidValue;
+    if (H % 4 || nsplit < 1 || nsplit_s < 1 || T > 65535) return hipErrorInvalidValue;
     // 8 columns a thread (16-byte bf16 loads) when H allows, else 4
     const bool v8 = H % 8 == 0;
     const dim3 grid(v8 ? (H / 8 + 255) / 256 : (H / 4 + 255) / 256, T), block(256);
@@ -182,10 +183,10 @@ hipError_t launch_combine(const void *Yp, const void *S, long long split_stride,
     do {                                                                                                  \
         if (v8)                                                                                           \
             hipLaunchKernelGGL((combine_kernel<IT, OT, 8>), grid, block, 0, s, (const IT *)Yp,             \
-                               (const IT *)S, split_stride, nsplit, assign_row, w, T, k, H, (OT *)Y);    \
+                               (const IT *)S, split_stride, nsplit, nsplit_s, assign_row, w, T, k, H, (OT *)Y);    \
         else                                                                                              \
             hipLaunchKernelGGL((combine_kernel<IT, OT, 4>), grid, block, 0, s, (const IT *)Yp,             \
-                               (const IT *)S, split_stride, nsplit, assign_row, w, T, k, H, (OT *)Y);    \
+                               (const IT *)S, split_stride, nsplit, nsplit_s, assign_row, w, T, k, H, (OT *)Y);    \
     } while (0)
     if (in_dt == MOE_F32 && out_dt == MOE_F32) MOE_COMBINE(float, float);
     else if (in_dt == MOE_F32 && out_dt == MOE_BF16) MOE_COMBINE(float, uint16_t);

@@ -177,9 +177,10 @@ hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int
 hipError_t launch_gather_rows(const void *X, int elem_bytes, int H, const int32_t *row_src,
                               int gk, int A, void *Xp, hipStream_t s);
 
-// Combine: Y[t] = sum_j w[t,j] * sum_s Yp_s[assign_row[t*k+j]] (+ sum_s S_s[t]).
+// Combine: Y[t] = sum_j w[t,j] * sum_{s<nsplit} Yp_s[assign_row[t*k+j]]
+//               (+ sum_{s<nsplit_s} S_s[t]).
 // in_dt/out_dt: MOE_F32 or MOE_BF16.
-hipError_t launch_combine(const void *Yp, const void *S, long long split_stride, int nsplit,
+hipError_t launch_combine(const void *Yp, const void *S, long long split_stride, int nsplit, int nsplit_s,
                           moe_dtype in_dt, const int32_t *assign_row, const float *w, int T,
                           int k, int H, moe_dtype out_dt, void *Y, hipStream_t s);
 

@@ -24,10 +24,16 @@ class LayerConfig:
     Fs: int = 0            # shared-expert width; 0 = no shared expert
     act: str = "bf16"      # activation / gate dtype: "f32" or "bf16"
     w: str = "bf16"        # expert weight dtype: "f32", "bf16" or "fp8"
+    ws: str = ""           # shared-expert weight dtype ("" = w; "bf16" beside fp8)
     zipf_s: float = 0.0    # > 0: gate bias b[e] = -s*ln(e+1) (hot low experts)
     x_std: float = 1.0
     w_std: float = 0.02
     seed: int = 0
+
+    @property
+    def shared_w(self) -> str:
+        """Storage dtype of the shared expert's weights."""
+        return self.ws or self.w
 
     @property
     def A(self) -> int:
@@ -48,6 +54,10 @@ CONFIGS = {
         LayerConfig("qwen3_prefill", T=8192, H=2048, F=768, E=128, k=8),
         LayerConfig("dsv3_decode", T=64, H=7168, F=2048, E=256, k=8, Fs=2048, w="fp8"),
         LayerConfig("dsv3_prefill", T=4096, H=7168, F=2048, E=256, k=8, Fs=2048, w="fp8"),
+        # the shared expert kept in bf16 beside the fp8 routed experts (same draws)
+        LayerConfig("dsv3_decode_bf16_shared", T=64, H=7168, F=2048, E=256, k=8, Fs=2048, w="fp8", ws="bf16"),
+        LayerConfig("dsv3_prefill_bf16_shared", T=4096, H=7168, F=2048, E=256, k=8, Fs=2048, w="fp8",
+                    ws="bf16"),
     ]
 }
 
@@ -67,6 +77,12 @@ MINI_CONFIGS = {
         # down projection over several 256-column tiles (H = 11 x 128: a
         # half tile at the end) with an even count of 128-deep K blocks
         LayerConfig("mini_fp8_wide", T=640, H=1408, F=512, E=16, k=4, Fs=512, w="fp8", seed=8),
+        # bf16 shared expert beside fp8 routed experts: as wide as the routed
+        # experts (decode), and narrower, ragged against the tiles (prefill)
+        LayerConfig("mini_fp8_bf16s_decode", T=20, H=384, F=256, E=16, k=4, Fs=256, w="fp8", ws="bf16",
+                    seed=9),
+        LayerConfig("mini_fp8_bf16s_prefill", T=520, H=512, F=384, E=16, k=4, Fs=160, w="fp8", ws="bf16",
+                    seed=10),
     ]
 }
 

@@ -118,7 +118,7 @@ def make_layer(cfg: LayerConfig, device="cpu", experts: bool = True) -> dict:
     out["W2"], out["S2"] = _expert_stack(cfg, "W2", cfg.E, cfg.F, cfg.H, device)
     if cfg.Fs > 0:
         for name, r, c in (("Ws1", cfg.H, cfg.Fs), ("Ws3", cfg.H, cfg.Fs), ("Ws2", cfg.Fs, cfg.H)):
-            w, s = _store(_normal(cfg, name, (r, c), cfg.w_std, device), cfg.w)
+            w, s = _store(_normal(cfg, name, (r, c), cfg.w_std, device), cfg.shared_w)
             out[name] = w
             out["S" + name[1:]] = s
     else:

@@ -131,7 +131,7 @@ def test_forward_validation_and_workspace():
     fp8_no_scales = _desc(w_dt=FP8)
     assert lib.moe_forward(ctypes.byref(fp8_no_scales), FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None,
                            None, None) == INVALID
-    shared_missing = _desc(Fs=512)
+    shared_missing = _desc(Fs=512, ws_dt=BF16)
     assert lib.moe_forward(ctypes.byref(shared_missing), FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None,
                            None, None) == INVALID
     assert lib.moe_forward(ctypes.byref(d), FAKE, 16, FAKE, FAKE, 16, None, None, None, None, None, None) == WS_SMALL
@@ -165,3 +165,36 @@ def test_tiled_a8_path_validation():
     a8 = lib.moe_grouped_ffn_workspace_bytes(m, g, h, f, BF16, FP8, 3)
     w8a16 = lib.moe_grouped_ffn_workspace_bytes(m, g, h, f, BF16, FP8, 2)
     assert a8 >= w8a16 > 0
+
+
+def test_shared_expert_dtype_validation():
+    lib = moe.lib()
+    ws = lib.moe_forward_workspace_bytes
+
+    def status(d):
+        # only for descriptors that validation rejects: nothing is launched
+        return lib.moe_forward(ctypes.byref(d), FAKE, 16, FAKE, FAKE, 1 << 40, None, None, None, None, None, None)
+
+    fp8 = dict(H=512, F=1024, w_dt=FP8, S1=0x1000, S3=0x1000, S2=0x1000,
+               Ws1=0x1000, Ws3=0x1000, Ws2=0x1000)
+    # bf16 shared expert beside fp8 routed experts: accepted, no shared scales
+    ok = _desc(Fs=512, ws_dt=BF16, **fp8)
+    assert ws(ctypes.byref(ok), 16) > 0 and ws(ctypes.byref(ok), 4096) > 0
+    assert status(_desc(Fs=512, ws_dt=BF16, Ss1=0x1000, Ss3=0x1000, Ss2=0x1000, **fp8)) == INVALID
+    # an fp8 shared expert needs its scales
+    assert status(_desc(Fs=1024, ws_dt=FP8, **fp8)) == INVALID
+    assert ws(ctypes.byref(_desc(Fs=1024, ws_dt=FP8, Ss1=0x1000, Ss3=0x1000, Ss2=0x1000, **fp8)), 16) > 0
+    # other pairs: a lower-precision shared expert, or f32 beside bf16
+    bf16 = dict(Ws1=0x1000, Ws3=0x1000, Ws2=0x1000)
+    assert status(_desc(Fs=512, ws_dt=FP8, Ss1=0x1000, Ss3=0x1000, Ss2=0x1000, **bf16)) == UNSUPPORTED
+    assert status(_desc(Fs=512, ws_dt=F32, **bf16)) == UNSUPPORTED
+    # a bf16 shared expert follows the bf16 shape rules (multiples of 32)
+    assert ws(ctypes.byref(_desc(Fs=100, ws_dt=BF16, **fp8)), 16) == 0
+    assert ws(ctypes.byref(_desc(Fs=160, ws_dt=BF16, **fp8)), 16) > 0
+    # without a shared expert ws_dt is ignored
+    assert ws(ctypes.byref(_desc(ws_dt=7)), 16) > 0
+    # the W8A8 path (3) runs a bf16 shared expert of any width beside it, an
+    # fp8 one only when it can join the routed launches
+    assert ws(ctypes.byref(_desc(Fs=512, ws_dt=BF16, path=3, **fp8)), 4096) > 0
+    assert ws(ctypes.byref(_desc(Fs=512, ws_dt=FP8, Ss1=0x1000, Ss3=0x1000, Ss2=0x1000, path=3, **fp8)), 4096) == 0
+    assert ws(ctypes.byref(_desc(Fs=1024, ws_dt=FP8, Ss1=0x1000, Ss3=0x1000, Ss2=0x1000, path=3, **fp8)), 4096) > 0

@@ -3,6 +3,8 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+
 from synth import CONFIGS, MINI_CONFIGS, make_layer, quantize_e4m3_blocks, redraw_rows
 from synth.gen import gate_bias
 
@@ -86,6 +88,24 @@ def test_layer_shapes_and_dtypes():
         else:
             assert d["S1"] is None
         assert (d["Ws1"] is not None) == (cfg.Fs > 0)
+        if cfg.Fs > 0:
+            assert d["Ws1"].shape == (cfg.H, cfg.Fs) and d["Ws2"].shape == (cfg.Fs, cfg.H)
+            assert (d["Ss1"] is not None) == (cfg.shared_w == "fp8")
+            assert d["Ws1"].dtype == (torch.uint8 if cfg.shared_w == "fp8" else torch.bfloat16)
+
+
+def test_bf16_shared_expert_holds_the_same_draws():
+    # the bf16 shared expert of a layer is the same draw as its E4M3 form:
+    # decoding the codes with their block scales lands within E4M3 rounding
+    base = MINI_CONFIGS["mini_fp8_bf16s_decode"]
+    d16 = make_layer(base)
+    d8 = make_layer(base.with_(ws=""))
+    assert torch.equal(d16["W1"], d8["W1"]) and torch.equal(d16["X"], d8["X"])
+    codes, scales = d8["Ws1"], d8["Ss1"]
+    deq = torch.from_numpy(oracle.dequant_blocks(codes.numpy(), scales.numpy()))
+    w16 = d16["Ws1"].double()
+    # E4M3 rounding of the fp32 draw (2^-4 relative) plus the bf16 rounding of it
+    assert (deq - w16).abs().max() <= (2.0 ** -4 + 2.0 ** -8) * w16.abs().max()
 
 
 def test_generation_is_deterministic_and_per_expert():
