@@ -72,6 +72,11 @@ def weight_bytes(cfg, dt=None) -> float:
     return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0}[dt or cfg.w]
 
 
+def gate_bytes(cfg) -> float:
+    """Bytes of the gate matrix (fp32, or the activation dtype)."""
+    return cfg.H * cfg.E * (4.0 if "f32" in (cfg.wg, cfg.act) else 2.0)
+
+
 def shared_bytes(cfg) -> float:
     """Weight (and fp8 block-scale) bytes of the shared expert."""
     if cfg.Fs == 0:
@@ -227,7 +232,7 @@ def t_sweep(args) -> int:
         _, _, _, _, counts = layers["auto"].forward(X, Y, aux=True)
         torch.cuda.synchronize()
         touched = int((counts > 0).sum().item())
-        w_bytes = touched * 3 * cfg.H * cfg.F * wb + shared_bytes(cfg) + cfg.H * cfg.E * 2
+        w_bytes = touched * 3 * cfg.H * cfg.F * wb + shared_bytes(cfg) + gate_bytes(cfg)
         flops = 6.0 * T * cfg.k * cfg.H * cfg.F + 6.0 * T * cfg.H * cfg.Fs
         rec = {"T": T, "touched_experts": touched}
         steps = max(3, min(args.steps, int(2e4 // max(T, 1)) or 3))
@@ -395,7 +400,7 @@ def main() -> int:
     roof["algorithmic_flops"] = gate_up_flops
 
     # whole-layer view: touched expert weights (+ gate, shared expert) over the step time
-    layer_w = touched * 3 * cfg.H * cfg.F * wb + cfg.H * cfg.E * ab + shared_bytes(cfg)
+    layer_w = touched * 3 * cfg.H * cfg.F * wb + gate_bytes(cfg) + shared_bytes(cfg)
     if cfg.w == "fp8":
         layer_w += touched * 3 * (cfg.H // 128) * (cfg.F // 128) * 4
     layer_flops = 6.0 * A * cfg.H * cfg.F + 6.0 * cfg.T * cfg.H * cfg.Fs + 2.0 * cfg.T * cfg.H * cfg.E
@@ -417,6 +422,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
                    "Fs": cfg.Fs, "weights": cfg.w, "shared_weights": cfg.shared_w if cfg.Fs else None,
+                   "gate": cfg.wg or cfg.act,
                    "activations": cfg.act, "path": args.path},
         "roofline": roof,
         "layer": {"touched_experts": touched, "weight_bytes": layer_w,

@@ -95,7 +95,11 @@ const char *moe_status_string(moe_status s);
  *   topk_w[t,j]   = p[t,topk_idx[t,j]] / sum_j' p[t,topk_idx[t,j']], p the
  *     softmax over all E logits; computed as the identical softmax over the
  *     k kept logits, in fp32.
- * X [T,H] and Wg [H,E] in x_dt (F32 or BF16); gate_bias [E] fp32 or NULL.
+ * X [T,H] in x_dt (F32 or BF16); Wg [H,E] in wg_dt: x_dt, or F32 beside
+ * BF16 tokens (the page "MoE-推理部署", expert-quantisation section: the
+ * router is usually kept at higher precision than the experts; every
+ * product is then taken in fp32); other pairs return MOE_ERR_UNSUPPORTED.
+ * gate_bias [E] fp32 or NULL.
  * Outputs: logits [T,E] fp32, topk_idx [T,k] int32, topk_w [T,k] fp32.
  * NaN logits are never selected while a non-NaN logit is left.
  * The sum over h is split into fixed K ranges whose fp32 partial sums are
@@ -104,7 +108,7 @@ const char *moe_status_string(moe_status s);
  * be NULL).
  * ------------------------------------------------------------------------- */
 size_t moe_route_workspace_bytes(int T, int H, int E);
-moe_status moe_route(const void *X, moe_dtype x_dt, const void *Wg, const float *gate_bias,
+moe_status moe_route(const void *X, moe_dtype x_dt, const void *Wg, moe_dtype wg_dt, const float *gate_bias,
                      int T, int H, int E, int k,
                      float *logits, int32_t *topk_idx, float *topk_w,
                      void *ws, size_t ws_bytes, hipStream_t stream);
@@ -199,13 +203,15 @@ typedef struct moe_layer_desc {
     int H, F, E, k, Fs;
     moe_dtype act_dt, w_dt;
     moe_ffn_path path;
-    const void *Wg;          /* [H, E], act_dt */
+    const void *Wg;          /* [H, E], act_dt (fp32 when gate_f32) */
     const float *gate_bias;  /* [E] or NULL */
     const void *W1, *W3, *W2;
     const float *S1, *S3, *S2;
     const void *Ws1, *Ws3, *Ws2;
     const float *Ss1, *Ss3, *Ss2;
     moe_dtype ws_dt;         /* shared expert weights: w_dt, or BF16 beside FP8 */
+    int gate_f32;            /* 0: Wg in act_dt; 1: Wg fp32 (higher-precision
+                                router, see moe_route); other values rejected */
 } moe_layer_desc;
 
 /* Stage markers for moe_forward's `events` argument: events[i] is recorded on

@@ -25,7 +25,7 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_route_workspace_bytes": (_SZ, [_I, _I, _I]),
-    "moe_route": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route": (_I, [_P, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
     "moe_grouped_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
@@ -48,7 +48,7 @@ class LayerDesc(ctypes.Structure):
         ("S1", _P), ("S3", _P), ("S2", _P),
         ("Ws1", _P), ("Ws3", _P), ("Ws2", _P),
         ("Ss1", _P), ("Ss3", _P), ("Ss2", _P),
-        ("ws_dt", _I),
+        ("ws_dt", _I), ("gate_f32", _I),
     ]
 
 
@@ -129,7 +129,8 @@ def route(X, Wg, k: int, gate_bias=None):
     w = torch.empty((T, k), dtype=torch.float32, device=X.device)
     nbytes = lib().moe_route_workspace_bytes(T, H, E)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device)
-    _check("moe_route", lib().moe_route(_ptr(X), act_dtype(X), _ptr(Wg), _ptr(gate_bias), T, H, E, k,
+    # the gate in X's dtype, or fp32 beside bf16 tokens (higher-precision router)
+    _check("moe_route", lib().moe_route(_ptr(X), act_dtype(X), _ptr(Wg), act_dtype(Wg), _ptr(gate_bias), T, H, E, k,
                                         _ptr(logits), _ptr(idx), _ptr(w), _ptr(ws), nbytes, _stream()))
     return logits, idx, w
 
@@ -223,8 +224,14 @@ class MoELayer:
         Fs = 0 if self.w["Ws1"] is None else self.w["Ws1"].shape[1]
         d = LayerDesc()
         d.H, d.F, d.E, d.k, d.Fs = H, F, E, k, Fs
-        d.act_dt = act_dtype(self.w["Wg"])
         d.w_dt = weight_dtype(W1)
+        # activations are f32 with f32 experts, else bf16; the gate may be
+        # fp32 beside bf16 activations (higher-precision router)
+        d.act_dt = MOE_F32 if d.w_dt == MOE_F32 else MOE_BF16
+        gate_dt = act_dtype(self.w["Wg"])
+        if gate_dt != d.act_dt and not (gate_dt == MOE_F32 and d.act_dt == MOE_BF16):
+            raise TypeError("the gate must have the activation dtype, or be float32 beside bfloat16")
+        d.gate_f32 = int(gate_dt == MOE_F32 and d.act_dt == MOE_BF16)
         # the shared expert's own dtype (bf16 beside fp8 routed experts allowed)
         d.ws_dt = weight_dtype(self.w["Ws1"]) if Fs > 0 else d.w_dt
         d.path = PATHS[path]

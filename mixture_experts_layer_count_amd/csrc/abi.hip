@@ -301,8 +301,8 @@ struct RoutePlan {
     bool tiled;
 };
 
-RoutePlan plan_route(int T, int H, int E, moe_dtype x_dt) {
-    if (x_dt == MOE_BF16 && T >= 512 && tiled_f32_supports(T, E, H, 1, H)) {
+RoutePlan plan_route(int T, int H, int E, moe_dtype x_dt, moe_dtype wg_dt) {
+    if (x_dt == MOE_BF16 && wg_dt == MOE_BF16 && T >= 512 && tiled_f32_supports(T, E, H, 1, H)) {
         const long long tiles = (long long)((T + 127) / 128) * ((E + 255) / 256);
         long long ks = 256 / tiles;  // one workgroup per CU, one round
         long long max_ks = H / 256 > 0 ? H / 256 : 1;
@@ -326,21 +326,21 @@ RoutePlan plan_route(int T, int H, int E, moe_dtype x_dt) {
 }
 
 // split-K partials of the router; the larger of the two forms' needs, so the
-// size does not depend on the token dtype
+// size depends on neither the token nor the gate dtype
 size_t route_ws_bytes(int T, int H, int E) {
     size_t need = 0;
     for (moe_dtype dt : {MOE_BF16, MOE_F32}) {
-        const RoutePlan r = plan_route(T, H, E, dt);
+        const RoutePlan r = plan_route(T, H, E, dt, dt);
         const size_t b = r.ksplit > 1 ? (size_t)r.ksplit * T * E * sizeof(float) : 0;
         if (b > need) need = b;
     }
     return need;
 }
 
-moe_status route_impl(const void *X, moe_dtype x_dt, const void *Wg, const float *gate_bias, int T, int H,
-                      int E, int k, float *logits, int32_t *topk_idx, float *topk_w, void *ws,
+moe_status route_impl(const void *X, moe_dtype x_dt, const void *Wg, moe_dtype wg_dt, const float *gate_bias,
+                      int T, int H, int E, int k, float *logits, int32_t *topk_idx, float *topk_w, void *ws,
                       hipStream_t stream) {
-    const RoutePlan r = plan_route(T, H, E, x_dt);
+    const RoutePlan r = plan_route(T, H, E, x_dt, wg_dt);
     float *part = r.ksplit > 1 ? static_cast<float *>(ws) : logits;
     GemmProblem g{};
     g.extra_group = -1;
@@ -357,14 +357,20 @@ moe_status route_impl(const void *X, moe_dtype x_dt, const void *Wg, const float
     g.ksplit = r.ksplit;
     g.kchunk = r.kchunk;
     if (r.tiled) MOE_TRY(launch_tiled_f32(g, stream));
-    else MOE_TRY(launch_stream_gemm(g, x_dt == MOE_F32 ? W_F32 : W_BF16, false, false, stream));
+    else {
+        // fp32 gate against bf16 tokens: the higher-precision router
+        const WType wt = x_dt == MOE_F32 ? W_F32 : (wg_dt == MOE_F32 ? W_F32_XBF16 : W_BF16);
+        MOE_TRY(launch_stream_gemm(g, wt, false, false, stream));
+    }
     return hip_status(launch_topk(part, r.ksplit, (long long)T * E, gate_bias, T, E, k, logits, topk_idx,
                                   topk_w, stream));
 }
 
-moe_status check_route(moe_dtype x_dt, int T, int H, int E, int k) {
+moe_status check_route(moe_dtype x_dt, moe_dtype wg_dt, int T, int H, int E, int k) {
     if (T < 0 || H < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
     if (!act_ok(x_dt)) return MOE_ERR_UNSUPPORTED;
+    // the gate in the token dtype, or fp32 beside bf16 tokens
+    if (wg_dt != x_dt && !(x_dt == MOE_BF16 && wg_dt == MOE_F32)) return MOE_ERR_UNSUPPORTED;
     if (E > 1024 || k > 64 || E % 4 || H % 32) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -376,16 +382,16 @@ size_t moe_route_workspace_bytes(int T, int H, int E) {
     return align_up(route_ws_bytes(T, H, E));
 }
 
-moe_status moe_route(const void *X, moe_dtype x_dt, const void *Wg, const float *gate_bias, int T,
-                     int H, int E, int k, float *logits, int32_t *topk_idx, float *topk_w, void *ws,
+moe_status moe_route(const void *X, moe_dtype x_dt, const void *Wg, moe_dtype wg_dt, const float *gate_bias,
+                     int T, int H, int E, int k, float *logits, int32_t *topk_idx, float *topk_w, void *ws,
                      size_t ws_bytes, hipStream_t stream) {
-    moe_status st = check_route(x_dt, T, H, E, k);
+    moe_status st = check_route(x_dt, wg_dt, T, H, E, k);
     if (st != MOE_OK) return st;
     if (T == 0) return MOE_OK;
     if (!X || !Wg || !logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
     const size_t need = route_ws_bytes(T, H, E);
     if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    return route_impl(X, x_dt, Wg, gate_bias, T, H, E, k, logits, topk_idx, topk_w, ws, stream);
+    return route_impl(X, x_dt, Wg, wg_dt, gate_bias, T, H, E, k, logits, topk_idx, topk_w, ws, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -526,6 +532,7 @@ moe_status check_desc(const moe_layer_desc *d) {
         return MOE_ERR_UNSUPPORTED;
     if (d->Fs > 0 && (st = check_ffn_dims(d->H, d->Fs, d->ws_dt)) != MOE_OK) return st;
     if (!path_ok(d->path)) return MOE_ERR_INVALID_ARG;
+    if (d->gate_f32 != 0 && d->gate_f32 != 1) return MOE_ERR_INVALID_ARG;
     // W8A8 takes an fp8 shared expert only inside its routed launches
     if (d->path == MOE_PATH_TILED_A8 &&
         (d->w_dt != MOE_FP8_E4M3 || (d->Fs > 0 && d->ws_dt == MOE_FP8_E4M3 && d->Fs != d->F)))
@@ -648,8 +655,8 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
 
     MOE_TRY(mark(MOE_EV_START));
     // 1. router
-    st = route_impl(X, d->act_dt, d->Wg, d->gate_bias, T, H, E, d->k, f.logits, f.idx, f.w, f.route_ws,
-                    stream);
+    st = route_impl(X, d->act_dt, d->Wg, d->gate_f32 ? MOE_F32 : d->act_dt, d->gate_bias, T, H, E, d->k,
+                    f.logits, f.idx, f.w, f.route_ws, stream);
     if (st != MOE_OK) return st;
     MOE_TRY(mark(MOE_EV_ROUTE));
     // 2. dispatch (the row gather is fused into the gate/up GEMM's loads)

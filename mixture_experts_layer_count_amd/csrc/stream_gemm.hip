@@ -51,6 +51,11 @@ template <> struct WTraits<W_F32> {
     typedef f32x4 raw;  // 4 columns
     typedef float act;
 };
+template <> struct WTraits<W_F32_XBF16> {
+    typedef float elem;
+    typedef f32x4 raw;  // 4 columns
+    typedef uint16_t act;
+};
 
 // Pack element `c` (0..3) of 8 consecutive K rows (each row: 4 bf16 columns
 // in two dwords) into a K-contiguous bf16x8 MFMA operand.
@@ -132,11 +137,29 @@ __device__ __forceinline__ void mma_step<W_F32>(f32x4 (&acc)[4], const f32x4 (&r
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], r[s][c], acc[c], 0, 0, 0);
 }
 
+// fp32 weights against bf16 token rows: the 8 token values widen exactly to
+// fp32 (a bf16 value is the high half of its fp32 bit pattern) and take the
+// fp32 matrix-core steps of the all-fp32 form
+template <>
+__device__ __forceinline__ void mma_step<W_F32_XBF16>(f32x4 (&acc)[4], const f32x4 (&r)[8], const void *afrag,
+                                                      float) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(afrag);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const uint32_t w = v[s >> 1];
+        const float a = __uint_as_float((s & 1) ? (w & 0xffff0000u) : (w << 16));
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, r[s][c], acc[c], 0, 0, 0);
+    }
+}
+
 // A fragment: 8 consecutive K values of the lane's row (bf16: 16 B, f32: 32 B).
 template <int WT> struct AFrag;
 template <> struct AFrag<W_BF16> { u32x4 v; };
 template <> struct AFrag<W_FP8> { u32x4 v; };
 template <> struct AFrag<W_F32> { f32x4 v[2]; };
+template <> struct AFrag<W_F32_XBF16> { u32x4 v; };
 
 template <int WT>
 __device__ __forceinline__ void load_a(AFrag<WT> &f, const typename WTraits<WT>::act *p, bool ok) {
@@ -343,6 +366,9 @@ hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool 
     case W_F32:
         if (out_bf16) return hipErrorInvalidValue;
         return swiglu ? launch_t<W_F32, true, false>(p, s) : launch_t<W_F32, false, false>(p, s);
+    case W_F32_XBF16:
+        if (swiglu || out_bf16) return hipErrorInvalidValue;
+        return launch_t<W_F32_XBF16, false, false>(p, s);
     }
     return hipErrorInvalidValue;
 }

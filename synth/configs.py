@@ -25,6 +25,7 @@ class LayerConfig:
     act: str = "bf16"      # activation / gate dtype: "f32" or "bf16"
     w: str = "bf16"        # expert weight dtype: "f32", "bf16" or "fp8"
     ws: str = ""           # shared-expert weight dtype ("" = w; "bf16" beside fp8)
+    wg: str = ""           # gate dtype ("" = act; "f32" beside bf16: higher-precision router)
     zipf_s: float = 0.0    # > 0: gate bias b[e] = -s*ln(e+1) (hot low experts)
     x_std: float = 1.0
     w_std: float = 0.02
@@ -58,6 +59,8 @@ CONFIGS = {
         LayerConfig("dsv3_decode_bf16_shared", T=64, H=7168, F=2048, E=256, k=8, Fs=2048, w="fp8", ws="bf16"),
         LayerConfig("dsv3_prefill_bf16_shared", T=4096, H=7168, F=2048, E=256, k=8, Fs=2048, w="fp8",
                     ws="bf16"),
+        # the router kept in fp32 beside bf16 tokens (same draws)
+        LayerConfig("qwen3_prefill_f32_router", T=8192, H=2048, F=768, E=128, k=8, wg="f32"),
     ]
 }
 
@@ -83,6 +86,11 @@ MINI_CONFIGS = {
                     seed=9),
         LayerConfig("mini_fp8_bf16s_prefill", T=520, H=512, F=384, E=16, k=4, Fs=160, w="fp8", ws="bf16",
                     seed=10),
+        # fp32 gate beside bf16 tokens, few tokens and many (where a bf16
+        # gate would take the tiled router)
+        LayerConfig("mini_bf16_f32gate_decode", T=13, H=544, F=672, E=8, k=2, wg="f32", seed=11),
+        LayerConfig("mini_fp8_f32gate_prefill", T=600, H=512, F=384, E=16, k=4, Fs=384, w="fp8", wg="f32",
+                    seed=12),
     ]
 }
 

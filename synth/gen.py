@@ -109,7 +109,7 @@ def make_layer(cfg: LayerConfig, device="cpu", experts: bool = True) -> dict:
     act = _DTYPES[cfg.act]
     out = {"cfg": cfg}
     out["X"] = _normal(cfg, "X", (cfg.T, cfg.H), cfg.x_std, device).to(act).contiguous()
-    out["Wg"] = _normal(cfg, "Wg", (cfg.H, cfg.E), cfg.w_std, device).to(act).contiguous()
+    out["Wg"] = _normal(cfg, "Wg", (cfg.H, cfg.E), cfg.w_std, device).to(_DTYPES[cfg.wg or cfg.act]).contiguous()
     out["gate_bias"] = gate_bias(cfg, device)
     if not experts:
         return out

@@ -48,17 +48,21 @@ def test_status_strings():
 def test_route_validation():
     lib = moe.lib()
     # k > E, k < 1, bad dtype, E not a multiple of 4, H not a multiple of 32
-    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 8, 9, FAKE, FAKE, FAKE, None, 0, None) == INVALID
-    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 8, 0, FAKE, FAKE, FAKE, None, 0, None) == INVALID
-    assert lib.moe_route(FAKE, FP8, FAKE, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
-    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 64, 6, 2, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
-    assert lib.moe_route(FAKE, BF16, FAKE, None, 4, 48, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
-    assert lib.moe_route(None, BF16, FAKE, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == INVALID
+    assert lib.moe_route(FAKE, BF16, FAKE, BF16, None, 4, 64, 8, 9, FAKE, FAKE, FAKE, None, 0, None) == INVALID
+    assert lib.moe_route(FAKE, BF16, FAKE, BF16, None, 4, 64, 8, 0, FAKE, FAKE, FAKE, None, 0, None) == INVALID
+    assert lib.moe_route(FAKE, FP8, FAKE, FP8, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
+    assert lib.moe_route(FAKE, BF16, FAKE, BF16, None, 4, 64, 6, 2, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
+    assert lib.moe_route(FAKE, BF16, FAKE, BF16, None, 4, 48, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
+    assert lib.moe_route(None, BF16, FAKE, BF16, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == INVALID
     # split-K partials need a workspace
     assert lib.moe_route_workspace_bytes(16, 4096, 8) > 0
-    assert lib.moe_route(FAKE, BF16, FAKE, None, 16, 4096, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == WS_SMALL
+    assert lib.moe_route(FAKE, BF16, FAKE, BF16, None, 16, 4096, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == WS_SMALL
     # T == 0: nothing to do, nothing launched
-    assert lib.moe_route(None, BF16, None, None, 0, 64, 8, 2, None, None, None, None, 0, None) == OK
+    assert lib.moe_route(None, BF16, None, BF16, None, 0, 64, 8, 2, None, None, None, None, 0, None) == OK
+    # gate dtypes: the token dtype, or fp32 beside bf16 tokens
+    assert lib.moe_route(FAKE, F32, FAKE, BF16, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
+    assert lib.moe_route(FAKE, BF16, FAKE, FP8, None, 4, 64, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
+    assert lib.moe_route(FAKE, BF16, FAKE, F32, None, 16, 4096, 8, 2, FAKE, FAKE, FAKE, None, 0, None) == WS_SMALL
 
 
 def test_permute_validation_and_workspace():
@@ -191,6 +195,9 @@ def test_shared_expert_dtype_validation():
     # a bf16 shared expert follows the bf16 shape rules (multiples of 32)
     assert ws(ctypes.byref(_desc(Fs=100, ws_dt=BF16, **fp8)), 16) == 0
     assert ws(ctypes.byref(_desc(Fs=160, ws_dt=BF16, **fp8)), 16) > 0
+    # gate_f32 is a 0/1 flag
+    assert ws(ctypes.byref(_desc(gate_f32=1)), 16) > 0
+    assert ws(ctypes.byref(_desc(gate_f32=2)), 16) == 0
     # without a shared expert ws_dt is ignored
     assert ws(ctypes.byref(_desc(ws_dt=7)), 16) > 0
     # the W8A8 path (3) runs a bf16 shared expert of any width beside it, an

@@ -330,7 +330,7 @@ def test_forward_empty_batch():
 
 FULL_SAMPLES = {"toy_fp32": None, "mixtral_decode": None, "qwen3_decode": None,
                 "mixtral_prefill": 6, "qwen3_prefill": 8, "dsv3_decode": 4, "dsv3_prefill": 4,
-                "dsv3_decode_bf16_shared": 4, "dsv3_prefill_bf16_shared": 4}
+                "dsv3_decode_bf16_shared": 4, "dsv3_prefill_bf16_shared": 4, "qwen3_prefill_f32_router": 8}
 
 
 @pytest.mark.parametrize("name", list(CONFIGS))
