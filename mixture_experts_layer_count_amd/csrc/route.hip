@@ -71,28 +71,45 @@ __global__ __launch_bounds__(kWaves * 64) void topk_kernel(const float *part, in
 
     float raw[NPER];              // logit as stored
     unsigned long long key[NPER];  // ranking key (0 once taken)
+    // fixed-order sum (ascending split) of the split-K partials: the loads of
+    // up to 4 of the lane's experts x 16 splits, and their biases, are issued
+    // together so that their latencies overlap
+    constexpr int IG = NPER < 4 ? NPER : 4;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-        const int e = lane + 64 * i;
-        float x = -INFINITY;
-        if (e < E) {
-            // fixed-order sum of the split-K partials (at most 16, loaded
-            // together so their latencies overlap)
-            x = 0.0f;
-            for (int s0 = 0; s0 < nsplit; s0 += 16) {
-                float v[16];
+    for (int i0 = 0; i0 < NPER; i0 += IG) {
+        float x[IG], b[IG];
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    v[u] = (s0 + u < nsplit) ? prow[(long long)(s0 + u) * split_stride + e] : 0.0f;
-#pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    if (s0 + u < nsplit) x = (s0 + u == 0) ? v[u] : x + v[u];
-            }
-            if (bias) x += bias[e];
-            row[e] = x;
+        for (int i = 0; i < IG; ++i) {
+            const int e = lane + 64 * (i0 + i);
+            x[i] = 0.0f;
+            b[i] = (bias && e < E) ? bias[e] : 0.0f;
         }
-        raw[i] = x;
-        key[i] = e < E ? rank_key((x != x) ? -INFINITY : x, e) : 0ull;
+        for (int s0 = 0; s0 < nsplit; s0 += 16) {
+            float v[IG][16];
+#pragma unroll
+            for (int i = 0; i < IG; ++i) {
+                const int e = lane + 64 * (i0 + i);
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    v[i][u] = (e < E && s0 + u < nsplit) ? prow[(long long)(s0 + u) * split_stride + e] : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < IG; ++i)
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    if (s0 + u < nsplit) x[i] = (s0 + u == 0) ? v[i][u] : x[i] + v[i][u];
+        }
+#pragma unroll
+        for (int i = 0; i < IG; ++i) {
+            const int e = lane + 64 * (i0 + i);
+            float xe = -INFINITY;
+            if (e < E) {
+                xe = bias ? x[i] + b[i] : x[i];
+                row[e] = xe;
+            }
+            raw[i0 + i] = xe;
+            key[i0 + i] = e < E ? rank_key((xe != xe) ? -INFINITY : xe, e) : 0ull;
+        }
     }
 
     float sel_val = 0.0f;  // lane j < k keeps the j-th pick
