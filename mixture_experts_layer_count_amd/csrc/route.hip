@@ -8,8 +8,7 @@
 //
 // One wavefront per token. Each lane holds E/64 logits in registers; k rounds
 // of a 64-lane argmax over 64-bit ranking keys (ties to the lower expert
-// index; DPP inside 16-lane rows, two shuffles across them) pick the experts
-// best first. The renormalised weight of the j-th pick equals the
+// index; DPP row steps and row broadcasts) pick the experts best first. The renormalised weight of the j-th pick equals the
 // softmax over the k kept logits, exp(l_j - l_0) / sum_j' exp(l_j' - l_0),
 // because the full softmax's denominator cancels.
 #include <math.h>
@@ -41,21 +40,30 @@ __device__ __forceinline__ unsigned long long dpp_key(unsigned long long x) {
     const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xf, 0xf, false);
     return ((unsigned long long)hi << 32) | lo;
 }
-__device__ __forceinline__ unsigned long long xor_key(unsigned long long x, int d) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, d, 64);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), d, 64);
+// the key of the last lane of an earlier row, for the rows ROW_MASK enables;
+// the other rows keep their own key
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ unsigned long long bcast_key(unsigned long long x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)x, (int)(uint32_t)x, CTRL, ROW_MASK, 0xf,
+                                                             false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(x >> 32), (int)(uint32_t)(x >> 32), CTRL,
+                                                             ROW_MASK, 0xf, false);
     return ((unsigned long long)hi << 32) | lo;
 }
-// wavefront-wide maximum key, in every lane: quad permutations and row
-// rotations inside each 16-lane row, then two exchanges across rows
+// wavefront-wide maximum key, the same in every lane: quad permutations and
+// row rotations give every lane its 16-lane row's maximum; row broadcasts
+// (lane 15 into row 1 and row 3, then lane 31 into rows 2 and 3) leave the
+// wavefront's maximum in lane 63, which is read out. All VALU (DPP) steps.
 __device__ __forceinline__ unsigned long long wave_max_key(unsigned long long x) {
     x = kmax(x, dpp_key<0xB1>(x));   // quad_perm [1,0,3,2]
     x = kmax(x, dpp_key<0x4E>(x));   // quad_perm [2,3,0,1]
     x = kmax(x, dpp_key<0x124>(x));  // row_ror:4
     x = kmax(x, dpp_key<0x128>(x));  // row_ror:8
-    x = kmax(x, xor_key(x, 16));
-    x = kmax(x, xor_key(x, 32));
-    return x;
+    x = kmax(x, bcast_key<0x142, 0xa>(x));  // row_bcast:15 into rows 1, 3
+    x = kmax(x, bcast_key<0x143, 0xc>(x));  // row_bcast:31 into rows 2, 3
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+    return ((unsigned long long)hi << 32) | lo;
 }
 
 template <int NPER>
@@ -134,11 +142,12 @@ __global__ __launch_bounds__(kWaves * 64) void topk_kernel(const float *part, in
         }
     }
 
-    const float top = __shfl(sel_val, 0, 64);
-    float ex = (lane < k) ? expf(sel_val - top) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) sum += __shfl_xor(sum, d, 64);
+    const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_val), 0));
+    const float ex = (lane < k) ? expf(sel_val - top) : 0.0f;
+    // the normaliser, summed over the picks in slot order (the same value in
+    // every lane)
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
     if (lane < k) {
         idx[(long long)t * k + lane] = sel_idx;
         w[(long long)t * k + lane] = ex / sum;
