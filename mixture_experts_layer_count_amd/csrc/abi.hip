@@ -659,12 +659,22 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
                     f.logits, f.idx, f.w, f.route_ws, stream);
     if (st != MOE_OK) return st;
     MOE_TRY(mark(MOE_EV_ROUTE));
-    // 2. dispatch (the row gather is fused into the gate/up GEMM's loads)
-    MOE_TRY(launch_permute(f.idx, A, E, f.counts, f.offsets, f.row_src, f.assign_row, f.perm_ws, stream));
+    // 2. dispatch (the row gather is fused into the gate/up GEMM's loads);
+    // a one-block permutation also writes the GEMMs' tile list
+    TileRequest tr;
+    tr.tiles = f.ffn.tiles;
+    tr.n_tiles = f.ffn.n_tiles;
+    tr.group_tile_start = f.ffn.group_tile_start;
+    tr.extra_rows = ex.rows;
+    tr.bm = p.bm;
+    bool tiles_built = false;
+    MOE_TRY(launch_permute(f.idx, A, E, f.counts, f.offsets, f.row_src, f.assign_row, f.perm_ws, stream, &tr,
+                           &tiles_built));
     MOE_TRY(mark(MOE_EV_PERMUTE));
     // 3. expert FFN; with `combined` the shared expert is group E of the same launches
-    MOE_TRY(launch_build_tiles(f.offsets, E, ex.rows, p.bm, f.ffn.tiles, f.ffn.n_tiles, f.ffn.group_tile_start,
-                               stream));
+    if (!tiles_built)
+        MOE_TRY(launch_build_tiles(f.offsets, E, ex.rows, p.bm, f.ffn.tiles, f.ffn.n_tiles,
+                                   f.ffn.group_tile_start, stream));
     // W8A8: the token rows are quantised once (per-row scales, so the gather
     // in the GEMM's loads picks the same codes as quantising gathered rows)
     if (p.a8) MOE_TRY(launch_quant_rows(X, H, nullptr, 1, T, H, f.ffn.xq, f.ffn.xs, stream));

@@ -172,10 +172,21 @@ hipError_t launch_build_tiles(const int32_t *offsets, int G, int extra_rows, int
 hipError_t launch_topk(const float *part, int nsplit, long long split_stride, const float *bias,
                        int T, int E, int k, float *logits, int32_t *idx, float *w, hipStream_t s);
 
-// Permutation (count / scan / scatter) and optional row gather.
+// Tile list requested from the permutation (same records as
+// launch_build_tiles for the E expert groups plus an extra group of
+// extra_rows rows).
+struct TileRequest {
+    int32_t *tiles = nullptr, *n_tiles = nullptr, *group_tile_start = nullptr;
+    int extra_rows = 0, bm = 0;
+};
+
+// Permutation (count / scan / scatter) and optional row gather. With `tr`,
+// a permutation that runs in one block also writes the tile list; then
+// *tiles_built is set and no launch_build_tiles is needed.
 size_t permute_ws_bytes(int A, int E);
 hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int32_t *offsets,
-                          int32_t *row_src, int32_t *assign_row, void *ws, hipStream_t s);
+                          int32_t *row_src, int32_t *assign_row, void *ws, hipStream_t s,
+                          const TileRequest *tr = nullptr, bool *tiles_built = nullptr);
 hipError_t launch_gather_rows(const void *X, int elem_bytes, int H, const int32_t *row_src,
                               int gk, int A, void *Xp, hipStream_t s);
 

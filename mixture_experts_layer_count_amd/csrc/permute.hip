@@ -15,7 +15,9 @@
 //  2. scan (one block): per expert, an exclusive sum over chunks, then an
 //     exclusive scan over experts gives offsets; chunk bases are offset by it.
 //  3. scatter: row = chunk base + rank; row_src[row] = a, assign_row[a] = row.
-// When all assignments fit one chunk, the three steps run in one block.
+// When all assignments fit one chunk, the three steps run in one block, and
+// that block also writes the grouped GEMMs' tile list (the work of
+// build_tiles_kernel) from the offsets it has just formed, saving a launch.
 #include "common.h"
 
 namespace moe {
@@ -32,7 +34,7 @@ __device__ __forceinline__ int ceil_log2(int E) {
 template <bool SINGLE>
 __global__ __launch_bounds__(kChunk) void permute_rank_kernel(
     const int32_t *idx, int A, int E, int32_t *chunk_counts, int32_t *rank, int32_t *counts,
-    int32_t *offsets, int32_t *row_src, int32_t *assign_row) {
+    int32_t *offsets, int32_t *row_src, int32_t *assign_row, TileRequest tr) {
     // [16][E] per-wave counts, then per-wave prefixes (<= 1024: 16 bits)
     extern __shared__ unsigned short lds[];
     __shared__ int scan_lds[16];
@@ -88,6 +90,34 @@ __global__ __launch_bounds__(kChunk) void permute_rank_kernel(
             const int row = off_lds[e] + r_in_chunk;
             row_src[row] = a;
             assign_row[a] = row;
+        }
+        if (tr.tiles) {
+            // tile list: group g's rows [lo, hi) in tiles of bm rows, groups
+            // in order (the extra group's rows follow the routed ones); the
+            // host guarantees E + 1 <= 1024 groups
+            const int NG = E + (tr.extra_rows > 0 ? 1 : 0);
+            int lo = 0, hi = 0, n = 0;
+            if (tid < NG) {
+                lo = tid < E ? off : all;
+                hi = tid < E ? off + total : all + tr.extra_rows;
+                n = (hi - lo + tr.bm - 1) / tr.bm;
+            }
+            int nt = 0;
+            const int first = block_exclusive_scan(n, scan_lds, &nt);
+            if (tid < NG) {
+                if (tr.group_tile_start) tr.group_tile_start[tid] = first;
+                for (int i = 0; i < n; ++i) {
+                    int32_t *t = tr.tiles + 4 * (first + i);
+                    t[0] = tid;
+                    t[1] = lo + i * tr.bm;
+                    t[2] = min(lo + (i + 1) * tr.bm, hi);
+                    t[3] = 0;
+                }
+            }
+            if (tid == 0) {
+                *tr.n_tiles = nt;
+                if (tr.group_tile_start) tr.group_tile_start[NG] = nt;
+            }
         }
     }
 }
@@ -186,19 +216,27 @@ size_t permute_ws_bytes(int A, int E) {
 }
 
 hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int32_t *offsets,
-                          int32_t *row_src, int32_t *assign_row, void *ws, hipStream_t s) {
+                          int32_t *row_src, int32_t *assign_row, void *ws, hipStream_t s,
+                          const TileRequest *tr, bool *tiles_built) {
     if (A < 0 || E < 1 || E > 1024) return hipErrorInvalidValue;
+    if (tiles_built) *tiles_built = false;
     const int nchunks = (A + kChunk - 1) / kChunk;
     const size_t lds = (size_t)16 * E * sizeof(unsigned short);
     if (nchunks <= 1) {
+        TileRequest t{};
+        if (tr && tr->tiles && tr->n_tiles && tr->bm > 0 && tr->extra_rows >= 0 &&
+            E + (tr->extra_rows > 0 ? 1 : 0) <= kChunk) {
+            t = *tr;
+            if (tiles_built) *tiles_built = true;
+        }
         hipLaunchKernelGGL(permute_rank_kernel<true>, dim3(1), dim3(kChunk), lds, s, idx, A, E,
-                           nullptr, nullptr, counts, offsets, row_src, assign_row);
+                           nullptr, nullptr, counts, offsets, row_src, assign_row, t);
         return hipGetLastError();
     }
     int32_t *chunk_counts = reinterpret_cast<int32_t *>(ws);
     int32_t *rank = chunk_counts + (size_t)nchunks * E;
     hipLaunchKernelGGL(permute_rank_kernel<false>, dim3(nchunks), dim3(kChunk), lds, s, idx, A, E,
-                       chunk_counts, rank, nullptr, nullptr, nullptr, nullptr);
+                       chunk_counts, rank, nullptr, nullptr, nullptr, nullptr, TileRequest{});
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, E,
