@@ -140,6 +140,9 @@ def test_forward_validation_and_workspace():
                            None, None) == INVALID
     assert lib.moe_forward(ctypes.byref(d), FAKE, 16, FAKE, FAKE, 16, None, None, None, None, None, None) == WS_SMALL
     assert lib.moe_forward(ctypes.byref(d), None, 0, None, None, 0, None, None, None, None, None, None) == OK
+    # the largest batch is 65535 tokens
+    assert lib.moe_forward(ctypes.byref(d), FAKE, 65536, FAKE, FAKE, 1 << 40, None, None, None, None, None,
+                           None) == UNSUPPORTED
 
 
 def test_quantize_validation():

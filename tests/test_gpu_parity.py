@@ -344,3 +344,26 @@ def test_forward_full_size(name):
         rng = np.random.default_rng(cfg.T)
         tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, size=n - 2, replace=False)]))
     _check_forward(cfg, d, moe.MoELayer(d, cfg.k), tokens)
+
+
+# The method's size limits: 1024 experts (the most the router and permutation
+# take) with and without the shared expert's extra group (1025 groups do not
+# fit the one-block tile list, so that case builds it separately), and the
+# largest batch (65535 tokens) on a small layer, checked on sampled tokens.
+LIMIT_CASES = {
+    "E1024": LayerConfig("limit_E1024", T=40, H=128, F=64, E=1024, k=2, seed=21),
+    "E1024_shared": LayerConfig("limit_E1024_shared", T=40, H=128, F=64, E=1024, k=2, Fs=64, seed=22),
+    "T65535": LayerConfig("limit_T65535", T=65535, H=64, F=64, E=8, k=2, seed=23),
+}
+
+
+@pytest.mark.parametrize("name", list(LIMIT_CASES))
+def test_forward_size_limits(name):
+    cfg = LIMIT_CASES[name]
+    say(f"[forward] size limit {name}: T={cfg.T} H={cfg.H} F={cfg.F} E={cfg.E} k={cfg.k} Fs={cfg.Fs}")
+    d = screened_layer(cfg)
+    tokens = None
+    if cfg.T > 4096:
+        rng = np.random.default_rng(cfg.seed)
+        tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, size=30, replace=False)]))
+    _check_forward(cfg, d, moe.MoELayer(d, cfg.k), tokens)
