@@ -7,9 +7,11 @@
 // Y[t] = sum_{j<k} w[t,j] * (sum_s Yp_s[assign_row[t*k+j]]) (+ sum_s S_s[t]),
 // accumulated in fp32 in ascending j (and ascending split s; the shared
 // expert's partials may have their own split count), then rounded
-// once to the output dtype. Each thread owns 8 (or, when H is not a multiple
-// of 8, 4) consecutive columns of one token row; the rows and weights of up
-// to 8 contributions are fetched before their row loads are issued together.
+// once to the output dtype. Each thread owns 16 consecutive columns of one
+// token row for bf16 rows (two 16-byte loads per row; 128-thread blocks when
+// a row needs no more), else 8 or, when H is not a multiple of 8, 4; the rows
+// and weights of up to 8 contributions are fetched before their row loads are
+// issued together.
 #include "common.h"
 
 namespace moe {
@@ -41,7 +43,7 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t *p, f32x4 v) {
     *reinterpret_cast<u32x2 *>(p) = o;
 }
 
-// V = 4 or 8 consecutive columns per thread (two 4-column halves)
+// V = 4, 8 or 16 consecutive columns per thread (4-column quarters)
 template <typename InT, int V>
 struct Vec {
     f32x4 h[V / 4];
@@ -49,10 +51,13 @@ struct Vec {
 template <typename InT, int V>
 __device__ __forceinline__ Vec<InT, V> loadv(const InT *p) {
     Vec<InT, V> r;
-    if constexpr (V == 8 && sizeof(InT) == 2) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
-        r.h[0] = f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
-        r.h[1] = f32x4{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
+    if constexpr ((V == 8 || V == 16) && sizeof(InT) == 2) {
+#pragma unroll
+        for (int q = 0; q < V / 8; ++q) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(p + 8 * q);
+            r.h[2 * q] = f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
+            r.h[2 * q + 1] = f32x4{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < V / 4; ++i) r.h[i] = load4<InT>(p + 4 * i);
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const InT *Yp, const InT *
                                                       const int32_t *assign_row, const float *w,
                                                       int T, int k, int H, OutT *Y) {
     const int t = blockIdx.y;
-    const int col = (blockIdx.x * 256 + threadIdx.x) * V;
+    const int col = (blockIdx.x * blockDim.x + threadIdx.x) * V;
     if (t >= T || col >= H) return;
     f32x4 acc[V / 4];
 #pragma unroll
@@ -176,12 +181,19 @@ hipError_t launch_combine(const void *Yp, const void *S, long long split_stride,
                           int k, int H, moe_dtype out_dt, void *Y, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     if (H % 4 || nsplit < 1 || nsplit_s < 1 || T > 65535) return hipErrorInvalidValue;
-    // 8 columns a thread (16-byte bf16 loads) when H allows, else 4
+    // 16 bf16 columns a thread (two 16-byte loads per row) when H allows
+    const bool v16 = H % 16 == 0 && in_dt == MOE_BF16;
     const bool v8 = H % 8 == 0;
-    const dim3 grid(v8 ? (H / 8 + 255) / 256 : (H / 4 + 255) / 256, T), block(256);
+    const int vw = v16 ? 16 : v8 ? 8 : 4;
+    const int nthr = H / vw;
+    const int bs = nthr <= 128 ? 128 : 256;
+    const dim3 grid((nthr + bs - 1) / bs, T), block(bs);
 #define MOE_COMBINE(IT, OT)                                                                               \
     do {                                                                                                  \
-        if (v8)                                                                                           \
+        if (v16)                                                                                          \
+            hipLaunchKernelGGL((combine_kernel<IT, OT, 16>), grid, block, 0, s, (const IT *)Yp,            \
+                               (const IT *)S, split_stride, nsplit, nsplit_s, assign_row, w, T, k, H, (OT *)Y); \
+        else if (v8)                                                                                      \
             hipLaunchKernelGGL((combine_kernel<IT, OT, 8>), grid, block, 0, s, (const IT *)Yp,             \
                                (const IT *)S, split_stride, nsplit, nsplit_s, assign_row, w, T, k, H, (OT *)Y);    \
         else                                                                                              \
