@@ -7,8 +7,9 @@
 // grouped GEMM (one group, fp32 accumulation).
 //
 // One wavefront per token. Each lane holds E/64 logits in registers; k rounds
-// of a 64-lane argmax over 64-bit ranking keys (ties to the lower expert
-// index; DPP row steps and row broadcasts) pick the experts best first. The renormalised weight of the j-th pick equals the
+// of a 64-lane argmax pick the experts best first: the largest 32-bit ranking
+// key by DPP row steps and row broadcasts, then the lowest expert index
+// holding it by ballot (ties go to the lower index). The renormalised weight of the j-th pick equals the
 // softmax over the k kept logits, exp(l_j - l_0) / sum_j' exp(l_j' - l_0),
 // because the full softmax's denominator cancels.
 #include <math.h>
@@ -20,50 +21,38 @@ namespace {
 
 constexpr int kWaves = 4;
 
-// Ranking key of (logit, expert): the logit's bits made monotonic as an
-// unsigned integer in the high word, the complemented expert index in the low
-// word, so a larger key means a larger logit, then the lower index. Every
-// real key is above 0, which marks taken entries. (NaN logits are ranked as
-// -inf before they get here.)
-__device__ __forceinline__ unsigned long long rank_key(float v, int e) {
-    uint32_t b = __float_as_uint(v);
-    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    return ((unsigned long long)b << 32) | (uint32_t)(~e);
+// Ranking key of a logit: its bits made monotonic as an unsigned integer, so
+// a larger key means a larger logit. Every real key is above 0 (-inf maps to
+// 0x007fffff), and 0 marks taken entries. (NaN logits are ranked as -inf
+// before they get here.) Equal keys go to the lower expert index, found by
+// ballot after the maximum.
+__device__ __forceinline__ uint32_t rank_key(float v) {
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-__device__ __forceinline__ unsigned long long kmax(unsigned long long a, unsigned long long b) {
-    return a > b ? a : b;
-}
-// the key of another lane of the same 16-lane row (DPP: no LDS round trip)
+// DPP row steps: the key of another lane of the same 16-lane row, or (with a
+// row mask) of the last lane of an earlier row for the enabled rows, the
+// other rows keeping their own
 template <int CTRL>
-__device__ __forceinline__ unsigned long long dpp_key(unsigned long long x) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xf, 0xf, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xf, 0xf, false);
-    return ((unsigned long long)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp_key(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
 }
-// the key of the last lane of an earlier row, for the rows ROW_MASK enables;
-// the other rows keep their own key
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ unsigned long long bcast_key(unsigned long long x) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)x, (int)(uint32_t)x, CTRL, ROW_MASK, 0xf,
-                                                             false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(x >> 32), (int)(uint32_t)(x >> 32), CTRL,
-                                                             ROW_MASK, 0xf, false);
-    return ((unsigned long long)hi << 32) | lo;
+__device__ __forceinline__ uint32_t bcast_key(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, ROW_MASK, 0xf, false);
 }
 // wavefront-wide maximum key, the same in every lane: quad permutations and
 // row rotations give every lane its 16-lane row's maximum; row broadcasts
 // (lane 15 into row 1 and row 3, then lane 31 into rows 2 and 3) leave the
 // wavefront's maximum in lane 63, which is read out. All VALU (DPP) steps.
-__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long x) {
-    x = kmax(x, dpp_key<0xB1>(x));   // quad_perm [1,0,3,2]
-    x = kmax(x, dpp_key<0x4E>(x));   // quad_perm [2,3,0,1]
-    x = kmax(x, dpp_key<0x124>(x));  // row_ror:4
-    x = kmax(x, dpp_key<0x128>(x));  // row_ror:8
-    x = kmax(x, bcast_key<0x142, 0xa>(x));  // row_bcast:15 into rows 1, 3
-    x = kmax(x, bcast_key<0x143, 0xc>(x));  // row_bcast:31 into rows 2, 3
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
-    return ((unsigned long long)hi << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t x) {
+    x = max(x, dpp_key<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = max(x, dpp_key<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = max(x, dpp_key<0x124>(x));  // row_ror:4
+    x = max(x, dpp_key<0x128>(x));  // row_ror:8
+    x = max(x, bcast_key<0x142, 0xa>(x));  // row_bcast:15 into rows 1, 3
+    x = max(x, bcast_key<0x143, 0xc>(x));  // row_bcast:31 into rows 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 template <int NPER>
@@ -78,7 +67,7 @@ __global__ __launch_bounds__(kWaves * 64) void topk_kernel(const float *part, in
     float *row = logits + (long long)t * E;
 
     float raw[NPER];              // logit as stored
-    unsigned long long key[NPER];  // ranking key (0 once taken)
+    uint32_t key[NPER];           // ranking key (0 once taken or past E)
     // fixed-order sum (ascending split) of the split-K partials: the loads of
     // up to 4 of the lane's experts x 16 splits, and their biases, are issued
     // together so that their latencies overlap
@@ -116,23 +105,31 @@ __global__ __launch_bounds__(kWaves * 64) void topk_kernel(const float *part, in
                 row[e] = xe;
             }
             raw[i0 + i] = xe;
-            key[i0 + i] = e < E ? rank_key((xe != xe) ? -INFINITY : xe, e) : 0ull;
+            key[i0 + i] = e < E ? rank_key((xe != xe) ? -INFINITY : xe) : 0u;
         }
     }
 
     float sel_val = 0.0f;  // lane j < k keeps the j-th pick
     int sel_idx = 0;
     for (int j = 0; j < k; ++j) {
-        unsigned long long best = 0;
+        uint32_t best = 0;
 #pragma unroll
-        for (int i = 0; i < NPER; ++i) best = kmax(best, key[i]);
+        for (int i = 0; i < NPER; ++i) best = max(best, key[i]);
         best = wave_max_key(best);
-        // every lane now holds the same best key; its owner marks it taken
-        const int bi = __builtin_amdgcn_readfirstlane((int)~(uint32_t)best);
+        // the lowest expert index holding the best key: expert e = lane + 64 i,
+        // so the first group i with a match, then its lowest matching lane
+        int bi = 0;
+#pragma unroll
+        for (int i = NPER - 1; i >= 0; --i) {
+            const unsigned long long m = __ballot(key[i] == best);
+            if (m) bi = 64 * i + __builtin_ctzll(m);
+        }
+        bi = __builtin_amdgcn_readfirstlane(bi);
+        // its owner marks it taken
         float r = raw[0];
 #pragma unroll
         for (int i = 0; i < NPER; ++i) {
-            if (lane + 64 * i == bi) key[i] = 0ull;
+            if (lane + 64 * i == bi) key[i] = 0u;
             if (i == (bi >> 6)) r = raw[i];
         }
         const float braw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), bi & 63));
