@@ -208,3 +208,24 @@ def test_shared_expert_dtype_validation():
     assert ws(ctypes.byref(_desc(Fs=512, ws_dt=BF16, path=3, **fp8)), 4096) > 0
     assert ws(ctypes.byref(_desc(Fs=512, ws_dt=FP8, Ss1=0x1000, Ss3=0x1000, Ss2=0x1000, path=3, **fp8)), 4096) == 0
     assert ws(ctypes.byref(_desc(Fs=1024, ws_dt=FP8, Ss1=0x1000, Ss3=0x1000, Ss2=0x1000, path=3, **fp8)), 4096) > 0
+
+
+def test_c_consumer_builds_and_passes(tmp_path):
+    """include/moe.h compiles as C11 and a C program linked against libmoe.so
+    sees the same validation answers (host-only paths, no GPU)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    hip_inc = "/opt/rocm/include"
+    if gcc is None or not os.path.isdir(hip_inc):
+        pytest.skip("gcc or the HIP headers are not available")
+    pkg = os.path.dirname(_lib.LIB_PATH)
+    exe = tmp_path / "c_abi_check"
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include",
+           f"-I{hip_inc}", os.path.join(ROOT, "tests", "c_abi_check.c"), "-o", str(exe), f"-L{pkg}", "-lmoe",
+           f"-Wl,-rpath,{pkg}"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stderr
+    assert "all checks passed" in run.stdout
