@@ -15,9 +15,9 @@
 //  2. scan (one block): per expert, an exclusive sum over chunks, then an
 //     exclusive scan over experts gives offsets; chunk bases are offset by it.
 //  3. scatter: row = chunk base + rank; row_src[row] = a, assign_row[a] = row.
-// When all assignments fit one chunk, the three steps run in one block, and
-// that block also writes the grouped GEMMs' tile list (the work of
-// build_tiles_kernel) from the offsets it has just formed, saving a launch.
+// When all assignments fit one chunk, the three steps run in one block. The
+// block that forms the offsets (that one, or the scan block) also writes the
+// grouped GEMMs' tile list (the work of build_tiles_kernel), saving a launch.
 #include "common.h"
 
 namespace moe {
@@ -29,6 +29,32 @@ __device__ __forceinline__ int ceil_log2(int E) {
     int b = 0;
     while ((1 << b) < E) ++b;
     return b;
+}
+
+// Tile list of the grouped GEMMs (the records of build_tiles_kernel), written
+// by a block that has just formed the offsets: thread g < E holds group g's
+// rows [lo, hi), thread E the extra group's (when tr.extra_rows > 0); the host
+// guarantees E + 1 <= 1024 groups. Called by the whole block.
+__device__ __forceinline__ void emit_tiles(const TileRequest &tr, int E, int lo, int hi, int *scan_lds) {
+    const int tid = threadIdx.x;
+    const int NG = E + (tr.extra_rows > 0 ? 1 : 0);
+    const int n = tid < NG ? (hi - lo + tr.bm - 1) / tr.bm : 0;
+    int nt = 0;
+    const int first = block_exclusive_scan(n, scan_lds, &nt);
+    if (tid < NG) {
+        if (tr.group_tile_start) tr.group_tile_start[tid] = first;
+        for (int i = 0; i < n; ++i) {
+            int32_t *t = tr.tiles + 4 * (first + i);
+            t[0] = tid;
+            t[1] = lo + i * tr.bm;
+            t[2] = min(lo + (i + 1) * tr.bm, hi);
+            t[3] = 0;
+        }
+    }
+    if (tid == 0) {
+        *tr.n_tiles = nt;
+        if (tr.group_tile_start) tr.group_tile_start[NG] = nt;
+    }
 }
 
 template <bool SINGLE>
@@ -92,32 +118,9 @@ __global__ __launch_bounds__(kChunk) void permute_rank_kernel(
             assign_row[a] = row;
         }
         if (tr.tiles) {
-            // tile list: group g's rows [lo, hi) in tiles of bm rows, groups
-            // in order (the extra group's rows follow the routed ones); the
-            // host guarantees E + 1 <= 1024 groups
-            const int NG = E + (tr.extra_rows > 0 ? 1 : 0);
-            int lo = 0, hi = 0, n = 0;
-            if (tid < NG) {
-                lo = tid < E ? off : all;
-                hi = tid < E ? off + total : all + tr.extra_rows;
-                n = (hi - lo + tr.bm - 1) / tr.bm;
-            }
-            int nt = 0;
-            const int first = block_exclusive_scan(n, scan_lds, &nt);
-            if (tid < NG) {
-                if (tr.group_tile_start) tr.group_tile_start[tid] = first;
-                for (int i = 0; i < n; ++i) {
-                    int32_t *t = tr.tiles + 4 * (first + i);
-                    t[0] = tid;
-                    t[1] = lo + i * tr.bm;
-                    t[2] = min(lo + (i + 1) * tr.bm, hi);
-                    t[3] = 0;
-                }
-            }
-            if (tid == 0) {
-                *tr.n_tiles = nt;
-                if (tr.group_tile_start) tr.group_tile_start[NG] = nt;
-            }
+            // the extra group's rows follow the routed ones
+            const bool real = tid < E;
+            emit_tiles(tr, E, real ? off : all, real ? off + total : all + tr.extra_rows, scan_lds);
         }
     }
 }
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(kChunk) void permute_rank_kernel(
 // scanned in LDS, and pass 2 rewrites the run's counts as exclusive prefixes.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t *chunk_counts, int nchunks,
                                                             int E, int32_t *counts,
-                                                            int32_t *offsets) {
+                                                            int32_t *offsets, TileRequest tr) {
     __shared__ int run_sum[1024];
     __shared__ int expert_off[1024];
     __shared__ int scan_lds[16];
@@ -181,6 +184,12 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t *chunk_count
         }
     }
     if (tid == 0) offsets[E] = all;
+    // the grouped GEMMs' tile list (thread e < E is (group 0, expert e): its
+    // off and total are the expert's offset and count)
+    if (tr.tiles) {
+        const bool real = tid < E;
+        emit_tiles(tr, E, real ? off : all, real ? off + total : all + tr.extra_rows, scan_lds);
+    }
 }
 
 __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t *idx, int A, int E,
@@ -209,6 +218,12 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *X, int ro
 
 }  // namespace
 
+// a block of 1024 threads can write the tile list of E (+1) groups
+static bool tile_request_fits(const TileRequest *tr, int E) {
+    return tr && tr->tiles && tr->n_tiles && tr->bm > 0 && tr->extra_rows >= 0 &&
+           E + (tr->extra_rows > 0 ? 1 : 0) <= kChunk;
+}
+
 size_t permute_ws_bytes(int A, int E) {
     const long long nchunks = (A + kChunk - 1) / kChunk;
     if (nchunks <= 1) return 0;
@@ -224,8 +239,7 @@ hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int
     const size_t lds = (size_t)16 * E * sizeof(unsigned short);
     if (nchunks <= 1) {
         TileRequest t{};
-        if (tr && tr->tiles && tr->n_tiles && tr->bm > 0 && tr->extra_rows >= 0 &&
-            E + (tr->extra_rows > 0 ? 1 : 0) <= kChunk) {
+        if (tile_request_fits(tr, E)) {
             t = *tr;
             if (tiles_built) *tiles_built = true;
         }
@@ -239,8 +253,13 @@ hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int
                        chunk_counts, rank, nullptr, nullptr, nullptr, nullptr, TileRequest{});
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    TileRequest t{};
+    if (tile_request_fits(tr, E)) {
+        t = *tr;
+        if (tiles_built) *tiles_built = true;
+    }
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, E,
-                       counts, offsets);
+                       counts, offsets, t);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(permute_scatter_kernel, dim3((A + 255) / 256), dim3(256), 0, s, idx, A, E,
