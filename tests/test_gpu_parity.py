@@ -354,6 +354,11 @@ LIMIT_CASES = {
     "E1024": LayerConfig("limit_E1024", T=40, H=128, F=64, E=1024, k=2, seed=21),
     "E1024_shared": LayerConfig("limit_E1024_shared", T=40, H=128, F=64, E=1024, k=2, Fs=64, seed=22),
     "T65535": LayerConfig("limit_T65535", T=65535, H=64, F=64, E=8, k=2, seed=23),
+    # more than one 1024-assignment chunk: the scan block writes the tile list
+    # for 1024 groups, and leaves 1025 groups to the separate tile kernel
+    "E1024_chunks": LayerConfig("limit_E1024_chunks", T=600, H=128, F=64, E=1024, k=2, seed=24),
+    "E1024_chunks_shared": LayerConfig("limit_E1024_chunks_shared", T=600, H=128, F=64, E=1024, k=2, Fs=64,
+                                       seed=25),
 }
 
 
