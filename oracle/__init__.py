@@ -14,7 +14,7 @@ activation and output projection, unpermute) and 九 (kept weights are
 renormalised); the page "MoE serving production quirks" (tianpan.co), section
 on the memory paradox (the gate runs a linear projection and a softmax over all
 experts); the page "MoE-推理部署" (zzmblog.top), section on expert quantisation
-(per-expert FP8 scales).
+(per-expert FP8 scales; MXFP4 as a single-GPU weight format).
 
 Parity pins: see the functions' docstrings and tests/test_oracle_*.py. The
 whole-layer output at model scale has no printed values on the pages; it is
@@ -22,7 +22,8 @@ pinned by the worked example, closed forms, special cases and a brute-force
 per-token loop on small inputs.
 """
 from .ref import (
-    to_f64, e4m3_decode, e4m3_encode, quantize_rows_e4m3, dequant_rows, round_bf16, dequant_blocks, router_logits, softmax, select_topk,
+    to_f64, e4m3_decode, e4m3_encode, quantize_rows_e4m3, dequant_rows, round_bf16, dequant_blocks,
+    e2m1_decode, e8m0_decode, dequant_mxfp4, router_logits, softmax, select_topk,
     route, routing_weights, permute, silu, swiglu_ffn, grouped_ffn, combine,
     Layer, forward, forward_tokens,
 )

@@ -5,9 +5,9 @@ router scores -> softmax -> top-k -> renormalise -> group assignments by expert
 (counts, offsets, stable permutation, inverse map) -> per-expert SwiGLU FFN ->
 combine (unpermute, weight, sum) [+ shared expert].
 
-Inputs are the canonical stored values (f32 / bf16 numbers, or E4M3 codes with
-fp32 block scales); they are upcast exactly to float64 and every step runs in
-float64. Nothing here is blocked, fused or reordered beyond what each
+Inputs are the canonical stored values (f32 / bf16 numbers, E4M3 codes with
+fp32 block scales, or MXFP4 codes with E8M0 scales); they are upcast exactly to
+float64 and every step runs in float64. Nothing here is blocked, fused or reordered beyond what each
 definition states.
 """
 from __future__ import annotations
@@ -81,6 +81,53 @@ def dequant_blocks(codes, scales, block: int = 128) -> np.ndarray:
     R, C = q.shape
     q = q.reshape(R // block, block, C // block, block)
     return (q * s[:, None, :, None]).reshape(R, C)
+
+
+def _u8(x) -> np.ndarray:
+    if torch is not None and isinstance(x, torch.Tensor):
+        x = x.detach().to("cpu").numpy()
+    return np.asarray(x, dtype=np.uint8)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """OCP FP4 E2M1 code (low 4 bits) -> float64, from the format definition.
+
+    Bit layout s|ee|m, exponent bias 1. Exponent field 0 encodes the subnormals
+    m * 2^-1; every other code is (-1)^s * (1 + m/2) * 2^(e-1). No infinities
+    or NaN; largest magnitude 6. MXFP4 is one of the expert-weight formats the
+    page "MoE-推理部署" names for single-GPU serving.
+    """
+    c = _u8(codes) & 0xF
+    s = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2(e.astype(np.float64) - 1.0))
+    return s * mag
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """OCP E8M0 scale code -> float64: 2^(e - 127), code 255 is NaN."""
+    e = _u8(codes).astype(np.float64)
+    return np.where(e == 255.0, np.nan, np.exp2(e - 127.0))
+
+
+def dequant_mxfp4(packed, scales, block: int = 32) -> np.ndarray:
+    """MXFP4 weights [K, N] in float64 from packed codes [K/2, N] and E8M0
+    scales [K/block, N].
+
+    Byte (i, n) holds column n's rows 2i (low nibble) and 2i + 1 (high nibble),
+    so the two values of a byte share one scale; every `block` consecutive K
+    rows of a column share one scale (the microscaling block runs along the
+    reduction dimension). An E2M1 value times a power of two is exact in
+    float64, so this is the exact stored weight.
+    """
+    b = _u8(packed)
+    K2, N = b.shape
+    q = np.empty((2 * K2, N), dtype=np.float64)
+    q[0::2] = e2m1_decode(b & 0xF)
+    q[1::2] = e2m1_decode(b >> 4)
+    sc = e8m0_decode(scales)
+    return q * np.repeat(sc, block, axis=0)[: 2 * K2]
 
 
 def e4m3_encode(x) -> np.ndarray:
@@ -337,7 +384,11 @@ class Layer:
         W = self.d[wkey] if e is None else self.d[wkey][e]
         S = self.d.get(skey)
         if S is not None:
-            return dequant_blocks(W, S if e is None else S[e])
+            S = S if e is None else S[e]
+            # E8M0 byte scales mark MXFP4 codes, fp32 scales E4M3 codes
+            if getattr(S, "dtype", None) in (np.uint8,) or (torch is not None and getattr(S, "dtype", None) == torch.uint8):
+                return dequant_mxfp4(W, S)
+            return dequant_blocks(W, S)
         return to_f64(W)
 
     def expert(self, e: int):

@@ -65,6 +65,43 @@ def quantize_e4m3_blocks(w: torch.Tensor):
     return codes.contiguous(), scale.contiguous()
 
 
+# magnitudes of the OCP FP4 E2M1 codes 0..7 (a code's sign is bit 3)
+_E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+_MX_BLOCK = 32
+
+
+def quantize_mxfp4(w: torch.Tensor):
+    """Store a float32 matrix [K, N] as MXFP4: E2M1 codes with one E8M0 scale
+    per 32 consecutive K rows of a column.
+
+    Per block: shared exponent floor(log2(amax)) - 2 (2 is E2M1's largest
+    exponent), clamped to the E8M0 range; each value divided by the scale goes
+    to the nearest E2M1 magnitude, ties to the even code, saturating at 6 (a
+    zero block gets the scale 1). Returns (packed uint8 [K/2, N], byte (i, n)
+    holding rows 2i (low nibble) and 2i + 1 (high nibble) of column n; scales
+    uint8 [K/32, N] as E8M0 codes).
+    """
+    K, N = w.shape
+    if K % _MX_BLOCK:
+        raise ValueError("MXFP4 needs K to be a multiple of 32")
+    w64 = w.to(torch.float64)
+    blk = w64.reshape(K // _MX_BLOCK, _MX_BLOCK, N)
+    amax = blk.abs().amax(dim=1)
+    e = torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2.0
+    e = torch.where(amax > 0, e, torch.zeros_like(e)).clamp(-127.0, 127.0)
+    scale_codes = (e + 127.0).to(torch.uint8)
+    x = blk / torch.exp2(e)[:, None, :]
+    mags = torch.tensor(_E2M1_MAG, dtype=torch.float64, device=w.device)
+    d = (x.abs()[..., None] - mags).abs()
+    # exact midpoints go to the even code (its mantissa bit clear)
+    d = d + (torch.arange(8, device=w.device) % 2).to(torch.float64) * 1e-12
+    code = d.argmin(dim=-1).to(torch.uint8)
+    code = code | torch.where(x < 0, 8, 0).to(torch.uint8)
+    code = code.reshape(K, N)
+    packed = (code[0::2] | (code[1::2] << 4)).contiguous()
+    return packed, scale_codes.contiguous()
+
+
 def _store(w32: torch.Tensor, wdt: str):
     """Cast a float32 weight matrix to its storage format."""
     if wdt == "fp8":
