@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s at 1 GPU + % HBM peak (decode) / % MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
-DECODE_WORKLOADS = {"toy_fp32", "mixtral_decode", "qwen3_decode", "dsv3_decode", "dsv3_decode_bf16_shared"}
+DECODE_WORKLOADS = {"toy_fp32", "mixtral_decode", "qwen3_decode", "dsv3_decode", "dsv3_decode_bf16_shared",
+                    "mixtral_decode_mxfp4", "qwen3_decode_mxfp4"}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 # sources of the gate/up kernel each path launches (the traffic record is
 # void once any of them changes)
@@ -69,7 +70,19 @@ def measured_traffic(workload: str, kernel: str):
 
 
 def weight_bytes(cfg, dt=None) -> float:
-    return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0}[dt or cfg.w]
+    """Bytes per weight value, scales excluded (MXFP4: two values a byte)."""
+    return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0, "mxfp4": 0.5}[dt or cfg.w]
+
+
+def scale_bytes(cfg, K: int, N: int, dt=None) -> float:
+    """Scale bytes of one [K, N] weight matrix: fp32 per 128x128 block (fp8),
+    one E8M0 byte per 32 K rows of a column (MXFP4), none otherwise."""
+    dt = dt or cfg.w
+    if dt == "fp8":
+        return (K // 128) * (N // 128) * 4.0
+    if dt == "mxfp4":
+        return (K // 32) * N * 1.0
+    return 0.0
 
 
 def gate_bytes(cfg) -> float:
@@ -82,8 +95,7 @@ def shared_bytes(cfg) -> float:
     if cfg.Fs == 0:
         return 0.0
     b = 3 * cfg.H * cfg.Fs * weight_bytes(cfg, cfg.shared_w)
-    if cfg.shared_w == "fp8":
-        b += 3 * (cfg.H // 128) * (cfg.Fs // 128) * 4
+    b += 2 * scale_bytes(cfg, cfg.H, cfg.Fs, cfg.shared_w) + scale_bytes(cfg, cfg.Fs, cfg.H, cfg.shared_w)
     return b
 
 
@@ -366,15 +378,11 @@ def main() -> int:
     # algorithmic work of the dominant kernel (routed gate/up + SwiGLU), per launch
     wb = weight_bytes(cfg)
     ab = 4.0 if cfg.act == "f32" else 2.0
-    gate_up_w = touched * 2 * cfg.H * cfg.F * wb
-    if cfg.w == "fp8":
-        gate_up_w += touched * 2 * (cfg.H // 128) * (cfg.F // 128) * 4
+    gate_up_w = touched * 2 * (cfg.H * cfg.F * wb + scale_bytes(cfg, cfg.H, cfg.F))
     gate_up_rows = A
     if cfg.Fs > 0 and cfg.Fs == cfg.F and cfg.shared_w == cfg.w:
         # the always-on shared expert runs as one more group of the same launch
-        gate_up_w += 2 * cfg.H * cfg.Fs * wb
-        if cfg.w == "fp8":
-            gate_up_w += 2 * (cfg.H // 128) * (cfg.Fs // 128) * 4
+        gate_up_w += 2 * (cfg.H * cfg.Fs * wb + scale_bytes(cfg, cfg.H, cfg.Fs))
         gate_up_rows += cfg.T
     gate_up_bytes = gate_up_w + cfg.T * cfg.H * ab + gate_up_rows * cfg.F * ab
     gate_up_flops = 4.0 * gate_up_rows * cfg.H * cfg.F
@@ -400,9 +408,8 @@ def main() -> int:
     roof["algorithmic_flops"] = gate_up_flops
 
     # whole-layer view: touched expert weights (+ gate, shared expert) over the step time
-    layer_w = touched * 3 * cfg.H * cfg.F * wb + gate_bytes(cfg) + shared_bytes(cfg)
-    if cfg.w == "fp8":
-        layer_w += touched * 3 * (cfg.H // 128) * (cfg.F // 128) * 4
+    layer_w = touched * (3 * cfg.H * cfg.F * wb + 2 * scale_bytes(cfg, cfg.H, cfg.F) + scale_bytes(cfg, cfg.F, cfg.H))
+    layer_w += gate_bytes(cfg) + shared_bytes(cfg)
     layer_flops = 6.0 * A * cfg.H * cfg.F + 6.0 * cfg.T * cfg.H * cfg.Fs + 2.0 * cfg.T * cfg.H * cfg.E
 
     out = {
@@ -418,7 +425,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16",
                   "fp8": "fp8-e4m3 weights and activations (fp32 scales)" if a8
-                  else "fp8-e4m3 weights, bf16 activations"}[cfg.w],
+                  else "fp8-e4m3 weights, bf16 activations",
+                  "mxfp4": "mxfp4 weights (e2m1 + e8m0 scales), bf16 activations"}[cfg.w],
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
                    "Fs": cfg.Fs, "weights": cfg.w, "shared_weights": cfg.shared_w if cfg.Fs else None,

@@ -37,10 +37,19 @@
  *    equal scores go to the lower expert index. Rows of an expert block are in
  *    ascending assignment order a = t*k + j (so ascending token order).
  *  - dtype combinations (activation, expert weights): (F32, F32), (BF16,
- *    BF16), (BF16, FP8_E4M3). The gate matrix has the activation dtype.
+ *    BF16), (BF16, FP8_E4M3), (BF16, MXFP4). The gate matrix has the
+ *    activation dtype (or fp32, see moe_route).
  *    FP8 weights are OCP E4M3 codes with one fp32 scale per 128x128 block,
- *    so their dimensions must be multiples of 128. H and F must be multiples
- *    of 32 (BF16/F32); E <= 1024; 1 <= k <= min(E, 64).
+ *    so their dimensions must be multiples of 128.
+ *    MXFP4 weights (the page "MoE-推理部署", expert-quantisation section, names
+ *    MXFP4 beside FP8): a [K, N] matrix is stored as [K/2, N] bytes, byte
+ *    (i, n) holding rows 2i (low nibble) and 2i + 1 (high nibble) of column
+ *    n as E2M1 codes, with [K/32, N] E8M0 scale bytes (2^(e - 127)), one per
+ *    32 K rows of a column; the S* pointers then point to these bytes. So W1,
+ *    W3 are [E, H/2, F] and W2 [E, F/2, H] bytes, S1, S3 [E, H/32, F] and S2
+ *    [E, F/32, H]. MXFP4 runs on the row-streaming kernel only (TILED falls
+ *    back to it; TILED_A8 is refused).
+ *    H and F must be multiples of 32; E <= 1024; 1 <= k <= min(E, 64).
  *  - Thread safety: no mutable global state; concurrent calls on different
  *    streams with disjoint outputs and workspaces are safe.
  */
@@ -66,7 +75,9 @@ typedef enum {
 typedef enum {
     MOE_F32 = 0,
     MOE_BF16 = 1,
-    MOE_FP8_E4M3 = 2 /* OCP E4M3 ("e4m3fn"), 1 byte per value, weights only */
+    MOE_FP8_E4M3 = 2, /* OCP E4M3 ("e4m3fn"), 1 byte per value, weights only */
+    MOE_MXFP4 = 3     /* OCP MXFP4 weights only: E2M1 codes, two K-consecutive values
+                         a byte, one E8M0 scale per 32 K rows of a column (below) */
 } moe_dtype;
 
 /* Expert-FFN kernel choice. AUTO picks the row-streaming (batched GEMV) path

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 PATHS = {"auto": 0, "gemv": 1, "tiled": 2, "tiled_a8": 3}
 
 # Every function include/moe.h declares, with (restype, argtypes).
@@ -97,10 +97,19 @@ def act_dtype(t: torch.Tensor) -> int:
     raise TypeError(f"activation dtype must be float32 or bfloat16, got {t.dtype}")
 
 
-def weight_dtype(t: torch.Tensor) -> int:
+def weight_dtype(t: torch.Tensor, scales=None) -> int:
+    """uint8 codes with uint8 (E8M0) scales are MXFP4, with fp32 scales E4M3."""
+    if t.dtype == torch.uint8 and scales is not None and scales.dtype == torch.uint8:
+        return MOE_MXFP4
     if t.dtype == torch.uint8 or t.dtype == torch.float8_e4m3fn:
         return MOE_FP8_E4M3
     return act_dtype(t)
+
+
+def _expert_dims(W1: torch.Tensor, wdt: int):
+    """(experts, H, F) of W1: MXFP4 stores two K rows a byte ([E, H/2, F])."""
+    G, K, F = W1.shape
+    return G, (2 * K if wdt == MOE_MXFP4 else K), F
 
 
 def _dev(*ts):
@@ -166,10 +175,10 @@ def grouped_ffn(Xin, offsets, W1, W3, W2, S1=None, S3=None, S2=None, row_src=Non
     _dev(Xin, offsets, W1, W3, W2, S1, S3, S2, row_src)
     _i32(offsets)
     _i32(row_src)
-    G, H, F = W1.shape
+    adt, wdt = act_dtype(Xin), weight_dtype(W1, S1)
+    G, H, F = _expert_dims(W1, wdt)
     if M is None:
         M = row_src.numel() if row_src is not None else Xin.shape[0]
-    adt, wdt = act_dtype(Xin), weight_dtype(W1)
     Yp = torch.empty((M, H), dtype=Xin.dtype, device=Xin.device)
     p = PATHS[path]
     nbytes = lib().moe_grouped_ffn_workspace_bytes(M, G, H, F, adt, wdt, p)
@@ -220,11 +229,11 @@ class MoELayer:
                    "Ws1", "Ws3", "Ws2", "Ss1", "Ss3", "Ss2")}
         _dev(*[v for v in self.w.values() if v is not None])
         W1 = self.w["W1"]
-        E, H, F = W1.shape
+        E, H, F = _expert_dims(W1, weight_dtype(W1, self.w["S1"]))
         Fs = 0 if self.w["Ws1"] is None else self.w["Ws1"].shape[1]
         d = LayerDesc()
         d.H, d.F, d.E, d.k, d.Fs = H, F, E, k, Fs
-        d.w_dt = weight_dtype(W1)
+        d.w_dt = weight_dtype(W1, self.w["S1"])
         # activations are f32 with f32 experts, else bf16; the gate may be
         # fp32 beside bf16 activations (higher-precision router)
         d.act_dt = MOE_F32 if d.w_dt == MOE_F32 else MOE_BF16
@@ -233,7 +242,7 @@ class MoELayer:
             raise TypeError("the gate must have the activation dtype, or be float32 beside bfloat16")
         d.gate_f32 = int(gate_dt == MOE_F32 and d.act_dt == MOE_BF16)
         # the shared expert's own dtype (bf16 beside fp8 routed experts allowed)
-        d.ws_dt = weight_dtype(self.w["Ws1"]) if Fs > 0 else d.w_dt
+        d.ws_dt = weight_dtype(self.w["Ws1"], self.w["Ss1"]) if Fs > 0 else d.w_dt
         d.path = PATHS[path]
         for key in self.w:
             setattr(d, key, None if self.w[key] is None else self.w[key].data_ptr())

@@ -33,10 +33,16 @@ bool act_ok(moe_dtype a) { return a == MOE_F32 || a == MOE_BF16; }
 
 bool pair_ok(moe_dtype act, moe_dtype w) {
     return (act == MOE_F32 && w == MOE_F32) || (act == MOE_BF16 && w == MOE_BF16) ||
-           (act == MOE_BF16 && w == MOE_FP8_E4M3);
+           (act == MOE_BF16 && w == MOE_FP8_E4M3) || (act == MOE_BF16 && w == MOE_MXFP4);
 }
 
-WType wtype(moe_dtype w) { return w == MOE_F32 ? W_F32 : w == MOE_BF16 ? W_BF16 : W_FP8; }
+// weights stored as codes with scales (E4M3 + fp32 block scales, or MXFP4
+// E2M1 + E8M0 scales)
+bool scaled(moe_dtype w) { return w == MOE_FP8_E4M3 || w == MOE_MXFP4; }
+
+WType wtype(moe_dtype w) {
+    return w == MOE_F32 ? W_F32 : w == MOE_BF16 ? W_BF16 : w == MOE_MXFP4 ? W_MXFP4 : W_FP8;
+}
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -241,8 +247,14 @@ int chunk_for(int K, int nsplit, moe_dtype w_dt) {
     return (c + gran - 1) / gran * gran;
 }
 
-hipError_t run_gemm(const FfnPlan &p, const GemmProblem &g, WType wt, bool swiglu, bool out_bf16,
-                    hipStream_t s) {
+// MXFP4 expert strides: [K/2][N] packed code bytes and [K/32][N] scale bytes
+void mxfp4_strides(GemmProblem &g) {
+    g.b_stride = (long long)g.K / 2 * g.N;
+    g.s_stride = (long long)(g.K / 32) * g.N;
+}
+
+hipError_t run_gemm(const FfnPlan &p, GemmProblem g, WType wt, bool swiglu, bool out_bf16, hipStream_t s) {
+    if (wt == W_MXFP4) mxfp4_strides(g);
     if (p.a8) return out_bf16 ? launch_tiled_a8(g, swiglu, p.bm, s) : hipErrorInvalidValue;
     return p.tiled ? launch_tiled_gemm(g, wt, swiglu, out_bf16, p.bm, s)
                    : launch_stream_gemm(g, wt, swiglu, out_bf16, s);
@@ -253,6 +265,7 @@ hipError_t run_gemm(const FfnPlan &p, const GemmProblem &g, WType wt, bool swigl
 // fixed order and applies SwiGLU.
 hipError_t run_gate_up_rows(const FfnPlan &p, GemmProblem g, const FfnWs &w, int rows, int F, WType wt,
                             moe_dtype act_dt, hipStream_t s) {
+    if (wt == W_MXFP4) mxfp4_strides(g);
     if (p.ksplit1 <= 1) return launch_stream_gemm(g, wt, true, act_dt == MOE_BF16, s);
     void *h = g.C;
     g.C = w.part1;
@@ -449,8 +462,8 @@ moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M
     if (path == MOE_PATH_TILED_A8 && w_dt != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
     if (M == 0) return MOE_OK;
     if (!Xin || !offsets || !W1 || !W3 || !W2 || !Yp) return MOE_ERR_INVALID_ARG;
-    const bool fp8 = w_dt == MOE_FP8_E4M3;
-    if (fp8 != (S1 != nullptr) || fp8 != (S3 != nullptr) || fp8 != (S2 != nullptr))
+    const bool sc = scaled(w_dt);
+    if (sc != (S1 != nullptr) || sc != (S3 != nullptr) || sc != (S2 != nullptr))
         return MOE_ERR_INVALID_ARG;
     const FfnPlan p = plan_ffn(M, G, H, F, w_dt, path);
     if ((path == MOE_PATH_TILED || path == MOE_PATH_TILED_A8) && !p.tiled) return MOE_ERR_UNSUPPORTED;
@@ -527,8 +540,8 @@ moe_status check_desc(const moe_layer_desc *d) {
     if (d->E > 1024 || d->k > 64 || d->E % 4) return MOE_ERR_UNSUPPORTED;
     moe_status st = check_ffn_dims(d->H, d->F, d->w_dt);
     if (st != MOE_OK) return st;
-    // the shared expert: the routed experts' dtype, or bf16 beside fp8
-    if (d->Fs > 0 && d->ws_dt != d->w_dt && !(d->w_dt == MOE_FP8_E4M3 && d->ws_dt == MOE_BF16))
+    // the shared expert: the routed experts' dtype, or bf16 beside fp8 or MXFP4
+    if (d->Fs > 0 && d->ws_dt != d->w_dt && !(scaled(d->w_dt) && d->ws_dt == MOE_BF16))
         return MOE_ERR_UNSUPPORTED;
     if (d->Fs > 0 && (st = check_ffn_dims(d->H, d->Fs, d->ws_dt)) != MOE_OK) return st;
     if (!path_ok(d->path)) return MOE_ERR_INVALID_ARG;
@@ -538,11 +551,11 @@ moe_status check_desc(const moe_layer_desc *d) {
         (d->w_dt != MOE_FP8_E4M3 || (d->Fs > 0 && d->ws_dt == MOE_FP8_E4M3 && d->Fs != d->F)))
         return MOE_ERR_UNSUPPORTED;
     if (!d->Wg || !d->W1 || !d->W3 || !d->W2) return MOE_ERR_INVALID_ARG;
-    const bool fp8 = d->w_dt == MOE_FP8_E4M3;
-    if (fp8 != (d->S1 != nullptr) || fp8 != (d->S3 != nullptr) || fp8 != (d->S2 != nullptr))
+    const bool sc = scaled(d->w_dt);
+    if (sc != (d->S1 != nullptr) || sc != (d->S3 != nullptr) || sc != (d->S2 != nullptr))
         return MOE_ERR_INVALID_ARG;
     if (d->Fs > 0) {
-        const bool sfp8 = d->ws_dt == MOE_FP8_E4M3;
+        const bool sfp8 = scaled(d->ws_dt);
         if (!d->Ws1 || !d->Ws3 || !d->Ws2) return MOE_ERR_INVALID_ARG;
         if (sfp8 != (d->Ss1 != nullptr) || sfp8 != (d->Ss3 != nullptr) || sfp8 != (d->Ss2 != nullptr))
             return MOE_ERR_INVALID_ARG;

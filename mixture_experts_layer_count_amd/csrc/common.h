@@ -81,7 +81,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *lds, int *total)
 // Weight element type of a GEMM: matches moe_dtype for the B operand.
 // W_F32_XBF16: fp32 weights against bf16 token rows (the higher-precision
 // router gate; row-streaming kernel, fp32 output only).
-enum WType { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_F32_XBF16 = 3 };
+// W_MXFP4: E2M1 codes packed two K-consecutive values a byte ([K/2][N]) with
+// one E8M0 scale per 32 K rows of a column ([K/32][N] bytes; row-streaming
+// kernel only).
+enum WType { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_F32_XBF16 = 3, W_MXFP4 = 4 };
 
 // Row-streaming grouped GEMM (small rows per group).
 //   C[r, n] = sum_k A(r)[k] * B_g[k, n]   (PLAIN)      or

@@ -61,6 +61,16 @@ template <> struct WTraits<W_F32_XBF16> {
     typedef f32x4 raw;  // 4 columns
     typedef uint16_t act;
 };
+template <> struct WTraits<W_MXFP4> {
+    typedef uint8_t elem;
+    typedef uint32_t raw;  // 4 columns of one K-pair row (8 K rows per lane: 4 raws)
+    typedef uint16_t act;
+};
+// weight rows (raws) a lane loads per 32-deep step: 8 K rows, or 4 K-pair
+// rows for MXFP4
+template <int WT> constexpr int rows_of() { return WT == W_MXFP4 ? 4 : 8; }
+// K values per stored weight row
+template <int WT> constexpr int kpack_of() { return WT == W_MXFP4 ? 2 : 1; }
 
 // Pack element `c` (0..3) of 8 consecutive K rows (each row: 4 bf16 columns
 // in two dwords) into a K-contiguous bf16x8 MFMA operand.
@@ -88,12 +98,12 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t q) {
 // Cache. Measured: Mixtral-shaped decode layer 0.487 -> 0.439 ms, Qwen3-shaped
 // 0.211 -> 0.191 ms, DeepSeek-shaped 1.81 -> 1.74 ms.
 template <int WT>
-__device__ __forceinline__ void load_rows(typename WTraits<WT>::raw (&r)[8],
+__device__ __forceinline__ void load_rows(typename WTraits<WT>::raw (&r)[rows_of<WT>()],
                                           const typename WTraits<WT>::elem *B, long long ldb,
                                           bool ok) {
     typedef typename WTraits<WT>::raw R;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < rows_of<WT>(); ++i) {
         if (ok) r[i] = __builtin_nontemporal_load(reinterpret_cast<const R *>(B + i * ldb));
         else r[i] = R{};
     }
@@ -102,8 +112,9 @@ __device__ __forceinline__ void load_rows(typename WTraits<WT>::raw (&r)[8],
 // One K step (32 deep) of acc[c] += A * B[:, c] for the wave's column tiles
 // (fp8: times the step's 128x128 block scale s).
 template <int WT>
-__device__ __forceinline__ void mma_step(f32x4 (&acc)[vec_of<WT>()], const typename WTraits<WT>::raw (&r)[8],
-                                         const void *afrag, float s);
+__device__ __forceinline__ void mma_step(f32x4 (&acc)[vec_of<WT>()],
+                                         const typename WTraits<WT>::raw (&r)[rows_of<WT>()], const void *afrag,
+                                         float s);
 
 template <>
 __device__ __forceinline__ void mma_step<W_BF16>(f32x4 (&acc)[4], const u32x2 (&r)[8], const void *afrag,
@@ -164,12 +175,40 @@ __device__ __forceinline__ void mma_step<W_F32_XBF16>(f32x4 (&acc)[4], const f32
     }
 }
 
+// MXFP4: byte c of K-pair row j holds rows 2j, 2j + 1 of the lane's column c,
+// so gathering byte c of the 4 rows gives the column's 8 K values, and each
+// byte converts to two bf16 values times the column's E8M0 scale (the
+// conversion takes only the scale's exponent: exact). s carries the 4 scale
+// bytes of the lane's columns for this 32-deep block.
+template <>
+__device__ __forceinline__ void mma_step<W_MXFP4>(f32x4 (&acc)[4], const uint32_t (&r)[4], const void *afrag,
+                                                  float s) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(afrag);
+    const uint32_t sw = __float_as_uint(s);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        // bytes 0, 1 <- byte c of rows 0, 1; then bytes 2, 3 <- rows 2, 3
+        const uint32_t sel = (uint32_t)c | ((uint32_t)(4 + c) << 8) | (0x0cu << 16) | (0x0cu << 24);
+        const uint32_t t01 = __builtin_amdgcn_perm(r[1], r[0], sel);
+        const uint32_t t23 = __builtin_amdgcn_perm(r[3], r[2], sel);
+        const uint32_t d = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+        const float sc = __uint_as_float(((sw >> (8 * c)) & 0xffu) << 23);
+        u32x4 v;
+        v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0));
+        v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1));
+        v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2));
+        v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 3));
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, v), acc[c], 0, 0, 0);
+    }
+}
+
 // A fragment: 8 consecutive K values of the lane's row (bf16: 16 B, f32: 32 B).
 template <int WT> struct AFrag;
 template <> struct AFrag<W_BF16> { u32x4 v; };
 template <> struct AFrag<W_FP8> { u32x4 v; };
 template <> struct AFrag<W_F32> { f32x4 v[2]; };
 template <> struct AFrag<W_F32_XBF16> { u32x4 v; };
+template <> struct AFrag<W_MXFP4> { u32x4 v; };
 
 template <int WT>
 __device__ __forceinline__ void load_a(AFrag<WT> &f, const typename WTraits<WT>::act *p, bool ok) {
@@ -190,14 +229,17 @@ __device__ __forceinline__ void load_a(AFrag<WT> &f, const typename WTraits<WT>:
 // multiplied), chosen by measurement: 3 for bf16 gate/up (two wavefronts per
 // SIMD), 4 for the single-matrix bf16 down projection; fp8 steps are twice as
 // wide (8 columns a lane), best at 2 for gate/up and 3 for down.
-template <int WT, bool SWIGLU> constexpr int ring_depth() { return !SWIGLU ? (WT == W_FP8 ? 3 : 4) : (WT == W_FP8 ? 2 : 3); }
+// MXFP4 steps carry a quarter of bf16's weight bytes, so its ring is deeper.
+template <int WT, bool SWIGLU> constexpr int ring_depth() {
+    return WT == W_MXFP4 ? (SWIGLU ? 4 : 6) : !SWIGLU ? (WT == W_FP8 ? 3 : 4) : (WT == W_FP8 ? 2 : 3);
+}
 
 // One K step's operands for one lane: weight rows of both matrices, the token
 // fragment and (fp8) the block scales of the step's 128-deep K block.
 template <int WT, bool SWIGLU>
 struct Stage {
-    typename WTraits<WT>::raw w0[8];
-    typename WTraits<WT>::raw w1[SWIGLU ? 8 : 1];
+    typename WTraits<WT>::raw w0[rows_of<WT>()];
+    typename WTraits<WT>::raw w1[SWIGLU ? rows_of<WT>() : 1];
     AFrag<WT> a;
     float s0, s1;
 };
@@ -248,8 +290,10 @@ __device__ __forceinline__ void stream_gemm_body(const GemmProblem &p, int n_sli
 
     const long long ldb = p.N;
     const long long goff = extra ? 0 : (long long)g * p.b_stride;
-    const E *B0 = reinterpret_cast<const E *>(extra ? p.Bx0 : p.B0) + goff + col + (8 * kg + kbeg) * ldb;
-    const E *B1 = SWIGLU ? reinterpret_cast<const E *>(extra ? p.Bx1 : p.B1) + goff + col + (8 * kg + kbeg) * ldb
+    constexpr int KP = kpack_of<WT>();  // K values per stored weight row
+    const long long brow = (8 * kg + kbeg) / KP;
+    const E *B0 = reinterpret_cast<const E *>(extra ? p.Bx0 : p.B0) + goff + col + brow * ldb;
+    const E *B1 = SWIGLU ? reinterpret_cast<const E *>(extra ? p.Bx1 : p.B1) + goff + col + brow * ldb
                          : nullptr;
     const float *S0p = extra ? p.Sx0 : p.S0;
     const float *S1p = extra ? p.Sx1 : p.S1;
@@ -257,13 +301,21 @@ __device__ __forceinline__ void stream_gemm_body(const GemmProblem &p, int n_sli
     const int sstride = p.N >> 7;
 
     auto issue = [&](Stage<WT, SWIGLU> &st, int step) {
-        load_rows<WT>(st.w0, B0 + (long long)step * 32 * ldb, ldb, colok);
-        if constexpr (SWIGLU) load_rows<WT>(st.w1, B1 + (long long)step * 32 * ldb, ldb, colok);
+        load_rows<WT>(st.w0, B0 + (long long)step * (32 / KP) * ldb, ldb, colok);
+        if constexpr (SWIGLU) load_rows<WT>(st.w1, B1 + (long long)step * (32 / KP) * ldb, ldb, colok);
         load_a<WT>(st.a, Ap + step * 32, rok);
         if constexpr (WT == W_FP8) {
             const long long si = sbase + (long long)((kbeg + step * 32) >> 7) * sstride;
             st.s0 = colok ? S0p[si] : 0.0f;
             st.s1 = (SWIGLU && colok) ? S1p[si] : 0.0f;
+        }
+        if constexpr (WT == W_MXFP4) {
+            // the E8M0 bytes of the lane's 4 columns for this 32-deep block
+            const long long si = (extra ? 0 : (long long)g * p.s_stride) + (long long)((kbeg + step * 32) >> 5) * p.N + col;
+            const uint8_t *S0b = reinterpret_cast<const uint8_t *>(S0p);
+            const uint8_t *S1b = reinterpret_cast<const uint8_t *>(S1p);
+            st.s0 = colok ? __uint_as_float(*reinterpret_cast<const uint32_t *>(S0b + si)) : 0.0f;
+            st.s1 = (SWIGLU && colok) ? __uint_as_float(*reinterpret_cast<const uint32_t *>(S1b + si)) : 0.0f;
         }
     };
 
@@ -394,6 +446,10 @@ hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool 
     case W_F32_XBF16:
         if (swiglu || out_bf16) return hipErrorInvalidValue;
         return launch_t<W_F32_XBF16, false, false>(p, s);
+    case W_MXFP4:
+        if (p.K % 32 || p.kchunk % 32 || p.N % 4) return hipErrorInvalidValue;
+        if (swiglu) return out_bf16 ? launch_t<W_MXFP4, true, true>(p, s) : launch_t<W_MXFP4, true, false>(p, s);
+        return out_bf16 ? launch_t<W_MXFP4, false, true>(p, s) : launch_t<W_MXFP4, false, false>(p, s);
     }
     return hipErrorInvalidValue;
 }

@@ -23,7 +23,7 @@ class LayerConfig:
     k: int
     Fs: int = 0            # shared-expert width; 0 = no shared expert
     act: str = "bf16"      # activation / gate dtype: "f32" or "bf16"
-    w: str = "bf16"        # expert weight dtype: "f32", "bf16" or "fp8"
+    w: str = "bf16"        # expert weight dtype: "f32", "bf16", "fp8" or "mxfp4"
     ws: str = ""           # shared-expert weight dtype ("" = w; "bf16" beside fp8)
     wg: str = ""           # gate dtype ("" = act; "f32" beside bf16: higher-precision router)
     zipf_s: float = 0.0    # > 0: gate bias b[e] = -s*ln(e+1) (hot low experts)
@@ -61,6 +61,9 @@ CONFIGS = {
                     ws="bf16"),
         # the router kept in fp32 beside bf16 tokens (same draws)
         LayerConfig("qwen3_prefill_f32_router", T=8192, H=2048, F=768, E=128, k=8, wg="f32"),
+        # MXFP4 experts (row-streaming kernel), decode batches
+        LayerConfig("mixtral_decode_mxfp4", T=16, H=4096, F=14336, E=8, k=2, w="mxfp4"),
+        LayerConfig("qwen3_decode_mxfp4", T=32, H=2048, F=768, E=128, k=8, w="mxfp4"),
     ]
 }
 
@@ -91,6 +94,10 @@ MINI_CONFIGS = {
         LayerConfig("mini_bf16_f32gate_decode", T=13, H=544, F=672, E=8, k=2, wg="f32", seed=11),
         LayerConfig("mini_fp8_f32gate_prefill", T=600, H=512, F=384, E=16, k=4, Fs=384, w="fp8", wg="f32",
                     seed=12),
+        # MXFP4 experts: ragged K splits and N tails (F = 352 = 5.5 slices),
+        # and with an MXFP4 shared expert in the routed launch
+        LayerConfig("mini_mxfp4_decode", T=13, H=544, F=352, E=8, k=2, w="mxfp4", seed=13),
+        LayerConfig("mini_mxfp4_shared", T=40, H=384, F=256, E=16, k=4, Fs=256, w="mxfp4", seed=14),
     ]
 }
 

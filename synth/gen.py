@@ -106,14 +106,20 @@ def _store(w32: torch.Tensor, wdt: str):
     """Cast a float32 weight matrix to its storage format."""
     if wdt == "fp8":
         return quantize_e4m3_blocks(w32)
+    if wdt == "mxfp4":
+        return quantize_mxfp4(w32)
     return w32.to(_DTYPES[wdt]).contiguous(), None
 
 
 def _expert_stack(cfg: LayerConfig, name: str, n: int, rows: int, cols: int, device):
-    """[n, rows, cols] expert weights (+ [n, rows/128, cols/128] scales for fp8)."""
+    """[n, rows, cols] expert weights (+ [n, rows/128, cols/128] scales for fp8;
+    MXFP4: [n, rows/2, cols] packed codes and [n, rows/32, cols] E8M0 scales)."""
     if cfg.w == "fp8":
         W = torch.empty((n, rows, cols), dtype=torch.uint8, device=device)
         S = torch.empty((n, rows // _BLOCK, cols // _BLOCK), dtype=torch.float32, device=device)
+    elif cfg.w == "mxfp4":
+        W = torch.empty((n, rows // 2, cols), dtype=torch.uint8, device=device)
+        S = torch.empty((n, rows // _MX_BLOCK, cols), dtype=torch.uint8, device=device)
     else:
         W = torch.empty((n, rows, cols), dtype=_DTYPES[cfg.w], device=device)
         S = None

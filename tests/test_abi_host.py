@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
 OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 
 
@@ -97,6 +97,12 @@ def test_grouped_ffn_validation():
     assert _ffn(lib, w_dt=FP8, S1=FAKE, S3=FAKE, S2=FAKE, F=480) == UNSUPPORTED  # fp8: F % 128
     assert _ffn(lib, ws_bytes=16) == WS_SMALL
     assert _ffn(lib, path=7) == INVALID
+    # MXFP4 experts: byte scales required, row-streaming path only, bf16 tokens only
+    assert _ffn(lib, w_dt=MXFP4) == INVALID
+    assert _ffn(lib, w_dt=MXFP4, S1=FAKE, S3=FAKE, S2=FAKE, path=2) == UNSUPPORTED
+    assert _ffn(lib, w_dt=MXFP4, S1=FAKE, S3=FAKE, S2=FAKE, path=3) == UNSUPPORTED
+    assert _ffn(lib, w_dt=MXFP4, S1=FAKE, S3=FAKE, S2=FAKE, act_dt=F32) == UNSUPPORTED
+    assert lib.moe_grouped_ffn_workspace_bytes(4096, 8, 512, 384, BF16, MXFP4, 0) > 0
     assert _ffn(lib, M=0, Xin=None) == OK
 
 

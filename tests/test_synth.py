@@ -80,18 +80,25 @@ def test_layer_shapes_and_dtypes():
         d = make_layer(cfg)
         assert d["X"].shape == (cfg.T, cfg.H)
         assert d["Wg"].shape == (cfg.H, cfg.E)
-        assert d["W1"].shape == (cfg.E, cfg.H, cfg.F) and d["W2"].shape == (cfg.E, cfg.F, cfg.H)
+        if cfg.w != "mxfp4":
+            assert d["W1"].shape == (cfg.E, cfg.H, cfg.F) and d["W2"].shape == (cfg.E, cfg.F, cfg.H)
         if cfg.w == "fp8":
             assert d["W1"].dtype == torch.uint8
             assert d["S1"].shape == (cfg.E, cfg.H // 128, cfg.F // 128)
             assert d["S2"].shape == (cfg.E, cfg.F // 128, cfg.H // 128)
+        elif cfg.w == "mxfp4":
+            assert d["W1"].dtype == torch.uint8 and d["S1"].dtype == torch.uint8
+            assert d["W1"].shape == (cfg.E, cfg.H // 2, cfg.F) and d["W2"].shape == (cfg.E, cfg.F // 2, cfg.H)
+            assert d["S1"].shape == (cfg.E, cfg.H // 32, cfg.F) and d["S2"].shape == (cfg.E, cfg.F // 32, cfg.H)
         else:
             assert d["S1"] is None
         assert (d["Ws1"] is not None) == (cfg.Fs > 0)
         if cfg.Fs > 0:
-            assert d["Ws1"].shape == (cfg.H, cfg.Fs) and d["Ws2"].shape == (cfg.Fs, cfg.H)
-            assert (d["Ss1"] is not None) == (cfg.shared_w == "fp8")
-            assert d["Ws1"].dtype == (torch.uint8 if cfg.shared_w == "fp8" else torch.bfloat16)
+            packed = cfg.shared_w == "mxfp4"
+            assert d["Ws1"].shape == (cfg.H // (2 if packed else 1), cfg.Fs)
+            assert d["Ws2"].shape == (cfg.Fs // (2 if packed else 1), cfg.H)
+            assert (d["Ss1"] is not None) == (cfg.shared_w in ("fp8", "mxfp4"))
+            assert d["Ws1"].dtype == (torch.uint8 if cfg.shared_w in ("fp8", "mxfp4") else torch.bfloat16)
 
 
 def test_bf16_shared_expert_holds_the_same_draws():
