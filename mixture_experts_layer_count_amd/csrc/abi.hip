@@ -107,7 +107,7 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path, 
         // gate/up: split over H only when its slices alone leave most SIMDs
         // idle (few touched experts); its fp32 partials are summed and passed
         // through SwiGLU by one small pass
-        const int slice = w_dt == MOE_FP8_E4M3 ? 128 : 64;
+        const int slice = (w_dt == MOE_FP8_E4M3 || w_dt == MOE_MXFP4) ? 128 : 64;
         const long long waves1 = tiles_est * ((F + slice - 1) / slice);
         if (waves1 < 1024) {
             int ks1 = (int)((2048 + waves1 - 1) / (waves1 > 0 ? waves1 : 1));

@@ -37,7 +37,7 @@ constexpr int kWaves = 4;   // wavefronts per block (at most)
 constexpr int kBM = 16;     // rows per tile
 // weight columns per lane: 8 for fp8 (8-byte loads, the same bytes per load
 // instruction as bf16), else 4; a wavefront slice is 16 lanes wide
-template <int WT> constexpr int vec_of() { return WT == W_FP8 ? 8 : 4; }
+template <int WT> constexpr int vec_of() { return WT == W_FP8 || WT == W_MXFP4 ? 8 : 4; }
 template <int WT> constexpr int slice_of() { return 16 * vec_of<WT>(); }
 
 template <int WT> struct WTraits;
@@ -63,9 +63,13 @@ template <> struct WTraits<W_F32_XBF16> {
 };
 template <> struct WTraits<W_MXFP4> {
     typedef uint8_t elem;
-    typedef uint32_t raw;  // 4 columns of one K-pair row (8 K rows per lane: 4 raws)
+    typedef u32x2 raw;  // 8 columns of one K-pair row (8 K rows per lane: 4 raws)
     typedef uint16_t act;
 };
+// per-step scale operand of a lane: fp8's 128x128 block scale, or the E8M0
+// bytes of MXFP4's 8 columns for the step's 32-deep block
+template <int WT> struct ScaleOf { typedef float type; };
+template <> struct ScaleOf<W_MXFP4> { typedef u32x2 type; };
 // weight rows (raws) a lane loads per 32-deep step: 8 K rows, or 4 K-pair
 // rows for MXFP4
 template <int WT> constexpr int rows_of() { return WT == W_MXFP4 ? 4 : 8; }
@@ -114,7 +118,7 @@ __device__ __forceinline__ void load_rows(typename WTraits<WT>::raw (&r)[rows_of
 template <int WT>
 __device__ __forceinline__ void mma_step(f32x4 (&acc)[vec_of<WT>()],
                                          const typename WTraits<WT>::raw (&r)[rows_of<WT>()], const void *afrag,
-                                         float s);
+                                         typename ScaleOf<WT>::type s);
 
 template <>
 __device__ __forceinline__ void mma_step<W_BF16>(f32x4 (&acc)[4], const u32x2 (&r)[8], const void *afrag,
@@ -175,24 +179,28 @@ __device__ __forceinline__ void mma_step<W_F32_XBF16>(f32x4 (&acc)[4], const f32
     }
 }
 
-// MXFP4: byte c of K-pair row j holds rows 2j, 2j + 1 of the lane's column c,
-// so gathering byte c of the 4 rows gives the column's 8 K values, and each
+// MXFP4: byte c of K-pair row j holds K rows 2j, 2j + 1 of the lane's column
+// c, so gathering byte c of the 4 rows gives the column's 8 K values; each
 // byte converts to two bf16 values times the column's E8M0 scale (the
-// conversion takes only the scale's exponent: exact). s carries the 4 scale
-// bytes of the lane's columns for this 32-deep block.
+// conversion takes only the scale's exponent: exact). s holds the 8 scale
+// bytes of the lane's columns for this 32-deep block. Eight columns a lane
+// make each row segment of a wavefront 128 contiguous bytes: whole lines.
 template <>
-__device__ __forceinline__ void mma_step<W_MXFP4>(f32x4 (&acc)[4], const uint32_t (&r)[4], const void *afrag,
-                                                  float s) {
+__device__ __forceinline__ void mma_step<W_MXFP4>(f32x4 (&acc)[8], const u32x2 (&r)[4], const void *afrag,
+                                                  u32x2 s) {
     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(afrag);
-    const uint32_t sw = __float_as_uint(s);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        // bytes 0, 1 <- byte c of rows 0, 1; then bytes 2, 3 <- rows 2, 3
-        const uint32_t sel = (uint32_t)c | ((uint32_t)(4 + c) << 8) | (0x0cu << 16) | (0x0cu << 24);
-        const uint32_t t01 = __builtin_amdgcn_perm(r[1], r[0], sel);
-        const uint32_t t23 = __builtin_amdgcn_perm(r[3], r[2], sel);
+    for (int c = 0; c < 8; ++c) {
+        const int b = c & 3;
+        const uint32_t r0 = c < 4 ? r[0].x : r[0].y, r1 = c < 4 ? r[1].x : r[1].y;
+        const uint32_t r2 = c < 4 ? r[2].x : r[2].y, r3 = c < 4 ? r[3].x : r[3].y;
+        // bytes 0, 1 <- byte b of rows 0, 1; then bytes 2, 3 <- rows 2, 3
+        const uint32_t sel = (uint32_t)b | ((uint32_t)(4 + b) << 8) | (0x0cu << 16) | (0x0cu << 24);
+        const uint32_t t01 = __builtin_amdgcn_perm(r1, r0, sel);
+        const uint32_t t23 = __builtin_amdgcn_perm(r3, r2, sel);
         const uint32_t d = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-        const float sc = __uint_as_float(((sw >> (8 * c)) & 0xffu) << 23);
+        const uint32_t sw = c < 4 ? s.x : s.y;
+        const float sc = __uint_as_float(((sw >> (8 * b)) & 0xffu) << 23);
         u32x4 v;
         v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0));
         v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1));
@@ -229,7 +237,7 @@ __device__ __forceinline__ void load_a(AFrag<WT> &f, const typename WTraits<WT>:
 // multiplied), chosen by measurement: 3 for bf16 gate/up (two wavefronts per
 // SIMD), 4 for the single-matrix bf16 down projection; fp8 steps are twice as
 // wide (8 columns a lane), best at 2 for gate/up and 3 for down.
-// MXFP4 steps carry a quarter of bf16's weight bytes, so its ring is deeper.
+// MXFP4 steps carry half of fp8's weight bytes (8 columns, K in pairs): best at 4 and 6.
 template <int WT, bool SWIGLU> constexpr int ring_depth() {
     return WT == W_MXFP4 ? (SWIGLU ? 4 : 6) : !SWIGLU ? (WT == W_FP8 ? 3 : 4) : (WT == W_FP8 ? 2 : 3);
 }
@@ -241,7 +249,7 @@ struct Stage {
     typename WTraits<WT>::raw w0[rows_of<WT>()];
     typename WTraits<WT>::raw w1[SWIGLU ? rows_of<WT>() : 1];
     AFrag<WT> a;
-    float s0, s1;
+    typename ScaleOf<WT>::type s0, s1;
 };
 
 template <int WT, bool SWIGLU, bool OUT_BF16>
@@ -310,12 +318,12 @@ __device__ __forceinline__ void stream_gemm_body(const GemmProblem &p, int n_sli
             st.s1 = (SWIGLU && colok) ? S1p[si] : 0.0f;
         }
         if constexpr (WT == W_MXFP4) {
-            // the E8M0 bytes of the lane's 4 columns for this 32-deep block
+            // the E8M0 bytes of the lane's 8 columns for this 32-deep block
             const long long si = (extra ? 0 : (long long)g * p.s_stride) + (long long)((kbeg + step * 32) >> 5) * p.N + col;
             const uint8_t *S0b = reinterpret_cast<const uint8_t *>(S0p);
             const uint8_t *S1b = reinterpret_cast<const uint8_t *>(S1p);
-            st.s0 = colok ? __uint_as_float(*reinterpret_cast<const uint32_t *>(S0b + si)) : 0.0f;
-            st.s1 = (SWIGLU && colok) ? __uint_as_float(*reinterpret_cast<const uint32_t *>(S1b + si)) : 0.0f;
+            st.s0 = colok ? *reinterpret_cast<const u32x2 *>(S0b + si) : u32x2{};
+            st.s1 = (SWIGLU && colok) ? *reinterpret_cast<const u32x2 *>(S1b + si) : u32x2{};
         }
     };
 
@@ -447,7 +455,7 @@ hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool 
         if (swiglu || out_bf16) return hipErrorInvalidValue;
         return launch_t<W_F32_XBF16, false, false>(p, s);
     case W_MXFP4:
-        if (p.K % 32 || p.kchunk % 32 || p.N % 4) return hipErrorInvalidValue;
+        if (p.K % 32 || p.kchunk % 32 || p.N % 8) return hipErrorInvalidValue;
         if (swiglu) return out_bf16 ? launch_t<W_MXFP4, true, true>(p, s) : launch_t<W_MXFP4, true, false>(p, s);
         return out_bf16 ? launch_t<W_MXFP4, false, true>(p, s) : launch_t<W_MXFP4, false, false>(p, s);
     }
