@@ -180,34 +180,44 @@ __device__ __forceinline__ void mma_step<W_F32_XBF16>(f32x4 (&acc)[4], const f32
 }
 
 // MXFP4: byte c of K-pair row j holds K rows 2j, 2j + 1 of the lane's column
-// c, so gathering byte c of the 4 rows gives the column's 8 K values; each
-// byte converts to two bf16 values times the column's E8M0 scale (the
-// conversion takes only the scale's exponent: exact). s holds the 8 scale
-// bytes of the lane's columns for this 32-deep block. Eight columns a lane
-// make each row segment of a wavefront 128 contiguous bytes: whole lines.
+// c, so converting byte c of rows 0..3 (the conversion selects the byte) gives
+// the column's 8 consecutive K values as four bf16 pairs, each times the
+// column's E8M0 scale (the conversion takes only the scale's exponent: exact).
+// s holds the 8 scale bytes of the lane's columns for this 32-deep block.
+// Eight columns a lane make each row segment of a wavefront 128 contiguous
+// bytes: whole lines.
+template <int B>
+__device__ __forceinline__ bf16x8 mxfp4_column(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, float sc) {
+    u32x4 v;
+    v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r0, sc, B));
+    v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r1, sc, B));
+    v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r2, sc, B));
+    v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r3, sc, B));
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int C>
+__device__ __forceinline__ void mxfp4_mma(f32x4 (&acc)[8], const u32x2 (&r)[4], const bf16x8 &a, u32x2 s) {
+    constexpr int B = C & 3;
+    const uint32_t sw = C < 4 ? s.x : s.y;
+    const float sc = __uint_as_float(((sw >> (8 * B)) & 0xffu) << 23);
+    const bf16x8 b = C < 4 ? mxfp4_column<B>(r[0].x, r[1].x, r[2].x, r[3].x, sc)
+                           : mxfp4_column<B>(r[0].y, r[1].y, r[2].y, r[3].y, sc);
+    acc[C] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[C], 0, 0, 0);
+}
+
 template <>
 __device__ __forceinline__ void mma_step<W_MXFP4>(f32x4 (&acc)[8], const u32x2 (&r)[4], const void *afrag,
                                                   u32x2 s) {
     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(afrag);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const int b = c & 3;
-        const uint32_t r0 = c < 4 ? r[0].x : r[0].y, r1 = c < 4 ? r[1].x : r[1].y;
-        const uint32_t r2 = c < 4 ? r[2].x : r[2].y, r3 = c < 4 ? r[3].x : r[3].y;
-        // bytes 0, 1 <- byte b of rows 0, 1; then bytes 2, 3 <- rows 2, 3
-        const uint32_t sel = (uint32_t)b | ((uint32_t)(4 + b) << 8) | (0x0cu << 16) | (0x0cu << 24);
-        const uint32_t t01 = __builtin_amdgcn_perm(r1, r0, sel);
-        const uint32_t t23 = __builtin_amdgcn_perm(r3, r2, sel);
-        const uint32_t d = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-        const uint32_t sw = c < 4 ? s.x : s.y;
-        const float sc = __uint_as_float(((sw >> (8 * b)) & 0xffu) << 23);
-        u32x4 v;
-        v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0));
-        v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1));
-        v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2));
-        v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 3));
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, v), acc[c], 0, 0, 0);
-    }
+    mxfp4_mma<0>(acc, r, a, s);
+    mxfp4_mma<1>(acc, r, a, s);
+    mxfp4_mma<2>(acc, r, a, s);
+    mxfp4_mma<3>(acc, r, a, s);
+    mxfp4_mma<4>(acc, r, a, s);
+    mxfp4_mma<5>(acc, r, a, s);
+    mxfp4_mma<6>(acc, r, a, s);
+    mxfp4_mma<7>(acc, r, a, s);
 }
 
 // A fragment: 8 consecutive K values of the lane's row (bf16: 16 B, f32: 32 B).
