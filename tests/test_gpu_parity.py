@@ -173,6 +173,38 @@ def test_grouped_ffn(name, path):
         assert err_m <= MIRROR_TOL
 
 
+
+@pytest.mark.parametrize("name", ["mini_mxfp4_decode", "mini_mxfp4_shared"])
+def test_mxfp4_every_code(name):
+    """Every E2M1 code in both nibbles (uniform random bytes: +-0, subnormal
+    +-0.5, up to +-6) and E8M0 scales spread over 2^-9 .. 2^7, so a wrong
+    nibble order, sign or scale exponent in the kernel's decode shows."""
+    cfg = MINI_CONFIGS[name]
+    say(f"[mxfp4 codes] {name}")
+    d = screened_layer(cfg)
+    rng = np.random.default_rng(2024)
+    for key in ("W1", "W3", "W2", "Ws1", "Ws3", "Ws2"):
+        if d.get(key) is None:
+            continue
+        w = d[key]
+        d[key] = torch.as_tensor(rng.integers(0, 256, size=tuple(w.shape), dtype=np.uint8), device="cuda")
+        skey = "S" + key[1:]
+        sc = d[skey]
+        d[skey] = torch.as_tensor(rng.integers(118, 135, size=tuple(sc.shape), dtype=np.uint8), device="cuda")
+    codes = d["W1"].cpu().numpy()
+    assert len(np.unique(codes & 15)) == 16 and len(np.unique(codes >> 4)) == 16
+    L = oracle.Layer(d, cfg.k)
+    _, idx, _ = oracle.route(L.X(), L.Wg(), L.gate_bias(), cfg.k)
+    counts, offsets, row_src, _ = oracle.permute(idx, cfg.E)
+    ref = oracle.grouped_ffn(L.X()[row_src // cfg.k], offsets, L.expert)
+    Yp = moe.grouped_ffn(d["X"], _to_dev_i32(offsets), d["W1"], d["W3"], d["W2"], d["S1"], d["S3"], d["S2"],
+                         row_src=_to_dev_i32(row_src), k=cfg.k, path="gemv")
+    torch.cuda.synchronize()
+    err = rel_err(Yp, ref)
+    say(f"    grouped FFN max rel err {err:.3e} (tol {tol_for(cfg)})")
+    assert err <= tol_for(cfg)
+    _check_forward(cfg, d, moe.MoELayer(d, cfg.k))
+
 # Group sizes on both sides of every tile height (128, 160, 256 rows), with
 # empty groups; the rows are pre-permuted token rows drawn by the generator.
 EDGE_SIZES = {
