@@ -118,7 +118,7 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path, 
             p.kchunk1 = chunk1;
             p.ksplit1 = (H + chunk1 - 1) / chunk1;
         }
-        const long long waves = tiles_est * ((H + 63) / 64);
+        const long long waves = tiles_est * ((H + slice - 1) / slice);
         int ks = (int)((2048 + waves - 1) / (waves > 0 ? waves : 1));
         ks = ks < 1 ? 1 : ks > 8 ? 8 : ks;
         const int gran = w_dt == MOE_FP8_E4M3 ? 128 : 32;

@@ -285,9 +285,11 @@ def permute(idx, E: int):
 # ----------------------------------------------------------------------------
 
 def silu(z):
-    """silu(z) = z / (1 + exp(-z)) (float64)."""
+    """silu(z) = z / (1 + exp(-z)) (float64). For z below about -709 exp(-z)
+    overflows to inf and the quotient is -0, the function's limit."""
     z = np.asarray(z, dtype=np.float64)
-    return z / (1.0 + np.exp(-z))
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
 
 
 def swiglu_ffn(x, W1, W3, W2, act_quant: bool = False) -> np.ndarray:
