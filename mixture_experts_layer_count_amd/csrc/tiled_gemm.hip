@@ -12,7 +12,7 @@ int tiled_gemm_bm(WType wt, long long rows, int groups) {
 }
 
 bool tiled_gemm_supports(WType wt, int N, int K) {
-    if (wt == W_F32 || wt == W_MXFP4) return false;  // MXFP4: row-streaming kernel only
+    if (wt == W_F32 || wt == W_MXFP4) return false;  // MXFP4 reaches these kernels decoded to bf16
     if (N % 8 || K % tiled::kBK || N < 16 || K < tiled::kBK) return false;
     if (wt == W_FP8 && (N % 128 || K % 128)) return false;
     return true;

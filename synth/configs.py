@@ -64,6 +64,9 @@ CONFIGS = {
         # MXFP4 experts (row-streaming kernel), decode batches
         LayerConfig("mixtral_decode_mxfp4", T=16, H=4096, F=14336, E=8, k=2, w="mxfp4"),
         LayerConfig("qwen3_decode_mxfp4", T=32, H=2048, F=768, E=128, k=8, w="mxfp4"),
+        # MXFP4 experts at prefill sizes: decoded to bf16 for the tiled kernels
+        LayerConfig("mixtral_prefill_mxfp4", T=4096, H=4096, F=14336, E=8, k=2, zipf_s=1.1, w="mxfp4"),
+        LayerConfig("qwen3_prefill_mxfp4", T=8192, H=2048, F=768, E=128, k=8, w="mxfp4"),
     ]
 }
 
@@ -98,6 +101,9 @@ MINI_CONFIGS = {
         # and with an MXFP4 shared expert in the routed launch
         LayerConfig("mini_mxfp4_decode", T=13, H=544, F=352, E=8, k=2, w="mxfp4", seed=13),
         LayerConfig("mini_mxfp4_shared", T=40, H=384, F=256, E=16, k=4, Fs=256, w="mxfp4", seed=14),
+        # prefill-sized MXFP4 (tiled after decoding), with a wider MXFP4 shared
+        # expert in launches of its own
+        LayerConfig("mini_mxfp4_prefill", T=256, H=384, F=256, E=8, k=2, Fs=512, w="mxfp4", seed=15),
     ]
 }
 

@@ -97,12 +97,15 @@ def test_grouped_ffn_validation():
     assert _ffn(lib, w_dt=FP8, S1=FAKE, S3=FAKE, S2=FAKE, F=480) == UNSUPPORTED  # fp8: F % 128
     assert _ffn(lib, ws_bytes=16) == WS_SMALL
     assert _ffn(lib, path=7) == INVALID
-    # MXFP4 experts: byte scales required, row-streaming path only, bf16 tokens only
+    # MXFP4 experts: byte scales required, no W8A8 form, bf16 tokens only
     assert _ffn(lib, w_dt=MXFP4) == INVALID
-    assert _ffn(lib, w_dt=MXFP4, S1=FAKE, S3=FAKE, S2=FAKE, path=2) == UNSUPPORTED
     assert _ffn(lib, w_dt=MXFP4, S1=FAKE, S3=FAKE, S2=FAKE, path=3) == UNSUPPORTED
     assert _ffn(lib, w_dt=MXFP4, S1=FAKE, S3=FAKE, S2=FAKE, act_dt=F32) == UNSUPPORTED
-    assert lib.moe_grouped_ffn_workspace_bytes(4096, 8, 512, 384, BF16, MXFP4, 0) > 0
+    # the tiled form decodes every expert to bf16 in the workspace: 3 * G*H*F * 2 bytes more
+    m, g, h, f = 4096, 8, 512, 384
+    tiled = lib.moe_grouped_ffn_workspace_bytes(m, g, h, f, BF16, MXFP4, 2)
+    assert tiled >= lib.moe_grouped_ffn_workspace_bytes(m, g, h, f, BF16, BF16, 2) + 3 * g * h * f * 2
+    assert lib.moe_grouped_ffn_workspace_bytes(m, g, h, f, BF16, MXFP4, 0) == tiled  # AUTO picks tiled
     assert _ffn(lib, M=0, Xin=None) == OK
 
 

@@ -125,7 +125,7 @@ def test_permute(T, k, E, mode):
 # ----------------------------------------------------------------------------
 
 FFN_CASES = [(n, p) for n in MINI_CONFIGS for p in ("gemv", "tiled", "tiled_a8")
-             if not (p == "tiled" and MINI_CONFIGS[n].w in ("f32", "mxfp4"))
+             if not (p == "tiled" and MINI_CONFIGS[n].w == "f32")
              and not (p == "tiled_a8" and MINI_CONFIGS[n].w != "fp8")]
 # W8A8 against the oracle's mirror of the activation quantisation. The two
 # agree except where an h value lands on the other side of an E4M3 rounding
@@ -197,13 +197,15 @@ def test_mxfp4_every_code(name):
     _, idx, _ = oracle.route(L.X(), L.Wg(), L.gate_bias(), cfg.k)
     counts, offsets, row_src, _ = oracle.permute(idx, cfg.E)
     ref = oracle.grouped_ffn(L.X()[row_src // cfg.k], offsets, L.expert)
-    Yp = moe.grouped_ffn(d["X"], _to_dev_i32(offsets), d["W1"], d["W3"], d["W2"], d["S1"], d["S3"], d["S2"],
-                         row_src=_to_dev_i32(row_src), k=cfg.k, path="gemv")
-    torch.cuda.synchronize()
-    err = rel_err(Yp, ref)
-    say(f"    grouped FFN max rel err {err:.3e} (tol {tol_for(cfg)})")
-    assert err <= tol_for(cfg)
-    _check_forward(cfg, d, moe.MoELayer(d, cfg.k))
+    # row-streaming decode in registers, and the bf16 decode pass feeding the tiled kernels
+    for path in ("gemv", "tiled"):
+        Yp = moe.grouped_ffn(d["X"], _to_dev_i32(offsets), d["W1"], d["W3"], d["W2"], d["S1"], d["S3"], d["S2"],
+                             row_src=_to_dev_i32(row_src), k=cfg.k, path=path)
+        torch.cuda.synchronize()
+        err = rel_err(Yp, ref)
+        say(f"    grouped FFN ({path}) max rel err {err:.3e} (tol {tol_for(cfg)})")
+        assert err <= tol_for(cfg)
+        _check_forward(cfg, d, moe.MoELayer(d, cfg.k, path=path))
 
 # Group sizes on both sides of every tile height (128, 160, 256 rows), with
 # empty groups; the rows are pre-permuted token rows drawn by the generator.
@@ -363,7 +365,8 @@ def test_forward_empty_batch():
 FULL_SAMPLES = {"toy_fp32": None, "mixtral_decode": None, "qwen3_decode": None,
                 "mixtral_prefill": 6, "qwen3_prefill": 8, "dsv3_decode": 4, "dsv3_prefill": 4,
                 "dsv3_decode_bf16_shared": 4, "dsv3_prefill_bf16_shared": 4, "qwen3_prefill_f32_router": 8,
-                "mixtral_decode_mxfp4": None, "qwen3_decode_mxfp4": None}
+                "mixtral_decode_mxfp4": None, "qwen3_decode_mxfp4": None,
+                "mixtral_prefill_mxfp4": 6, "qwen3_prefill_mxfp4": 8}
 
 
 @pytest.mark.parametrize("name", list(CONFIGS))
