@@ -160,7 +160,7 @@ bool tiled_a8_supports(int N, int K);
 // and saturated. Output row r reads X[row_src[r] / gk] (X[r] if row_src is
 // NULL; row stride ldx elements) -> Q [R][C], S [R][C/128].
 // MXFP4 codes [G][K/2][N] with E8M0 scales [G][K/32][N] -> bf16 [G][K][N]
-// (K % 32 == 0, N % 4 == 0)
+// (K % 32 == 0, N % 8 == 0)
 hipError_t launch_mxfp4_to_bf16(const void *codes, const void *scales, int G, int K, int N, void *out,
                                 hipStream_t s);
 hipError_t launch_quant_rows(const void *X, long long ldx, const int32_t *row_src, int gk, int R, int C,
