@@ -47,8 +47,10 @@
  *    n as E2M1 codes, with [K/32, N] E8M0 scale bytes (2^(e - 127)), one per
  *    32 K rows of a column; the S* pointers then point to these bytes. So W1,
  *    W3 are [E, H/2, F] and W2 [E, F/2, H] bytes, S1, S3 [E, H/32, F] and S2
- *    [E, F/32, H]. MXFP4 runs on the row-streaming kernel only (TILED falls
- *    back to it; TILED_A8 is refused).
+ *    [E, F/32, H]. The row-streaming path decodes the codes in registers; the
+ *    tiled path (TILED, or AUTO at >= 15 rows per expert) first decodes every
+ *    expert to bf16 in the workspace (3*E*H*F*2 bytes more, counted by the
+ *    workspace-size calls). TILED_A8 is refused.
  *    H and F must be multiples of 32; E <= 1024; 1 <= k <= min(E, 64).
  *  - Thread safety: no mutable global state; concurrent calls on different
  *    streams with disjoint outputs and workspaces are safe.
