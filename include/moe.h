@@ -48,7 +48,7 @@
  *    32 K rows of a column; the S* pointers then point to these bytes. So W1,
  *    W3 are [E, H/2, F] and W2 [E, F/2, H] bytes, S1, S3 [E, H/32, F] and S2
  *    [E, F/32, H]. The row-streaming path decodes the codes in registers; the
- *    tiled path (TILED, or AUTO at >= 15 rows per expert) first decodes every
+ *    tiled path (TILED, or AUTO at >= 192 rows per expert) first decodes every
  *    expert to bf16 in the workspace (3*E*H*F*2 bytes more, counted by the
  *    workspace-size calls). TILED_A8 is refused.
  *    H and F must be multiples of 32; E <= 1024; 1 <= k <= min(E, 64).

@@ -94,8 +94,11 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path, 
         p.tiled = false;
     } else {
         // the tiled kernels win from about 12-25 rows per group (measured by
-        // token-count sweeps of the Mixtral-, Qwen3- and DeepSeek-shaped layers)
-        p.tiled = can_tile && (long long)M >= 15LL * G;
+        // token-count sweeps of the Mixtral-, Qwen3- and DeepSeek-shaped layers);
+        // MXFP4 from 128-256 (the row-streaming form reads a quarter of bf16's
+        // bytes, and the tiled form first decodes every expert to bf16)
+        const long long min_rows = w_dt == MOE_MXFP4 ? 192 : 15;
+        p.tiled = can_tile && (long long)M >= min_rows * G;
         p.a8 = p.tiled && can_a8;
     }
     p.deq = p.tiled && w_dt == MOE_MXFP4;
