@@ -422,12 +422,15 @@ def forward(layer: Layer) -> dict:
                 row_src=row_src, assign_row=assign_row, Xp=Xp, Yp=Yp, S=S, Y=Y)
 
 
-def forward_tokens(layer: Layer, tokens, idx=None, act_quant: bool = False) -> dict:
+def forward_tokens(layer: Layer, tokens, idx=None, act_quant: bool = False, workers: int = 1) -> dict:
     """fp64 outputs for a subset of tokens only (the layer is per-token
     independent: each token's output depends on its own row, its own routing
     and the shared weights). `idx` optionally fixes the routing decision
     (rows for the sampled tokens) instead of re-deriving it. `act_quant`
     mirrors activation quantisation in the expert FFNs (see swiglu_ffn).
+    `workers` > 1 evaluates the chosen experts on that many threads: each
+    expert fills its own (token, slot) entries of y with the same
+    expressions, so the result does not depend on it.
     Returns logits, idx, w, per-token expert outputs y[t, j] and Y for the
     sampled tokens, in the given order.
     """
@@ -440,10 +443,19 @@ def forward_tokens(layer: Layer, tokens, idx=None, act_quant: bool = False) -> d
     w = routing_weights(logits, idx)
     n = len(tokens)
     y = np.zeros((n, layer.k, layer.H), dtype=np.float64)
-    for e in np.unique(idx):
+
+    def one_expert(e):
         W1, W3, W2 = layer.expert(int(e))
         ts, js = np.nonzero(idx == e)
         y[ts, js] = swiglu_ffn(X[ts], W1, W3, W2, act_quant)
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one_expert, np.unique(idx)))
+    else:
+        for e in np.unique(idx):
+            one_expert(e)
     Y = np.einsum("tj,tjh->th", w, y)
     S = None
     if layer.has_shared():

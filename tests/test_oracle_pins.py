@@ -298,6 +298,9 @@ def test_oracle_matches_brute_force(seed, E, k, Fs, zipf):
     np.testing.assert_allclose(out["Y"], Y, rtol=1e-12, atol=1e-13)
     sub = oracle.forward_tokens(L, [5, 0, 3])
     np.testing.assert_allclose(sub["Y"], out["Y"][[5, 0, 3]], rtol=1e-13, atol=1e-14)
+    # experts evaluated on a thread pool: the same values, bit for bit
+    par = oracle.forward_tokens(L, [5, 0, 3], workers=4)
+    assert np.array_equal(par["Y"], sub["Y"]) and np.array_equal(par["y"], sub["y"])
 
 
 def test_shared_expert_special_cases():
