@@ -5,11 +5,15 @@ One step = one full MoE layer forward (router, dispatch, grouped SwiGLU expert
 FFN, combine) over one batch of T tokens, through libmoe's C ABI, with inputs
 and weights already resident in HBM. Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-all-configs]
 
-The dominant kernel (the routed gate/up grouped GEMM with fused SwiGLU, which
-streams two thirds of the touched expert weights) is timed with HIP events
-recorded by libmoe on its own stream around that kernel, in every timed step.
+The default workload is the largest configuration, the DeepSeek-V3-shaped
+prefill layer (4096 tokens, 256 fp8 experts + 1 shared). The dominant kernel
+(the routed gate/up grouped GEMM with fused SwiGLU, which streams two thirds of
+the touched expert weights) is timed with HIP events recorded by libmoe on its
+own stream around that kernel, in every timed step. Per-step latency (p50,
+p95) and per-stage times come from separate passes. After the headline, every
+other configuration is timed in the same run (key "configs").
 """
 from __future__ import annotations
 
@@ -107,7 +111,17 @@ def cpu_baseline(cfg, d, k: int) -> dict:
 
     n = cfg.T if cfg.T <= 64 and cfg.E <= 16 else (16 if cfg.E <= 16 else 4)
     tokens = np.arange(min(n, cfg.T))
-    host = {key: (v.cpu() if hasattr(v, "cpu") else v) for key, v in d.items()}
+    # host copies of the sample's inputs: its token rows, the gate, the shared
+    # expert, and only the experts the sample's tokens choose (the whole
+    # DeepSeek-shaped layer is 11 GB)
+    small = {key: (v.cpu() if hasattr(v, "cpu") else v) for key, v in d.items()
+             if key not in ("W1", "W3", "W2", "S1", "S3", "S2")}
+    _, idx, _ = oracle.route(oracle.to_f64(small["X"][: len(tokens)]), small["Wg"], small.get("gate_bias"), k)
+    chosen = sorted(set(int(e) for e in np.unique(idx)))
+    host = dict(small)
+    for key in ("W1", "W3", "W2", "S1", "S3", "S2"):
+        if d.get(key) is not None:
+            host[key] = _HostExperts(d[key], chosen)
     L = oracle.Layer(host, k)
     # repeat the sample until about 10 s of CPU work have been timed
     passes, t0 = 0, time.perf_counter()
@@ -119,9 +133,34 @@ def cpu_baseline(cfg, d, k: int) -> dict:
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     return {"value": passes * len(tokens) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(tokens)} of {cfg.T} tokens x {passes} passes, full fp64 layer forward (route over "
-                      f"all E, SwiGLU of each chosen expert, combine); {dt:.1f} s on "
-                      f"{platform.processor() or 'host'}"}
+                      f"all E, SwiGLU of each chosen expert, combine); {dt:.1f} s on {cpu_model()}"}
+
+
+class _HostExperts:
+    """Host copies of some experts of a stacked [E, ...] device tensor,
+    indexed by expert like the tensor itself."""
+
+    def __init__(self, t, experts):
+        self.shape = tuple(t.shape)
+        self.dtype = t.dtype
+        self._rows = {e: t[e].cpu() for e in experts}
+
+    def __getitem__(self, e):
+        return self._rows[int(e)]
+
+
+def cpu_model() -> str:
+    """The host processor's model name (from /proc/cpuinfo on Linux)."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "host"
 
 
 GATE_UP_KERNEL = re.compile(r"(stream|tiled)_gemm_kernel<[^,]+, true|tiled_a8_kernel<true")
@@ -294,14 +333,156 @@ def copy_calibration(nbytes: int = COPY_CALIBRATION_BYTES) -> None:
     print(json.dumps({"copy_calibration_bytes": nbytes}))
 
 
+# HBM-graded workloads: decode batches (weights streamed for few rows) and the
+# DeepSeek-shaped fp8 prefill, whose layer arithmetic intensity (about 287
+# flop per byte) lies below the fp8 ridge, so HBM bounds it
+HBM_GRADED = DECODE_WORKLOADS | {"dsv3_prefill", "dsv3_prefill_bf16_shared"}
+# every configuration of the layer, timed beside the headline in one run
+ALL_CONFIGS = ["toy_fp32", "mixtral_decode", "mixtral_prefill", "qwen3_decode", "qwen3_prefill",
+               "dsv3_decode", "dsv3_prefill"]
+EV_START, EV_SCHED, EV_GATE_UP, EV_COMBINE = 0, 3, 4, 8
+
+
+def percentile(xs, q: float) -> float:
+    """Linear-interpolated q-quantile (0 <= q <= 1) of a non-empty sample."""
+    s = sorted(xs)
+    pos = q * (len(s) - 1)
+    lo = int(pos)
+    hi = min(lo + 1, len(s) - 1)
+    return s[lo] + (s[hi] - s[lo]) * (pos - lo)
+
+
+def uses_a8(cfg, path: str) -> bool:
+    """The W8A8 tiled kernels run (fp8 weights at prefill sizes under AUTO)."""
+    if cfg.w != "fp8":
+        return False
+    return path == "tiled_a8" or (path == "auto" and cfg.T * cfg.k >= 15 * cfg.E)
+
+
+def gate_up_work(cfg, touched: int, a8: bool):
+    """Algorithmic bytes and flops of one routed gate/up launch (with the
+    shared expert when it is a group of the same launch)."""
+    wb = weight_bytes(cfg)
+    ab = 4.0 if cfg.act == "f32" else 2.0
+    xb = 1.0 if a8 else ab  # W8A8 reads E4M3 token rows and writes E4M3 h
+    w = touched * 2 * (cfg.H * cfg.F * wb + scale_bytes(cfg, cfg.H, cfg.F))
+    rows = cfg.T * cfg.k
+    if cfg.Fs > 0 and cfg.Fs == cfg.F and cfg.shared_w == cfg.w:
+        w += 2 * (cfg.H * cfg.Fs * wb + scale_bytes(cfg, cfg.H, cfg.Fs))
+        rows += cfg.T
+    act = cfg.T * cfg.H * xb + rows * cfg.F * xb
+    if a8:  # per-row 128-column fp32 scales of the token rows and of h
+        act += 4.0 * (cfg.T * cfg.H / 128 + rows * cfg.F / 128)
+    return w + act, 4.0 * rows * cfg.H * cfg.F
+
+
+def measure(cfg, path: str, steps: int, warmup: int, workload: str) -> dict:
+    """Time `steps` layer forwards (after `warmup`) of one workload, with the
+    gate/up kernel bracketed by HIP events in every timed step; then per-step
+    latency and per-stage times in separate passes."""
+    import torch
+    import mixture_experts_layer_count_amd as moe
+    from mixture_experts_layer_count_amd._lib import MOE_N_EVENTS
+    from synth import make_layer
+
+    d = make_layer(cfg, device="cuda")
+    layer = moe.MoELayer(d, cfg.k, path=path)
+    X = d["X"]
+    Y = torch.empty_like(X)
+    _, _, _, _, counts = layer.forward(X, Y, aux=True)
+    torch.cuda.synchronize()
+    touched = int((counts > 0).sum().item())
+
+    evs = [moe.StageEvents(want=[EV_SCHED, EV_GATE_UP]) for _ in range(steps)]
+    for _ in range(warmup):
+        layer.forward(X, Y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layer.forward(X, Y, events=evs[i].handles)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / steps
+    gate_up_ms = statistics.fmean(e.elapsed_ms(EV_SCHED, EV_GATE_UP) for e in evs)
+
+    # latency distribution: one marker pair around each whole forward
+    n_lat = max(20, steps)
+    lat_ev = [moe.StageEvents(want=[EV_START, EV_COMBINE]) for _ in range(n_lat)]
+    for e in lat_ev:
+        layer.forward(X, Y, events=e.handles)
+    torch.cuda.synchronize()
+    lat = [e.elapsed_ms(EV_START, EV_COMBINE) for e in lat_ev]
+    # per-stage times: every marker recorded (each costs a few microseconds)
+    stage_runs = []
+    for _ in range(max(10, min(steps, 20))):
+        ev = moe.StageEvents()
+        layer.forward(X, Y, events=ev.handles)
+        stage_runs.append([ev.elapsed_ms(i, i + 1) for i in range(MOE_N_EVENTS - 1)])
+    torch.cuda.synchronize()
+    stages = {name: {"p50": round(percentile([r[i] for r in stage_runs], 0.5), 4),
+                     "p95": round(percentile([r[i] for r in stage_runs], 0.95), 4)}
+              for i, name in enumerate(moe.STAGES)}
+
+    a8 = uses_a8(cfg, path)
+    gu_bytes, gu_flops = gate_up_work(cfg, touched, a8)
+    mfma_dt = "f32" if cfg.w == "f32" else ("fp8" if a8 else "bf16")
+    mfma_peak = MFMA_PEAK_TFLOPS[mfma_dt]
+    gb_s = gu_bytes / (gate_up_ms * 1e-3) / 1e9
+    tf_s = gu_flops / (gate_up_ms * 1e-3) / 1e12
+    if workload in HBM_GRADED:
+        roof = {"bound": "hbm", "achieved": round(gb_s, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gb_s / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tf_s, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(tf_s / mfma_peak, 4)}
+    roof["traffic"] = measured_traffic(workload, "gate_up_swiglu")
+    roof["kernel"] = "gate_up_swiglu"
+    roof["kernel_ms"] = round(gate_up_ms, 4)
+    roof["algorithmic_bytes"] = gu_bytes
+    roof["algorithmic_flops"] = gu_flops
+    roof["mfma_dtype"] = mfma_dt
+    roof["mfma_frac"] = round(tf_s / mfma_peak, 4)
+    roof["hbm_frac"] = round(gb_s / HBM_PEAK_GBS, 4)
+
+    # whole-layer view: touched expert weights (+ gate, shared expert) and
+    # flops over the step time
+    wb = weight_bytes(cfg)
+    A = cfg.T * cfg.k
+    layer_w = touched * (3 * cfg.H * cfg.F * wb + 2 * scale_bytes(cfg, cfg.H, cfg.F) + scale_bytes(cfg, cfg.F, cfg.H))
+    layer_w += gate_bytes(cfg) + shared_bytes(cfg)
+    layer_flops = 6.0 * A * cfg.H * cfg.F + 6.0 * cfg.T * cfg.H * cfg.Fs + 2.0 * cfg.T * cfg.H * cfg.E
+    res = {
+        "workload": cfg.name, "T": cfg.T, "steps": steps, "warmup": warmup,
+        "value": round(cfg.T * steps / elapsed, 1), "ms_per_step": round(ms_per_step, 4),
+        "latency_ms": {"p50": round(percentile(lat, 0.5), 4), "p95": round(percentile(lat, 0.95), 4),
+                       "max": round(max(lat), 4), "samples": n_lat},
+        "roofline": roof,
+        "layer": {"touched_experts": touched, "weight_bytes": layer_w,
+                  "hbm_frac": round(layer_w / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                  "mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / (mfma_peak * 1e12), 4),
+                  "mfma_dtype": mfma_dt, "stages_ms": stages},
+        "_data": (d, a8),
+    }
+    del layer, X, Y
+    return res
+
+
+def dtype_label(cfg, a8: bool) -> str:
+    return {"f32": "f32", "bf16": "bf16",
+            "fp8": "fp8-e4m3 weights and activations (fp32 scales)" if a8 else "fp8-e4m3 weights, bf16 activations",
+            "mxfp4": "mxfp4 weights (e2m1 + e8m0 scales), bf16 activations"}[cfg.w]
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mixtral_decode")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "tiled", "tiled_a8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-all-configs", action="store_true",
+                    help="time only --workload (by default every configuration is timed after it)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--record-traffic", action="store_true",
                     help="write the gate/up HBM traffic record from rocprofv3 counter runs (no GPU)")
@@ -336,110 +517,56 @@ def main() -> int:
     if args.sweep:
         return t_sweep(args)
 
-    import mixture_experts_layer_count_amd as moe
-    from mixture_experts_layer_count_amd._lib import MOE_N_EVENTS
-    from synth import get_config, make_layer
+    from synth import get_config
 
     cfg = get_config(args.workload)
-    d = make_layer(cfg, device="cuda")
-    layer = moe.MoELayer(d, cfg.k, path=args.path)
-    X = d["X"]
-    Y = torch.empty_like(X)
-
-    # routing of this batch: which experts are touched (bytes actually streamed)
-    _, _, idx, _, counts = layer.forward(X, Y, aux=True)
-    torch.cuda.synchronize()
-    touched = int((counts > 0).sum().item())
-    A = cfg.T * cfg.k
-
-    EV_SCHED, EV_GATE_UP = 3, 4
-    evs = [moe.StageEvents(want=[EV_SCHED, EV_GATE_UP]) for _ in range(args.steps)]
-    for _ in range(args.warmup):
-        layer.forward(X, Y)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        layer.forward(X, Y, events=evs[i].handles)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    gate_up_ms = statistics.fmean(e.elapsed_ms(EV_SCHED, EV_GATE_UP) for e in evs)
-
-    # per-stage breakdown (separate, untimed pass: every marker recorded)
-    stage_runs = []
-    for _ in range(max(5, min(args.steps, 20))):
-        ev = moe.StageEvents()
-        layer.forward(X, Y, events=ev.handles)
-        stage_runs.append([ev.elapsed_ms(i, i + 1) for i in range(MOE_N_EVENTS - 1)])
-    torch.cuda.synchronize()
-    stages_ms = {name: round(statistics.median(r[i] for r in stage_runs), 4) for i, name in enumerate(moe.STAGES)}
-
-    # algorithmic work of the dominant kernel (routed gate/up + SwiGLU), per launch
-    wb = weight_bytes(cfg)
-    ab = 4.0 if cfg.act == "f32" else 2.0
-    gate_up_w = touched * 2 * (cfg.H * cfg.F * wb + scale_bytes(cfg, cfg.H, cfg.F))
-    gate_up_rows = A
-    if cfg.Fs > 0 and cfg.Fs == cfg.F and cfg.shared_w == cfg.w:
-        # the always-on shared expert runs as one more group of the same launch
-        gate_up_w += 2 * (cfg.H * cfg.Fs * wb + scale_bytes(cfg, cfg.H, cfg.Fs))
-        gate_up_rows += cfg.T
-    gate_up_bytes = gate_up_w + cfg.T * cfg.H * ab + gate_up_rows * cfg.F * ab
-    gate_up_flops = 4.0 * gate_up_rows * cfg.H * cfg.F
-    decode = args.workload in DECODE_WORKLOADS
-    a8 = cfg.w == "fp8" and (args.path == "tiled_a8" or (args.path == "auto" and not decode))
-    kernel_name = "gate_up_swiglu"
-    if decode:
-        achieved = gate_up_bytes / (gate_up_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        # fp8 weights: W8A8 on the fp8 matrix cores on the tiled_a8 path (the
-        # prefill default), else decoded to bf16 for the bf16 MFMA
-        mfma_dt = "f32" if cfg.w == "f32" else ("fp8" if a8 else "bf16")
-        achieved = gate_up_flops / (gate_up_ms * 1e-3) / 1e12
-        peak = MFMA_PEAK_TFLOPS[mfma_dt]
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
-    roof["traffic"] = measured_traffic(args.workload, kernel_name)
-    roof["kernel"] = kernel_name
-    roof["kernel_ms"] = round(gate_up_ms, 4)
-    roof["algorithmic_bytes"] = gate_up_bytes
-    roof["algorithmic_flops"] = gate_up_flops
-
-    # whole-layer view: touched expert weights (+ gate, shared expert) over the step time
-    layer_w = touched * (3 * cfg.H * cfg.F * wb + 2 * scale_bytes(cfg, cfg.H, cfg.F) + scale_bytes(cfg, cfg.F, cfg.H))
-    layer_w += gate_bytes(cfg) + shared_bytes(cfg)
-    layer_flops = 6.0 * A * cfg.H * cfg.F + 6.0 * cfg.T * cfg.H * cfg.Fs + 2.0 * cfg.T * cfg.H * cfg.E
-
+    m = measure(cfg, args.path, args.steps, args.warmup, args.workload)
+    d, a8 = m.pop("_data")
     out = {
         "metric": METRIC,
-        "value": round(cfg.T * args.steps / elapsed, 1),
+        "value": m["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16",
-                  "fp8": "fp8-e4m3 weights and activations (fp32 scales)" if a8
-                  else "fp8-e4m3 weights, bf16 activations",
-                  "mxfp4": "mxfp4 weights (e2m1 + e8m0 scales), bf16 activations"}[cfg.w],
+        "dtype": dtype_label(cfg, a8),
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
                    "Fs": cfg.Fs, "weights": cfg.w, "shared_weights": cfg.shared_w if cfg.Fs else None,
-                   "gate": cfg.wg or cfg.act,
-                   "activations": cfg.act, "path": args.path},
-        "roofline": roof,
-        "layer": {"touched_experts": touched, "weight_bytes": layer_w,
-                  "hbm_frac": round(layer_w / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-                  "mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / (MFMA_PEAK_TFLOPS["bf16"] * 1e12), 4),
-                  "stages_ms": stages_ms},
+                   "gate": cfg.wg or cfg.act, "activations": cfg.act, "path": args.path},
+        "roofline": m["roofline"],
+        "latency_ms": m["latency_ms"],
+        "layer": m["layer"],
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, d, cfg.k)
+    del d
+    torch.cuda.empty_cache()
+    if not args.no_all_configs:
+        # the other configurations, timed in the same run (each its own
+        # seeded layer, freed before the next is drawn)
+        table = {}
+        for name in ALL_CONFIGS:
+            if name == args.workload:
+                continue
+            c = get_config(name)
+            decode = name in DECODE_WORKLOADS
+            r = measure(c, "auto", 50 if decode else 10, 5 if decode else 3, name)
+            r.pop("_data")
+            torch.cuda.empty_cache()
+            table[name] = {"T": r["T"], "steps": r["steps"], "ms_per_step": r["ms_per_step"],
+                           "tokens_per_s": r["value"], "latency_ms": r["latency_ms"],
+                           "dominant_kernel": {k2: r["roofline"][k2] for k2 in
+                                               ("kernel", "bound", "achieved", "unit", "frac", "kernel_ms",
+                                                "mfma_dtype", "mfma_frac", "hbm_frac", "traffic")},
+                           "layer_hbm_frac": r["layer"]["hbm_frac"], "layer_mfma_frac": r["layer"]["mfma_frac"],
+                           "stages_p50_ms": {s: v["p50"] for s, v in r["layer"]["stages_ms"].items()}}
+            print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+        out["configs"] = table
     print(json.dumps(out))
     return 0
 

@@ -51,7 +51,10 @@
  *    tiled path (TILED, or AUTO at >= 192 rows per expert) first decodes every
  *    expert to bf16 in the workspace (3*E*H*F*2 bytes more, counted by the
  *    workspace-size calls). TILED_A8 is refused.
- *    H and F must be multiples of 32; E <= 1024; 1 <= k <= min(E, 64).
+ *    H and F must be multiples of 32 and at most 2^20; E <= 1024;
+ *    1 <= k <= min(E, 64); moe_route needs T*E < 2^31, moe_permute T*k < 2^31,
+ *    moe_forward T <= 65535. Larger sizes return MOE_ERR_UNSUPPORTED (and the
+ *    *_workspace_bytes calls 0).
  *  - Thread safety: no mutable global state; concurrent calls on different
  *    streams with disjoint outputs and workspaces are safe.
  */

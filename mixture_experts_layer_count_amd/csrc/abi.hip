@@ -53,9 +53,11 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
     } while (0)
 
 // Shape rules for expert matrices [K][N].
+constexpr int kMaxDim = 1 << 20;  // largest H or F (keeps every size product in range)
+
 moe_status check_ffn_dims(int H, int F, moe_dtype w_dt) {
     if (H < 1 || F < 1) return MOE_ERR_INVALID_ARG;
-    if (H % 32 || F % 32) return MOE_ERR_UNSUPPORTED;
+    if (H % 32 || F % 32 || H > kMaxDim || F > kMaxDim) return MOE_ERR_UNSUPPORTED;
     if (w_dt == MOE_FP8_E4M3 && (H % 128 || F % 128)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -340,7 +342,7 @@ struct RoutePlan {
 
 RoutePlan plan_route(int T, int H, int E, moe_dtype x_dt, moe_dtype wg_dt) {
     if (x_dt == MOE_BF16 && wg_dt == MOE_BF16 && T >= 512 && tiled_f32_supports(T, E, H, 1, H)) {
-        const long long tiles = (long long)((T + 127) / 128) * ((E + 255) / 256);
+        const long long tiles = (((long long)T + 127) / 128) * (((long long)E + 255) / 256);
         long long ks = 256 / tiles;  // one workgroup per CU, one round
         long long max_ks = H / 256 > 0 ? H / 256 : 1;
         if (max_ks > 16) max_ks = 16;
@@ -350,7 +352,7 @@ RoutePlan plan_route(int T, int H, int E, moe_dtype x_dt, moe_dtype wg_dt) {
         chunk = (chunk + 31) / 32 * 32;
         return RoutePlan{(H + chunk - 1) / chunk, chunk, true};
     }
-    long long base = (long long)((T + 15) / 16) * ((E + 63) / 64);
+    long long base = (((long long)T + 15) / 16) * (((long long)E + 63) / 64);
     if (base < 1) base = 1;
     long long ks = (4096 + base - 1) / base;
     long long max_ks = H / 128 > 0 ? H / 128 : 1;
@@ -408,14 +410,15 @@ moe_status check_route(moe_dtype x_dt, moe_dtype wg_dt, int T, int H, int E, int
     if (!act_ok(x_dt)) return MOE_ERR_UNSUPPORTED;
     // the gate in the token dtype, or fp32 beside bf16 tokens
     if (wg_dt != x_dt && !(x_dt == MOE_BF16 && wg_dt == MOE_F32)) return MOE_ERR_UNSUPPORTED;
-    if (E > 1024 || k > 64 || E % 4 || H % 32) return MOE_ERR_UNSUPPORTED;
+    if (E > 1024 || k > 64 || E % 4 || H % 32 || H > kMaxDim) return MOE_ERR_UNSUPPORTED;
+    if ((long long)T * E > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
 }  // namespace
 
 size_t moe_route_workspace_bytes(int T, int H, int E) {
-    if (T < 0 || H < 1 || E < 1) return 0;
+    if (T < 0 || H < 1 || E < 1 || E > 1024 || H > kMaxDim || (long long)T * E > 0x7fffffffLL) return 0;
     return align_up(route_ws_bytes(T, H, E));
 }
 
@@ -434,6 +437,7 @@ moe_status moe_route(const void *X, moe_dtype x_dt, const void *Wg, moe_dtype wg
 // ---------------------------------------------------------------------------
 size_t moe_permute_workspace_bytes(int T, int k, int E) {
     if (T < 0 || k < 1 || E < 1) return 0;
+    if ((long long)T * k > 0x7fffffffLL) return 0;  // moe_permute refuses such sizes
     return align_up(permute_ws_bytes(T * k, E));
 }
 
@@ -461,7 +465,7 @@ moe_status moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *co
 // ---------------------------------------------------------------------------
 size_t moe_grouped_ffn_workspace_bytes(int M, int G, int H, int F, moe_dtype act_dt,
                                        moe_dtype w_dt, moe_ffn_path path) {
-    if (M < 0 || G < 1 || H < 1 || F < 1) return 0;
+    if (M < 0 || G < 1 || H < 1 || F < 1 || H > kMaxDim || F > kMaxDim) return 0;
     const FfnPlan p = plan_ffn(M, G, H, F, w_dt, path);
     Carver c(nullptr);
     FfnWs w{};
@@ -659,7 +663,8 @@ ForwardWs carve_forward(const moe_layer_desc *d, int T, void *base) {
 }  // namespace
 
 size_t moe_forward_workspace_bytes(const moe_layer_desc *desc, int T) {
-    if (check_desc(desc) != MOE_OK || T < 0) return 0;
+    // moe_forward takes at most 65535 tokens
+    if (check_desc(desc) != MOE_OK || T < 0 || T > 65535) return 0;
     return carve_forward(desc, T, nullptr).bytes;
 }
 

@@ -6,7 +6,7 @@ arithmetic (no routing, no permutation, no expert FFN, no combine). Both the
 CPU oracle and the HIP path are fed from here.
 """
 from .configs import CONFIGS, MINI_CONFIGS, LayerConfig, get_config
-from .gen import make_layer, redraw_rows, quantize_e4m3_blocks, quantize_mxfp4, tensor_seed
+from .gen import make_layer, redraw_rows, quantize_e4m3_blocks, quantize_mxfp4, spread_block_scales, tensor_seed
 
 __all__ = ["CONFIGS", "MINI_CONFIGS", "LayerConfig", "get_config", "make_layer",
-           "redraw_rows", "quantize_e4m3_blocks", "quantize_mxfp4", "tensor_seed"]
+           "redraw_rows", "quantize_e4m3_blocks", "quantize_mxfp4", "spread_block_scales", "tensor_seed"]

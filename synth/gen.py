@@ -176,3 +176,22 @@ def redraw_rows(cfg: LayerConfig, X: torch.Tensor, rows, attempt: int) -> None:
         t = int(t)
         x = _normal(cfg, "X-redraw", (cfg.H,), cfg.x_std, X.device, t, attempt)
         X[t].copy_(x.to(X.dtype))
+
+
+def spread_block_scales(d: dict, seed: int, lo: int = -4, hi: int = 4) -> dict:
+    """A copy of layer `d` whose fp32 128x128 block scales (S1, S3, S2 and the
+    shared expert's Ss1, Ss3, Ss2) are each multiplied by a seeded power of two
+    2^u, u uniform in [lo, hi]. The E4M3 codes are unchanged, so the stored
+    weights stay exact; blocks then differ in scale by up to 2^(hi - lo), and a
+    weight read with another block's scale is far off."""
+    out = dict(d)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    for key in ("S1", "S3", "S2", "Ss1", "Ss3", "Ss2"):
+        s = d.get(key)
+        if s is None or s.dtype != torch.float32:
+            continue
+        u = torch.randint(lo, hi + 1, tuple(s.shape), generator=g).to(torch.float32)
+        out[key] = (s * torch.exp2(u).to(s.device)).contiguous()
+    return out
+

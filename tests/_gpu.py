@@ -59,3 +59,29 @@ def rel_err(got, ref) -> float:
 
 def tol_for(cfg) -> float:
     return TOL[cfg.w] if cfg.w == "fp8" else TOL[cfg.act]
+
+
+def cover_tokens(idx: np.ndarray, extra=()) -> np.ndarray:
+    """Tokens whose outputs are compared at full size: a greedy cover of the
+    routed sets (each step adds the token that chooses the most experts not
+    yet covered, until every touched expert is), plus the first and last row
+    of every expert block (rows are in ascending token order, so the smallest
+    and largest token that chose the expert), plus `extra`. Every token also
+    passes through the shared expert, whose block's first and last rows are
+    tokens 0 and T - 1 (in `extra` by the caller when there is one)."""
+    idx = np.asarray(idx)
+    T = idx.shape[0]
+    uncovered = set(np.unique(idx).tolist())
+    sets = [set(row.tolist()) for row in idx]
+    chosen = []
+    while uncovered:
+        t = max(range(T), key=lambda i: len(sets[i] & uncovered))
+        chosen.append(t)
+        uncovered -= sets[t]
+    ends = []
+    for e in np.unique(idx):
+        ts = np.nonzero((idx == e).any(axis=1))[0]
+        ends += [ts[0], ts[-1]]
+    return np.unique(np.concatenate([np.asarray(chosen, dtype=np.int64), np.asarray(ends, dtype=np.int64),
+                                     np.asarray(list(extra), dtype=np.int64)]))
+

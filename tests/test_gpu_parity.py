@@ -5,6 +5,8 @@ bit-exact given the same fp32 logits; layer outputs within the max relative
 error max|Y - Y_ref| / max|Y_ref| of 2e-2 (bf16), 6e-2 (fp8 weights) and 1e-4
 (f32). Inputs are seeded, with top-k logit gaps of at least 1e-3.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -13,7 +15,10 @@ import mixture_experts_layer_count_amd as moe
 import oracle
 from synth import CONFIGS, MINI_CONFIGS, LayerConfig
 from synth.worked import load_fixture, worked_example_layer
-from _gpu import rel_err, say, screened_layer, tol_for
+from _gpu import cover_tokens, rel_err, say, screened_layer, tol_for
+
+# host threads for the oracle's per-expert work (model-sized layers)
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +86,43 @@ def test_route_shapes(T, E, k, H):
     torch.cuda.synchronize()
     _check_routing(cfg, d, logits, idx, w)
     np.testing.assert_allclose(w.sum(dim=1).cpu().numpy(), 1.0, atol=1e-6)
+
+
+def test_route_exact_ties():
+    """Equal scores go to the lower expert index. Zero token rows (padding
+    tokens) give all-equal logits: the k lowest experts, each with weight
+    1/k. Duplicated gate columns give pairs of equal logits: the lower index
+    of a pair comes first wherever both are chosen. Both the row-streaming
+    router (few tokens) and the tiled one (512 tokens and more) run."""
+    for T in (200, 600):
+        cfg = LayerConfig(f"ties_{T}", T=T, H=256, F=32, E=64, k=6, seed=90 + T)
+        say(f"[route] exact ties T={T}")
+        d = screened_layer(cfg, experts=False)
+        X = d["X"].clone()
+        X[::3] = 0.0                                  # every third token is padding
+        Wg = d["Wg"].clone()
+        pairs = [(3, 40), (10, 11), (17, 63), (0, 32)]  # same slice, next column, other slices
+        for a, b in pairs:
+            Wg[:, b] = Wg[:, a]
+        logits, idx, w = moe.route(X, Wg, cfg.k)
+        torch.cuda.synchronize()
+        lg, ix, wt = logits.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+        for a, b in pairs:
+            assert np.array_equal(lg[:, a], lg[:, b])  # the tie is exact in the GPU's fp32 logits
+        np.testing.assert_array_equal(ix, oracle.select_topk(lg, cfg.k))
+        zero = np.arange(0, T, 3)
+        assert (lg[zero] == 0.0).all()
+        np.testing.assert_array_equal(ix[zero], np.tile(np.arange(cfg.k), (zero.size, 1)))
+        np.testing.assert_allclose(wt[zero], 1.0 / cfg.k, rtol=0, atol=1e-7)
+        both = 0
+        for a, b in pairs:
+            for t in range(T):
+                row = list(ix[t])
+                if a in row and b in row:
+                    assert row.index(a) == row.index(b) - 1  # adjacent, lower index first
+                    both += 1
+        assert both > 0
+        np.testing.assert_allclose(wt, oracle.routing_weights(lg.astype(np.float64), ix), rtol=0, atol=2e-6)
 
 
 # ----------------------------------------------------------------------------
@@ -207,6 +249,35 @@ def test_mxfp4_every_code(name):
         assert err <= tol_for(cfg)
         _check_forward(cfg, d, moe.MoELayer(d, cfg.k, path=path))
 
+# fp8 block scales spread by seeded powers of two (2^-4 .. 2^4): with the
+# synthetic scales alone (all within about 1.5x of each other) a kernel that
+# read a neighbouring block's scale would stay inside the fp8 bar; with the
+# spread it moves the output far beyond it (shown on the CPU in
+# test_scale_spread.py). Routed experts through moe_grouped_ffn, then the whole
+# layer with its shared expert, on every path.
+SPREAD_CASES = [(n, p) for n in ("mini_fp8_decode", "mini_fp8_prefill", "mini_fp8_wide", "mini_fp8_bf16s_prefill")
+                for p in ("gemv", "tiled", "tiled_a8")]
+
+
+@pytest.mark.parametrize("name,path", SPREAD_CASES)
+def test_fp8_block_scales_spread(name, path):
+    from synth import spread_block_scales
+    cfg = MINI_CONFIGS[name]
+    say(f"[fp8 spread scales] {name} path={path}")
+    d = spread_block_scales(screened_layer(cfg), seed=cfg.seed + 2025)
+    L = oracle.Layer(d, cfg.k)
+    _, idx, _ = oracle.route(L.X(), L.Wg(), L.gate_bias(), cfg.k)
+    counts, offsets, row_src, _ = oracle.permute(idx, cfg.E)
+    ref = oracle.grouped_ffn(L.X()[row_src // cfg.k], offsets, L.expert)
+    Yp = moe.grouped_ffn(d["X"], _to_dev_i32(offsets), d["W1"], d["W3"], d["W2"], d["S1"], d["S3"], d["S2"],
+                         row_src=_to_dev_i32(row_src), k=cfg.k, path=path)
+    torch.cuda.synchronize()
+    err = rel_err(Yp, ref)
+    say(f"    grouped FFN max rel err {err:.3e} (tol {tol_for(cfg)})")
+    assert err <= tol_for(cfg)
+    _check_forward(cfg, d, moe.MoELayer(d, cfg.k, path=path), mirror=path == "tiled_a8")
+
+
 # Group sizes on both sides of every tile height (128, 160, 256 rows), with
 # empty groups; the rows are pre-permuted token rows drawn by the generator.
 EDGE_SIZES = {
@@ -230,6 +301,9 @@ def test_grouped_ffn_tile_edges(name, path):
     M = int(offsets[-1])
     say(f"[ffn edges] {name} path={path} sizes={sizes}")
     d = screened_layer(cfg)
+    if cfg.w == "fp8":  # block scales spread, so scale indexing at the tile edges shows
+        from synth import spread_block_scales
+        d = spread_block_scales(d, seed=cfg.seed + 77)
     L = oracle.Layer(d, cfg.k)
     Xp = make_layer(dataclasses.replace(cfg, name=cfg.name + "_edges", T=M), device="cuda", experts=False)["X"]
     Yp = moe.grouped_ffn(Xp, _to_dev_i32(offsets), d["W1"], d["W3"], d["W2"], d["S1"], d["S3"], d["S2"], path=path)
@@ -306,13 +380,20 @@ def _check_forward(cfg, d, layer, tokens=None, mirror=False):
     L = oracle.Layer(d, cfg.k)
     if tokens is None:
         tokens = np.arange(cfg.T)
-    ref = oracle.forward_tokens(L, tokens, idx=idx_np[tokens])
+    elif isinstance(tokens, str) and tokens == "cover":
+        # every touched expert, the first and last row of every expert block
+        # (and of the shared expert's block), and a few tokens drawn at random
+        rng = np.random.default_rng(cfg.T)
+        tokens = cover_tokens(idx_np, [0, cfg.T - 1, *rng.choice(cfg.T, size=4, replace=False)])
+        say(f"    comparing {tokens.size} of {cfg.T} tokens (covering {np.unique(idx_np[tokens]).size} of "
+            f"{np.unique(idx_np).size} touched experts)")
+    ref = oracle.forward_tokens(L, tokens, idx=idx_np[tokens], workers=ORACLE_THREADS)
     err = rel_err(Y[torch.as_tensor(tokens, device="cuda")], ref["Y"])
     say(f"    max rel err {err:.3e} (tol {tol_for(cfg)})")
     assert err <= tol_for(cfg)
     assert torch.isfinite(Y.float()).all()
     if mirror:
-        ref_m = oracle.forward_tokens(L, tokens, idx=idx_np[tokens], act_quant=True)
+        ref_m = oracle.forward_tokens(L, tokens, idx=idx_np[tokens], act_quant=True, workers=ORACLE_THREADS)
         err_m = mean_rel(Y[torch.as_tensor(tokens, device="cuda")], ref_m["Y"])
         say(f"    against the quantisation mirror: mean {err_m:.3e} (tol {MIRROR_TOL})")
         assert err_m <= MIRROR_TOL
@@ -362,24 +443,15 @@ def test_forward_empty_batch():
     assert Y.shape == (0, cfg.H)
 
 
-FULL_SAMPLES = {"toy_fp32": None, "mixtral_decode": None, "qwen3_decode": None,
-                "mixtral_prefill": 6, "qwen3_prefill": 8, "dsv3_decode": 4, "dsv3_prefill": 4,
-                "dsv3_decode_bf16_shared": 4, "dsv3_prefill_bf16_shared": 4, "qwen3_prefill_f32_router": 8,
-                "mixtral_decode_mxfp4": None, "qwen3_decode_mxfp4": None,
-                "mixtral_prefill_mxfp4": 6, "qwen3_prefill_mxfp4": 8}
-
-
 @pytest.mark.parametrize("name", list(CONFIGS))
 def test_forward_full_size(name):
+    """Routing on every token; outputs on every token of the decode batches,
+    and at prefill sizes on a set of tokens that covers every touched expert
+    and the first and last row of every expert block."""
     cfg = CONFIGS[name]
     say(f"[forward] full size {name} T={cfg.T} H={cfg.H} F={cfg.F} E={cfg.E} k={cfg.k} Fs={cfg.Fs} w={cfg.w}")
     d = screened_layer(cfg)
-    n = FULL_SAMPLES[name]
-    tokens = None
-    if n is not None:
-        rng = np.random.default_rng(cfg.T)
-        tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, size=n - 2, replace=False)]))
-    _check_forward(cfg, d, moe.MoELayer(d, cfg.k), tokens)
+    _check_forward(cfg, d, moe.MoELayer(d, cfg.k), None if cfg.T <= 64 else "cover")
 
 
 # The method's size limits: 1024 experts (the most the router and permutation
