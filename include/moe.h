@@ -74,7 +74,9 @@ typedef enum {
     MOE_ERR_INVALID_ARG = 1,         /* null pointer, bad size, k > E, ... */
     MOE_ERR_UNSUPPORTED = 2,         /* valid but not implemented: dtype pair, alignment */
     MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes below the *_workspace_bytes() value */
-    MOE_ERR_HIP = 4                  /* a HIP launch failed */
+    MOE_ERR_HIP = 4,                 /* a HIP launch failed */
+    MOE_ERR_SCRATCH_LIMIT = 5        /* moe_forward_noalloc: the layer's workspace exceeds
+                                        moe_forward_noalloc_max_bytes() */
 } moe_status;
 
 typedef enum {
@@ -253,6 +255,33 @@ moe_status moe_forward(const moe_layer_desc *desc, const void *X, int T, void *Y
                        void *ws, size_t ws_bytes, hipStream_t stream,
                        float *logits_out, int32_t *topk_idx_out, float *topk_w_out,
                        int32_t *counts_out, hipEvent_t const *events /* [MOE_N_EVENTS] or NULL */);
+
+/* ---------------------------------------------------------------------------
+ * moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments, kernels and results as moe_forward
+ * (bit for bit); the workspace is a fixed array of
+ * moe_forward_noalloc_max_bytes() bytes (256 MiB) in device global memory that
+ * the library's code object holds on every GPU it is loaded on, until the
+ * process ends. Nothing is allocated or freed, on the device or by any
+ * library routine.
+ *  - The layer's workspace (moe_forward_workspace_bytes(desc, T)) must fit:
+ *    otherwise MOE_ERR_SCRATCH_LIMIT, returned on the host before the device
+ *    is touched. Every decode batch of the Mixtral-, Qwen3- and
+ *    DeepSeek-V3-shaped layers fits; prefill batches of thousands of tokens
+ *    do not (use moe_forward with a workspace).
+ *  - The work runs on the current device; `stream` (NULL = null stream) must
+ *    belong to it, else MOE_ERR_INVALID_ARG.
+ *  - Every call on one GPU uses that GPU's one array, and no kernel relies on
+ *    its contents at entry (each writes what it later reads, as with a fresh
+ *    workspace). Calls that overlap in time on one GPU (on different streams,
+ *    or from several threads without ordering) race on the array and give
+ *    undefined results: order them, e.g. on one stream.
+ * ------------------------------------------------------------------------- */
+size_t moe_forward_noalloc_max_bytes(void);
+moe_status moe_forward_noalloc(const moe_layer_desc *desc, const void *X, int T, void *Y, hipStream_t stream,
+                               float *logits_out, int32_t *topk_idx_out, float *topk_w_out,
+                               int32_t *counts_out, hipEvent_t const *events);
 
 #ifdef __cplusplus
 }

@@ -14,7 +14,8 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+(MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP,
+ MOE_ERR_SCRATCH_LIMIT) = range(6)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 PATHS = {"auto": 0, "gemv": 1, "tiled": 2, "tiled_a8": 3}
 
@@ -35,6 +36,8 @@ SIGNATURES = {
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _I, _P, _P]),
     "moe_forward_workspace_bytes": (_SZ, [_P, _I]),
     "moe_forward": (_I, [_P, _P, _I, _P, _P, _SZ, _P, _P, _P, _P, _P, _P]),
+    "moe_forward_noalloc_max_bytes": (_SZ, []),
+    "moe_forward_noalloc": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -279,6 +282,25 @@ class MoELayer:
                     torch.empty(self.E, dtype=torch.int32, device=dev)]
         _check("moe_forward", lib().moe_forward(ctypes.byref(self.desc), _ptr(X), T, _ptr(Y), _ptr(ws),
                                                 ws.numel(), _stream(), *[_ptr(o) for o in outs], events))
+        return (Y, *outs) if aux else Y
+
+
+    def forward_noalloc(self, X, Y=None, aux: bool = False, events=None):
+        """As forward(), through moe_forward_noalloc: no workspace is passed
+        (the library's fixed device scratch is used instead)."""
+        _dev(X, Y)
+        T = X.shape[0]
+        dev = X.device
+        if Y is None:
+            Y = torch.empty_like(X)
+        outs = [None] * 4
+        if aux:
+            outs = [torch.empty((T, self.E), dtype=torch.float32, device=dev),
+                    torch.empty((T, self.k), dtype=torch.int32, device=dev),
+                    torch.empty((T, self.k), dtype=torch.float32, device=dev),
+                    torch.empty(self.E, dtype=torch.int32, device=dev)]
+        _check("moe_forward_noalloc", lib().moe_forward_noalloc(ctypes.byref(self.desc), _ptr(X), T, _ptr(Y),
+                                                                _stream(), *[_ptr(o) for o in outs], events))
         return (Y, *outs) if aux else Y
 
 

@@ -323,6 +323,8 @@ const char *moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported dtype or shape";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch failed";
+    case MOE_ERR_SCRATCH_LIMIT:
+        return "MOE_ERR_SCRATCH_LIMIT: the layer's workspace exceeds the fixed scratch of moe_forward_noalloc";
     }
     return "unknown moe_status";
 }

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = moe.lib()
-    for code in range(5):
+    for code in range(6):
         assert lib.moe_status_string(code).startswith(b"MOE_")
     assert b"unknown" in lib.moe_status_string(99)
 
@@ -238,3 +238,26 @@ def test_c_consumer_builds_and_passes(tmp_path):
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stderr
     assert "all checks passed" in run.stdout
+
+
+def test_forward_noalloc_limit_on_host():
+    """moe_forward_noalloc refuses, on the host and before touching a device,
+    a layer whose workspace exceeds its fixed scratch (the DeepSeek-V3-shaped
+    fp8 prefill batch of 4096 tokens needs about 790 MiB), and validates the
+    descriptor like moe_forward."""
+    lib = moe.lib()
+    cap = lib.moe_forward_noalloc_max_bytes()
+    assert cap == 256 << 20
+    d = _lib.LayerDesc()
+    d.H, d.F, d.E, d.k, d.Fs = 7168, 2048, 256, 8, 2048
+    d.act_dt, d.w_dt, d.ws_dt = BF16, FP8, FP8
+    for key in ("Wg", "W1", "W3", "W2", "S1", "S3", "S2", "Ws1", "Ws3", "Ws2", "Ss1", "Ss3", "Ss2"):
+        setattr(d, key, 0x1000)
+    assert lib.moe_forward_workspace_bytes(ctypes.byref(d), 4096) > cap
+    assert lib.moe_forward_workspace_bytes(ctypes.byref(d), 64) <= cap
+    assert lib.moe_forward_noalloc(ctypes.byref(d), FAKE, 4096, FAKE, None, None, None, None, None, None) == 5
+    assert b"SCRATCH" in lib.moe_status_string(5)
+    assert lib.moe_forward_noalloc(ctypes.byref(d), None, 0, None, None, None, None, None, None, None) == OK
+    assert lib.moe_forward_noalloc(None, FAKE, 16, FAKE, None, None, None, None, None, None) == INVALID
+    d.k = 300  # k > E
+    assert lib.moe_forward_noalloc(ctypes.byref(d), FAKE, 16, FAKE, None, None, None, None, None, None) == INVALID
