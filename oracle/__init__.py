@@ -14,7 +14,8 @@ activation and output projection, unpermute) and 九 (kept weights are
 renormalised); the page "MoE serving production quirks" (tianpan.co), section
 on the memory paradox (the gate runs a linear projection and a softmax over all
 experts); the page "MoE-推理部署" (zzmblog.top), section on expert quantisation
-(per-expert FP8 scales; MXFP4 as a single-GPU weight format).
+(per-expert FP8 scales; MXFP4 as a single-GPU weight format). oracle.ep follows
+"MOE推理流程解析" §五 (expert-parallel dispatch and combine).
 
 Parity pins: see the functions' docstrings and tests/test_oracle_*.py. The
 whole-layer output at model scale has no printed values on the pages; it is
@@ -28,10 +29,11 @@ from .ref import (
     Layer, forward, forward_tokens,
 )
 from .brute import brute_force_forward
+from . import ep
 
 __all__ = [
     "to_f64", "e4m3_decode", "e4m3_encode", "quantize_rows_e4m3", "dequant_rows", "round_bf16", "dequant_blocks", "router_logits", "softmax",
     "select_topk", "route", "routing_weights", "permute", "silu", "swiglu_ffn",
     "grouped_ffn", "combine", "Layer", "forward", "forward_tokens",
-    "brute_force_forward",
+    "brute_force_forward", "ep",
 ]
