@@ -257,6 +257,77 @@ moe_status moe_forward(const moe_layer_desc *desc, const void *X, int T, void *Y
                        int32_t *counts_out, hipEvent_t const *events /* [MOE_N_EVENTS] or NULL */);
 
 /* ---------------------------------------------------------------------------
+ * Expert-parallel dispatch and combine (page "MOE推理流程解析" §五): experts
+ * are placed on G ranks in contiguous blocks, expert e on rank e / (E/G)
+ * (E divisible by G); an assignment whose expert is on another rank travels
+ * there as a record of the token row plus (token id, expert, source rank,
+ * routing weight); each rank groups what it received by expert and runs one
+ * matrix per active local expert (moe_permute + moe_grouped_ffn on the local
+ * expert ids); the results travel back and the source restores token order,
+ * weights and sums (moe_combine with send_slot as the inverse map). Here the
+ * G ranks share one device and moe_ep_exchange is the all-to-all between
+ * their buffers; on several GPUs it would be an RCCL all-to-all(v), whose
+ * split sizes are the count matrix below. Per-rank buffers of the exchange
+ * are laid out at a fixed stride from one base pointer.
+ * ------------------------------------------------------------------------- */
+typedef struct moe_ep_record {
+    int32_t token;    /* token id: token0 + local token index */
+    int32_t expert;   /* global expert index */
+    int32_t src_rank; /* rank the token lives on */
+    float weight;     /* routing weight of the assignment */
+} moe_ep_record;      /* 16 bytes */
+
+/* Dispatch on source rank `rank` of G: bucket its A = T*k assignments a =
+ * t*k + j (topk_idx, topk_w [T,k], as moe_route writes them) by destination
+ * rank, stably (ascending a within a destination), and pack them.
+ *   send_offsets [G+1]: first send row of each destination, send_offsets[G] = A
+ *   send_slot [A]:      send row of assignment a
+ *   send_rows [A, H]:   send row r holds X[a/k] (x_dt: F32 or BF16; H*size
+ *                       a multiple of 16 bytes)
+ *   send_meta [A]:      the record of that assignment (token = token0 + a/k)
+ * Assignments naming an expert outside [0, E) are left out (their rows and
+ * slots unset; send_offsets[G] counts the others). Deterministic.
+ * Workspace: moe_ep_dispatch_workspace_bytes(T, k, G). */
+size_t moe_ep_dispatch_workspace_bytes(int T, int k, int G);
+moe_status moe_ep_dispatch(const int32_t *topk_idx, const float *topk_w, const void *X, moe_dtype x_dt, int T,
+                           int k, int H, int E, int G, int rank, int token0, int32_t *send_offsets,
+                           int32_t *send_slot, void *send_rows, moe_ep_record *send_meta, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* Receive layout from every rank's send_offsets (device [G][G+1], row s =
+ * rank s's send_offsets): recv_offsets[d][s] = first receive row of rank d
+ * holding rank s's rows (sum of what ranks s' < s send to d),
+ * recv_offsets[d][G] = rows rank d receives. G <= 1024. */
+moe_status moe_ep_recv_offsets(const int32_t *send_offsets, int G, int32_t *recv_offsets, hipStream_t stream);
+
+/* All-to-all between G ranks' buffers on this device. Rank r's input rows
+ * start at in + r*in_rank_stride, its output rows at out + r*out_rank_stride
+ * (strides in bytes). For every ordered pair (s, d) and i < in_offsets[s][d+1]
+ * - in_offsets[s][d]:
+ *   out row out_offsets[d][s] + i of rank d = in row g(in_offsets[s][d] + i) of rank s,
+ * g(j) = gather[s*gather_rank_stride + j] when gather != NULL, else j.
+ * Offsets are device [G][G+1] arrays. Dispatch: in/out = send/receive rows
+ * (or records, 16 bytes), in_offsets = send_offsets, out_offsets =
+ * recv_offsets. Return: in = each expert rank's grouped-FFN output (local
+ * permuted order), gather = its moe_permute assign_row, in_offsets =
+ * recv_offsets, out_offsets = send_offsets, so results land in send order.
+ * row_bytes, the strides and the base pointers must be multiples of 16;
+ * max_rows bounds every pair's row count (rows beyond it are not copied);
+ * G*G <= 65535. The caller sizes every buffer for the rows the offsets
+ * name. */
+moe_status moe_ep_exchange(int G, const void *in, long long in_rank_stride, const int32_t *in_offsets,
+                           const int32_t *gather, long long gather_rank_stride, void *out,
+                           long long out_rank_stride, const int32_t *out_offsets, int row_bytes, int max_rows,
+                           hipStream_t stream);
+
+/* Receiver side of rank `rank`: local_idx[i] = recv_meta[i].expert - rank*E/G
+ * for the n received records (-1 for a record naming another rank's expert),
+ * the expert ids moe_permute groups the received rows by (T = n, k = 1,
+ * E = E/G). */
+moe_status moe_ep_local_experts(const moe_ep_record *recv_meta, int n, int E, int G, int rank, int32_t *local_idx,
+                                hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_forward without a caller workspace, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc. Same arguments, kernels and results as moe_forward

@@ -7,9 +7,11 @@ is a HIP kernel in libmoe.so (C ABI: include/moe.h); this package is its thin
 Python binding, with torch providing device memory and streams.
 """
 from ._lib import (
-    LIB_PATH, MOE_N_EVENTS, STAGES, MoEError, MoELayer, StageEvents, combine, grouped_ffn, lib,
-    permute, quantize_e4m3_rows, route,
+    EP_STAGES, LIB_PATH, MOE_N_EVENTS, STAGES, EPLoopback, MoEError, MoELayer, StageEvents, combine, ep_dispatch,
+    ep_exchange, ep_local_experts, ep_recv_offsets, grouped_ffn, lib, permute, quantize_e4m3_rows, rank_tokens,
+    route,
 )
 
-__all__ = ["LIB_PATH", "MOE_N_EVENTS", "STAGES", "MoEError", "MoELayer", "StageEvents", "combine",
-           "grouped_ffn", "lib", "permute", "quantize_e4m3_rows", "route"]
+__all__ = ["EP_STAGES", "LIB_PATH", "MOE_N_EVENTS", "STAGES", "EPLoopback", "MoEError", "MoELayer", "StageEvents",
+           "combine", "ep_dispatch", "ep_exchange", "ep_local_experts", "ep_recv_offsets", "grouped_ffn", "lib",
+           "permute", "quantize_e4m3_rows", "rank_tokens", "route"]

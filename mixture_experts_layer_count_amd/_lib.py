@@ -37,6 +37,12 @@ SIGNATURES = {
     "moe_forward_workspace_bytes": (_SZ, [_P, _I]),
     "moe_forward": (_I, [_P, _P, _I, _P, _P, _SZ, _P, _P, _P, _P, _P, _P]),
     "moe_forward_noalloc_max_bytes": (_SZ, []),
+    "moe_ep_dispatch_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "moe_ep_dispatch": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_ep_recv_offsets": (_I, [_P, _I, _P, _P]),
+    "moe_ep_exchange": (_I, [_I, _P, ctypes.c_longlong, _P, _P, ctypes.c_longlong, _P, ctypes.c_longlong, _P, _I,
+                             _I, _P]),
+    "moe_ep_local_experts": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "moe_forward_noalloc": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P]),
 }
 
@@ -147,9 +153,10 @@ def route(X, Wg, k: int, gate_bias=None):
     return logits, idx, w
 
 
-def permute(topk_idx, E: int, X=None):
-    """-> (counts [E], offsets [E+1], row_src [A], assign_row [A], Xp [A,H] or None)."""
-    _dev(topk_idx, X)
+def permute(topk_idx, E: int, X=None, assign_row=None):
+    """-> (counts [E], offsets [E+1], row_src [A], assign_row [A], Xp [A,H] or None).
+    `assign_row`: optional int32 [A] output buffer."""
+    _dev(topk_idx, X, assign_row)
     _i32(topk_idx)
     T, k = topk_idx.shape
     dev = topk_idx.device
@@ -157,7 +164,10 @@ def permute(topk_idx, E: int, X=None):
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     row_src = torch.empty(A, dtype=torch.int32, device=dev)
-    assign_row = torch.empty(A, dtype=torch.int32, device=dev)
+    if assign_row is None:
+        assign_row = torch.empty(A, dtype=torch.int32, device=dev)
+    elif assign_row.numel() != A or assign_row.dtype != torch.int32:
+        raise ValueError("assign_row must be int32 with T*k elements")
     Xp = None
     H, xdt = 0, MOE_F32
     if X is not None:
@@ -173,16 +183,22 @@ def permute(topk_idx, E: int, X=None):
 
 
 def grouped_ffn(Xin, offsets, W1, W3, W2, S1=None, S3=None, S2=None, row_src=None, k: int = 1,
-                M: int | None = None, path: str = "auto"):
-    """Yp [M,H] = per-group SwiGLU FFN of the input rows (see moe_grouped_ffn)."""
-    _dev(Xin, offsets, W1, W3, W2, S1, S3, S2, row_src)
+                M: int | None = None, path: str = "auto", out=None):
+    """Yp [M,H] = per-group SwiGLU FFN of the input rows (see moe_grouped_ffn).
+    `out`: optional [M,H] output buffer."""
+    _dev(Xin, offsets, W1, W3, W2, S1, S3, S2, row_src, out)
     _i32(offsets)
     _i32(row_src)
     adt, wdt = act_dtype(Xin), weight_dtype(W1, S1)
     G, H, F = _expert_dims(W1, wdt)
     if M is None:
         M = row_src.numel() if row_src is not None else Xin.shape[0]
-    Yp = torch.empty((M, H), dtype=Xin.dtype, device=Xin.device)
+    if out is None:
+        Yp = torch.empty((M, H), dtype=Xin.dtype, device=Xin.device)
+    elif tuple(out.shape) != (M, H) or out.dtype != Xin.dtype:
+        raise ValueError("out must be [M, H] in the activation dtype")
+    else:
+        Yp = out
     p = PATHS[path]
     nbytes = lib().moe_grouped_ffn_workspace_bytes(M, G, H, F, adt, wdt, p)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=Xin.device)
@@ -207,13 +223,19 @@ def quantize_e4m3_rows(X, row_src=None, k: int = 1, R: int | None = None):
     return Q, S
 
 
-def combine(Yp, assign_row, topk_w, S=None):
-    """Y [T,H] = sum_j w[t,j] * Yp[assign_row[t*k+j]] (+ S[t])."""
-    _dev(Yp, assign_row, topk_w, S)
+def combine(Yp, assign_row, topk_w, S=None, out=None):
+    """Y [T,H] = sum_j w[t,j] * Yp[assign_row[t*k+j]] (+ S[t]). `out`: optional
+    [T,H] output buffer."""
+    _dev(Yp, assign_row, topk_w, S, out)
     _i32(assign_row)
     T, k = topk_w.shape
     H = Yp.shape[1]
-    Y = torch.empty((T, H), dtype=Yp.dtype, device=Yp.device)
+    if out is None:
+        Y = torch.empty((T, H), dtype=Yp.dtype, device=Yp.device)
+    elif tuple(out.shape) != (T, H) or out.dtype != Yp.dtype:
+        raise ValueError("out must be [T, H] in Yp's dtype")
+    else:
+        Y = out
     _check("moe_combine", lib().moe_combine(_ptr(Yp), _ptr(assign_row), _ptr(topk_w), T, k, H, _ptr(S),
                                             act_dtype(Yp), _ptr(Y), _stream()))
     return Y
@@ -302,6 +324,184 @@ class MoELayer:
         _check("moe_forward_noalloc", lib().moe_forward_noalloc(ctypes.byref(self.desc), _ptr(X), T, _ptr(Y),
                                                                 _stream(), *[_ptr(o) for o in outs], events))
         return (Y, *outs) if aux else Y
+
+
+# ---------------------------------------------------------------------------
+# Expert-parallel dispatch and combine between G ranks on one device
+# ---------------------------------------------------------------------------
+RECORD_INTS = 4  # moe_ep_record: token, expert, src_rank (int32), weight (fp32 bits)
+
+
+def ep_dispatch(topk_idx, topk_w, X, E: int, G: int, rank: int, token0: int = 0, out=None):
+    """-> (send_offsets [G+1], send_slot [A], send_rows [A,H], send_meta [A,4]
+    int32 records). `out` optionally gives those four output buffers."""
+    _dev(topk_idx, topk_w, X)
+    _i32(topk_idx)
+    T, k = topk_idx.shape
+    H = X.shape[1]
+    A = T * k
+    dev = X.device
+    if out is None:
+        out = (torch.empty(G + 1, dtype=torch.int32, device=dev), torch.empty(A, dtype=torch.int32, device=dev),
+               torch.empty((A, H), dtype=X.dtype, device=dev),
+               torch.empty((A, RECORD_INTS), dtype=torch.int32, device=dev))
+    so, slot, rows, meta = out
+    _dev(so, slot, rows, meta)
+    if so.numel() != G + 1 or slot.numel() != A or tuple(rows.shape) != (A, H) or meta.numel() != A * RECORD_INTS:
+        raise ValueError("ep_dispatch output buffers have the wrong sizes")
+    nbytes = lib().moe_ep_dispatch_workspace_bytes(T, k, G)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check("moe_ep_dispatch", lib().moe_ep_dispatch(
+        _ptr(topk_idx), _ptr(topk_w), _ptr(X), act_dtype(X), T, k, H, E, G, rank, token0, _ptr(so), _ptr(slot),
+        _ptr(rows), _ptr(meta), _ptr(ws), nbytes, _stream()))
+    return so, slot, rows, meta
+
+
+def ep_recv_offsets(send_offsets):
+    """[G][G+1] send offsets of every rank -> [G][G+1] receive offsets."""
+    _dev(send_offsets)
+    _i32(send_offsets)
+    G = send_offsets.shape[0]
+    recv = torch.empty_like(send_offsets)
+    _check("moe_ep_recv_offsets", lib().moe_ep_recv_offsets(_ptr(send_offsets), G, _ptr(recv), _stream()))
+    return recv
+
+
+def ep_exchange(inp, in_offsets, out, out_offsets, max_rows: int, gather=None):
+    """All-to-all between the G ranks' row blocks inp [G, *, ...] -> out
+    [G, *, ...] (rows = the trailing dimensions; see moe_ep_exchange)."""
+    _dev(inp, in_offsets, out, out_offsets, gather)
+    _i32(in_offsets)
+    _i32(out_offsets)
+    G = inp.shape[0]
+    row_bytes = inp[0, 0].numel() * inp.element_size() if inp.shape[1] > 0 else out[0, 0].numel() * out.element_size()
+    _check("moe_ep_exchange", lib().moe_ep_exchange(
+        G, _ptr(inp), inp.stride(0) * inp.element_size(), _ptr(in_offsets), _ptr(gather),
+        0 if gather is None else gather.stride(0), _ptr(out), out.stride(0) * out.element_size(), _ptr(out_offsets),
+        row_bytes, max_rows, _stream()))
+    return out
+
+
+def ep_local_experts(recv_meta, n: int, E: int, G: int, rank: int, out=None):
+    """Local expert ids of the first n received records of rank `rank`."""
+    _dev(recv_meta, out)
+    local = torch.empty(n, dtype=torch.int32, device=recv_meta.device) if out is None else out
+    _check("moe_ep_local_experts", lib().moe_ep_local_experts(_ptr(recv_meta), n, E, G, rank, _ptr(local),
+                                                              _stream()))
+    return local
+
+
+def rank_tokens(T: int, G: int, r: int) -> slice:
+    """Token slice of rank r: the r-th of G contiguous slices of ceil(T/G)."""
+    n = -(-T // G)
+    return slice(min(r * n, T), min((r + 1) * n, T))
+
+
+class EPLoopback:
+    """One MoE layer with its experts spread over G ranks that share one
+    device (page "MOE推理流程解析" §五), each rank's steps issued in order:
+    route its tokens -> dispatch (bucket by owner, pack records) -> all-to-all
+    -> local permutation + grouped FFN of its experts -> return all-to-all ->
+    combine at the source (+ the shared expert, replicated per rank).
+    Between the two halves the host reads the G x G count matrix, as an
+    all-to-all(v) needs its split sizes; every other step stays on the device.
+    `events`: optional list of torch.cuda.Event, recorded after each stage
+    (EP_STAGES)."""
+
+    def __init__(self, weights: dict, k: int, G: int, path: str = "auto"):
+        self.w = weights
+        self.k, self.G, self.path = k, G, path
+        W1 = weights["W1"]
+        self.wdt = weight_dtype(W1, weights.get("S1"))
+        self.E, self.H, self.F = _expert_dims(W1, self.wdt)
+        if self.E % G:
+            raise ValueError("E must be divisible by G")
+        self.El = self.E // G
+
+    def _experts(self, d: int):
+        sl = slice(d * self.El, (d + 1) * self.El)
+        get = lambda key: None if self.w.get(key) is None else self.w[key][sl]
+        return [get(key) for key in ("W1", "W3", "W2", "S1", "S3", "S2")]
+
+    def forward(self, X, Y=None, events=None, keep: bool = False):
+        _dev(X, Y)
+        T, H = X.shape
+        G, k, E = self.G, self.k, self.E
+        dev = X.device
+        if Y is None:
+            Y = torch.empty_like(X)
+        mark = (lambda i: events[i].record()) if events else (lambda i: None)
+        ranks = [rank_tokens(T, G, r) for r in range(G)]
+        cap_s = max(max(sl.stop - sl.start for sl in ranks), 1) * k
+        mark(0)
+        # route on every rank (each on its own tokens)
+        routes = [route(X[sl], self.w["Wg"], k, self.w.get("gate_bias")) if sl.stop > sl.start else None
+                  for sl in ranks]
+        mark(1)
+        # dispatch: buckets by owner and records, into rank-strided buffers
+        send_off = torch.zeros((G, G + 1), dtype=torch.int32, device=dev)
+        send_slot = torch.empty((G, cap_s), dtype=torch.int32, device=dev)
+        send_rows = torch.empty((G, cap_s, H), dtype=X.dtype, device=dev)
+        send_meta = torch.empty((G, cap_s, RECORD_INTS), dtype=torch.int32, device=dev)
+        for r, sl in enumerate(ranks):
+            n = (sl.stop - sl.start) * k
+            if n == 0:
+                continue
+            ep_dispatch(routes[r][1], routes[r][2], X[sl], E, G, r, sl.start,
+                        out=(send_off[r], send_slot[r, :n], send_rows[r, :n], send_meta[r, :n]))
+        recv_off = ep_recv_offsets(send_off)
+        mark(2)
+        # the count matrix on the host (an all-to-all(v) needs its split sizes)
+        recv_h = recv_off.cpu()
+        n_recv = [int(recv_h[d, G]) for d in range(G)]
+        cap_r = max(max(n_recv), 1)
+        recv_rows = torch.empty((G, cap_r, H), dtype=X.dtype, device=dev)
+        recv_meta = torch.empty((G, cap_r, RECORD_INTS), dtype=torch.int32, device=dev)
+        ep_exchange(send_rows, send_off, recv_rows, recv_off, cap_s)
+        ep_exchange(send_meta, send_off, recv_meta, recv_off, cap_s)
+        mark(3)
+        # each rank's experts on what it received
+        Yp = torch.empty((G, cap_r, H), dtype=X.dtype, device=dev)
+        assign = torch.empty((G, cap_r), dtype=torch.int32, device=dev)
+        local = []
+        for d in range(G):
+            n = n_recv[d]
+            if n == 0:
+                local.append(None)
+                continue
+            lidx = ep_local_experts(recv_meta[d, :n], n, E, G, d)
+            counts, offsets, row_src, _, _ = permute(lidx.view(n, 1), self.El, assign_row=assign[d, :n])
+            W1, W3, W2, S1, S3, S2 = self._experts(d)
+            grouped_ffn(recv_rows[d, :n], offsets, W1, W3, W2, S1, S3, S2, row_src=row_src, k=1, path=self.path,
+                        out=Yp[d, :n])
+            local.append((lidx, counts, offsets, row_src))
+        mark(4)
+        # results back to their sources, in send order
+        ret = torch.empty((G, cap_s, H), dtype=X.dtype, device=dev)
+        ep_exchange(Yp, recv_off, ret, send_off, cap_s, gather=assign)
+        mark(5)
+        # combine at the source (+ the shared expert on the rank's own tokens)
+        shared = self.w.get("Ws1") is not None
+        for r, sl in enumerate(ranks):
+            nt = sl.stop - sl.start
+            if nt == 0:
+                continue
+            S = None
+            if shared:
+                off = torch.tensor([0, nt], dtype=torch.int32, device=dev)
+                sw = [None if self.w.get(key) is None else self.w[key].unsqueeze(0)
+                      for key in ("Ws1", "Ws3", "Ws2", "Ss1", "Ss3", "Ss2")]
+                S = grouped_ffn(X[sl], off, *sw, path=self.path)
+            combine(ret[r, :nt * k], send_slot[r, :nt * k], routes[r][2], S, out=Y[sl])
+        mark(6)
+        if keep:
+            self.last = dict(routes=routes, send_off=send_off, send_slot=send_slot, send_rows=send_rows,
+                             send_meta=send_meta, recv_off=recv_off, n_recv=n_recv, recv_rows=recv_rows,
+                             recv_meta=recv_meta, Yp=Yp, assign=assign, local=local, ret=ret)
+        return Y
+
+
+EP_STAGES = ["route", "dispatch", "exchange", "experts", "return", "combine"]
 
 
 # ---------------------------------------------------------------------------

@@ -261,3 +261,29 @@ def test_forward_noalloc_limit_on_host():
     assert lib.moe_forward_noalloc(None, FAKE, 16, FAKE, None, None, None, None, None, None) == INVALID
     d.k = 300  # k > E
     assert lib.moe_forward_noalloc(ctypes.byref(d), FAKE, 16, FAKE, None, None, None, None, None, None) == INVALID
+
+
+def test_ep_validation():
+    """Expert-parallel calls answer bad arguments on the host."""
+    lib = moe.lib()
+    assert lib.moe_ep_dispatch_workspace_bytes(16, 2, 4) > 0
+    assert lib.moe_ep_dispatch_workspace_bytes(16, 2, 2000) == 0
+    # E not divisible by G, rank out of range, k > E, fp8 rows
+    args = lambda E, G, rank, k=2, dt=BF16: (FAKE, FAKE, FAKE, dt, 4, k, 64, E, G, rank, 0, FAKE, FAKE, FAKE, FAKE,
+                                             FAKE, 1 << 20, None)
+    assert lib.moe_ep_dispatch(*args(6, 4, 0)) == INVALID
+    assert lib.moe_ep_dispatch(*args(8, 4, 4)) == INVALID
+    assert lib.moe_ep_dispatch(*args(8, 4, 0, k=9)) == INVALID
+    assert lib.moe_ep_dispatch(*args(8, 4, 0, dt=FP8)) == UNSUPPORTED
+    assert lib.moe_ep_dispatch(FAKE, FAKE, FAKE, BF16, 4, 2, 64, 8, 4, 0, 0, FAKE, FAKE, FAKE, FAKE, None, 0,
+                               None) == WS_SMALL
+    assert lib.moe_ep_dispatch(None, None, None, BF16, 0, 2, 64, 8, 4, 0, 0, None, None, None, None, None, 0,
+                               None) == OK
+    # exchange: row bytes and strides multiples of 16; G*G grid limit
+    assert lib.moe_ep_exchange(4, FAKE, 64, FAKE, None, 0, FAKE, 64, FAKE, 24, 8, None) == UNSUPPORTED
+    assert lib.moe_ep_exchange(4, FAKE, 40, FAKE, None, 0, FAKE, 64, FAKE, 16, 8, None) == UNSUPPORTED
+    assert lib.moe_ep_exchange(300, FAKE, 64, FAKE, None, 0, FAKE, 64, FAKE, 16, 8, None) == UNSUPPORTED
+    assert lib.moe_ep_exchange(0, FAKE, 64, FAKE, None, 0, FAKE, 64, FAKE, 16, 8, None) == INVALID
+    assert lib.moe_ep_exchange(4, FAKE, 64, FAKE, None, 0, FAKE, 64, FAKE, 16, 0, None) == OK
+    assert lib.moe_ep_local_experts(FAKE, 4, 8, 3, 0, FAKE, None) == INVALID
+    assert lib.moe_ep_recv_offsets(FAKE, 0, FAKE, None) == INVALID
