@@ -467,6 +467,78 @@ def measure(cfg, path: str, steps: int, warmup: int, workload: str) -> dict:
     return res
 
 
+def ep_bench(args) -> int:
+    """The layer with its experts spread over G ranks sharing this GPU
+    (dispatch by owner, all-to-all, local experts, return, combine at the
+    source): ms per step, per-stage p50/p95, and the all-to-all kernels'
+    bandwidth against the HBM peak (their bytes: token rows and records read
+    and written on the way out, result rows and the gather index on the way
+    back). The single-GPU layer is timed beside it on the same weights."""
+    import torch
+    import mixture_experts_layer_count_amd as moe
+    from synth import get_config, make_layer
+
+    cfg = get_config(args.workload)
+    G = args.ep
+    d = make_layer(cfg, device="cuda")
+    X = d["X"]
+    epl = moe.EPLoopback(d, cfg.k, G)
+    Y = torch.empty_like(X)
+    n_ev = len(moe.EP_STAGES) + 1
+    for _ in range(args.warmup):
+        epl.forward(X, Y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        epl.forward(X, Y)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    runs = []
+    for _ in range(max(10, args.steps)):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        epl.forward(X, Y, events=ev)
+        runs.append(ev)
+    torch.cuda.synchronize()
+    stage = {}
+    for i, name in enumerate(moe.EP_STAGES):
+        xs = [r[i].elapsed_time(r[i + 1]) for r in runs]
+        stage[name] = {"p50": round(percentile(xs, 0.5), 4), "p95": round(percentile(xs, 0.95), 4)}
+    step = [r[0].elapsed_time(r[-1]) for r in runs]
+    A = cfg.T * cfg.k
+    ab = 4 if cfg.act == "f32" else 2
+    out_bytes = 2.0 * A * (cfg.H * ab + 16)              # rows + records, read and written
+    back_bytes = 2.0 * A * cfg.H * ab + 4.0 * A          # result rows read and written, gather index
+    ex_ms, ret_ms = stage["exchange"]["p50"], stage["return"]["p50"]
+    layer = moe.MoELayer(d, cfg.k)
+    for _ in range(args.warmup):
+        layer.forward(X, Y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(X, Y)
+    torch.cuda.synchronize()
+    single_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    gbs = out_bytes / (ex_ms * 1e-3) / 1e9
+    out = {
+        "metric": "MoE-layer tokens/s, experts spread over G ranks on one GPU (loopback all-to-all)",
+        "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "ranks": G,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "latency_ms": {"p50": round(percentile(step, 0.5), 4), "p95": round(percentile(step, 0.95), 4)},
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k, "Fs": cfg.Fs,
+                   "weights": cfg.w, "experts_per_rank": cfg.E // G},
+        "stages_ms": stage,
+        "roofline": {"kernel": "ep_exchange (dispatch all-to-all: rows + records)", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": out_bytes,
+                     "return_bytes": back_bytes,
+                     "return_gb_s": round(back_bytes / (ret_ms * 1e-3) / 1e9, 1) if ret_ms > 0 else None},
+        "single_gpu_layer_ms": round(single_ms, 4),
+        "data": "synthetic",
+    }
+    print(json.dumps(out))
+    return 0
+
+
 def dtype_label(cfg, a8: bool) -> str:
     return {"f32": "f32", "bf16": "bf16",
             "fp8": "fp8-e4m3 weights and activations (fp32 scales)" if a8 else "fp8-e4m3 weights, bf16 activations",
@@ -494,6 +566,8 @@ def main() -> int:
     ap.add_argument("--sweep", metavar="WORKLOAD",
                     help="token-count sweep of this workload's layer shape (T = 1 .. --sweep-max-t), every path")
     ap.add_argument("--sweep-max-t", type=int, default=8192)
+    ap.add_argument("--ep", type=int, default=0, metavar="G",
+                    help="time the layer with its experts spread over G ranks on this GPU (loopback all-to-all)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 kernel-trace run (no GPU)")
     args = ap.parse_args()
@@ -516,6 +590,8 @@ def main() -> int:
         return 0
     if args.sweep:
         return t_sweep(args)
+    if args.ep:
+        return ep_bench(args)
 
     from synth import get_config
 
@@ -555,7 +631,7 @@ def main() -> int:
                 continue
             c = get_config(name)
             decode = name in DECODE_WORKLOADS
-            r = measure(c, "auto", 50 if decode else 10, 5 if decode else 3, name)
+            r = measure(c, "auto", 50 if decode else 20, 10, name)
             r.pop("_data")
             torch.cuda.empty_cache()
             table[name] = {"T": r["T"], "steps": r["steps"], "ms_per_step": r["ms_per_step"],

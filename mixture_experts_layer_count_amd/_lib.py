@@ -405,8 +405,9 @@ class EPLoopback:
     combine at the source (+ the shared expert, replicated per rank).
     Between the two halves the host reads the G x G count matrix, as an
     all-to-all(v) needs its split sizes; every other step stays on the device.
-    `events`: optional list of torch.cuda.Event, recorded after each stage
-    (EP_STAGES)."""
+    `events`: optional list of len(EP_STAGES) + 1 torch.cuda.Event, the
+    first recorded before the first stage and event i + 1 after stage i of
+    EP_STAGES ("counts" is the host's read of the count matrix)."""
 
     def __init__(self, weights: dict, k: int, G: int, path: str = "auto"):
         self.w = weights
@@ -457,9 +458,10 @@ class EPLoopback:
         cap_r = max(max(n_recv), 1)
         recv_rows = torch.empty((G, cap_r, H), dtype=X.dtype, device=dev)
         recv_meta = torch.empty((G, cap_r, RECORD_INTS), dtype=torch.int32, device=dev)
+        mark(3)
         ep_exchange(send_rows, send_off, recv_rows, recv_off, cap_s)
         ep_exchange(send_meta, send_off, recv_meta, recv_off, cap_s)
-        mark(3)
+        mark(4)
         # each rank's experts on what it received
         Yp = torch.empty((G, cap_r, H), dtype=X.dtype, device=dev)
         assign = torch.empty((G, cap_r), dtype=torch.int32, device=dev)
@@ -475,11 +477,11 @@ class EPLoopback:
             grouped_ffn(recv_rows[d, :n], offsets, W1, W3, W2, S1, S3, S2, row_src=row_src, k=1, path=self.path,
                         out=Yp[d, :n])
             local.append((lidx, counts, offsets, row_src))
-        mark(4)
+        mark(5)
         # results back to their sources, in send order
         ret = torch.empty((G, cap_s, H), dtype=X.dtype, device=dev)
         ep_exchange(Yp, recv_off, ret, send_off, cap_s, gather=assign)
-        mark(5)
+        mark(6)
         # combine at the source (+ the shared expert on the rank's own tokens)
         shared = self.w.get("Ws1") is not None
         for r, sl in enumerate(ranks):
@@ -493,7 +495,7 @@ class EPLoopback:
                       for key in ("Ws1", "Ws3", "Ws2", "Ss1", "Ss3", "Ss2")]
                 S = grouped_ffn(X[sl], off, *sw, path=self.path)
             combine(ret[r, :nt * k], send_slot[r, :nt * k], routes[r][2], S, out=Y[sl])
-        mark(6)
+        mark(7)
         if keep:
             self.last = dict(routes=routes, send_off=send_off, send_slot=send_slot, send_rows=send_rows,
                              send_meta=send_meta, recv_off=recv_off, n_recv=n_recv, recv_rows=recv_rows,
@@ -501,7 +503,7 @@ class EPLoopback:
         return Y
 
 
-EP_STAGES = ["route", "dispatch", "exchange", "experts", "return", "combine"]
+EP_STAGES = ["route", "dispatch", "counts", "exchange", "experts", "return", "combine"]
 
 
 # ---------------------------------------------------------------------------
