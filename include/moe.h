@@ -47,10 +47,11 @@
  *    n as E2M1 codes, with [K/32, N] E8M0 scale bytes (2^(e - 127)), one per
  *    32 K rows of a column; the S* pointers then point to these bytes. So W1,
  *    W3 are [E, H/2, F] and W2 [E, F/2, H] bytes, S1, S3 [E, H/32, F] and S2
- *    [E, F/32, H]. The row-streaming path decodes the codes in registers; the
- *    tiled path (TILED, or AUTO at >= 192 rows per expert) first decodes every
- *    expert to bf16 in the workspace (3*E*H*F*2 bytes more, counted by the
- *    workspace-size calls). TILED_A8 is refused.
+ *    [E, F/32, H]. Both kernels decode the codes on chip (the row-streaming
+ *    path in registers, the tiled path after staging codes and scales in LDS)
+ *    and multiply in bf16; the workspace is the bf16 one. Scale code 0 is
+ *    2^-127; code 255 (NaN) makes the outputs that depend on it non-finite.
+ *    TILED_A8 is refused.
  *    H and F must be multiples of 32 and at most 2^20; E <= 1024;
  *    1 <= k <= min(E, 64); moe_route needs T*E < 2^31, moe_permute T*k < 2^31,
  *    moe_forward T <= 65535. Larger sizes return MOE_ERR_UNSUPPORTED (and the

@@ -68,7 +68,6 @@ moe_status check_ffn_dims(int H, int F, moe_dtype w_dt) {
 struct FfnPlan {
     bool tiled;
     bool a8;      // tiled with E4M3 activations (W8A8)
-    bool deq;     // tiled MXFP4: weights decoded to bf16 in the workspace first
     int bm;
     int ksplit1;  // split-K of gate/up (row-streaming path; 1: none)
     int kchunk1;
@@ -84,8 +83,7 @@ bool path_ok(moe_ffn_path path) {
 // whenever it picks the tiled path).
 FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path, bool a8_ok = true) {
     FfnPlan p{};
-    // the tiled kernels take MXFP4 weights decoded to bf16
-    const WType wt = w_dt == MOE_MXFP4 ? W_BF16 : wtype(w_dt);
+    const WType wt = wtype(w_dt);
     const bool can_tile = tiled_gemm_supports(wt, F, H) && tiled_gemm_supports(wt, H, F);
     const bool can_a8 = a8_ok && w_dt == MOE_FP8_E4M3 && tiled_a8_supports(F, H) && tiled_a8_supports(H, F);
     if (path == MOE_PATH_TILED_A8) {
@@ -96,14 +94,13 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path, 
         p.tiled = false;
     } else {
         // the tiled kernels win from about 12-25 rows per group (measured by
-        // token-count sweeps of the Mixtral-, Qwen3- and DeepSeek-shaped layers);
-        // MXFP4 from 128-256 (the row-streaming form reads a quarter of bf16's
-        // bytes, and the tiled form first decodes every expert to bf16)
-        const long long min_rows = w_dt == MOE_MXFP4 ? 192 : 15;
+        // token-count sweeps of the Mixtral-, Qwen3- and DeepSeek-shaped
+        // layers; MXFP4 weights, decoded inside both kernels, cross over at
+        // about the same rows per group)
+        const long long min_rows = 15;
         p.tiled = can_tile && (long long)M >= min_rows * G;
         p.a8 = p.tiled && can_a8;
     }
-    p.deq = p.tiled && w_dt == MOE_MXFP4;
     p.bm = p.a8 ? tiled_a8_bm(M, G) : p.tiled ? tiled_gemm_bm(wt, M, G) : kGemvBM;
     p.ksplit1 = 1;
     p.kchunk1 = H;
@@ -145,7 +142,6 @@ struct FfnWs {
     float *part1;  // gate/up split-K partials [ksplit1][rows][2 hw] (g then u), or null
     uint8_t *xq, *hq;  // W8A8: E4M3 codes of the expert inputs [xrows][H] and of h [rows][hw]
     float *xs, *hs;    // and their per-row 128-column scales
-    void *deq1, *deq3, *deq2;  // MXFP4 decoded to bf16: [groups][H][hw] (W1, W3), [groups][hw][H] (W2)
 };
 
 // Weights of the optional extra group: the always-on shared expert run in
@@ -176,24 +172,7 @@ size_t ffn_ws_carve(Carver &c, FfnWs &w, const FfnPlan &p, int rows, int groups,
         w.hq = static_cast<uint8_t *>(c.take((size_t)rows * hw));
         w.hs = static_cast<float *>(c.take(sizeof(float) * (size_t)rows * (hw / 128)));
     }
-    if (p.deq) {
-        const size_t b = 2 * (size_t)groups * H * hw;
-        w.deq1 = c.take(b);
-        w.deq3 = c.take(b);
-        w.deq2 = c.take(b);
-    }
     return c.used;
-}
-
-// MXFP4 weights of G groups (W1, W3: [G][H/2][F] codes; W2: [G][F/2][H])
-// decoded to bf16 at group offset g0 of the workspace copies (ld F resp. H).
-hipError_t decode_mxfp4(const FfnWs &w, int g0, int G, int H, int F, const void *W1, const void *W3,
-                        const void *W2, const float *S1, const float *S3, const float *S2, hipStream_t s) {
-    const size_t off = 2 * (size_t)g0 * H * F;
-    hipError_t e = launch_mxfp4_to_bf16(W1, S1, G, H, F, static_cast<char *>(w.deq1) + off, s);
-    if (e == hipSuccess) e = launch_mxfp4_to_bf16(W3, S3, G, H, F, static_cast<char *>(w.deq3) + off, s);
-    if (e == hipSuccess) e = launch_mxfp4_to_bf16(W2, S2, G, F, H, static_cast<char *>(w.deq2) + off, s);
-    return e;
 }
 
 GemmProblem base_problem(const FfnWs *ws, int G, int max_tiles, const ExtraGroup &ex, int extra_row0) {
@@ -502,14 +481,7 @@ moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M
     Carver c(ws);
     FfnWs w{};
     ffn_ws_carve(c, w, p, M, G, H, F, act_dt, M);
-    if (p.deq) {
-        MOE_TRY(decode_mxfp4(w, 0, G, H, F, W1, W3, W2, S1, S3, S2, stream));
-        W1 = w.deq1;
-        W3 = w.deq3;
-        W2 = w.deq2;
-        S1 = S3 = S2 = nullptr;
-    }
-    const WType wt = p.deq ? W_BF16 : wtype(w_dt);
+    const WType wt = wtype(w_dt);
     const bool bf = act_dt == MOE_BF16;
     const int max_tiles = (int)max_tiles_for(M, G, p.bm);
     const ExtraGroup none{};
@@ -607,7 +579,6 @@ struct ForwardWs {
     FfnWs ffn;
     FfnPlan plan, plan_s;
     float *part1_s;  // split-K partials of a separate shared-expert gate/up, or null
-    FfnWs deq_s;     // a separate tiled MXFP4 shared expert decoded to bf16 (deq1/3/2 only)
     bool combined;   // shared expert runs as an extra group of the routed launches
     size_t bytes;
 };
@@ -651,13 +622,6 @@ ForwardWs carve_forward(const moe_layer_desc *d, int T, void *base) {
     f.part1_s = nullptr;
     if (separate && !f.plan_s.tiled && f.plan_s.ksplit1 > 1)
         f.part1_s = static_cast<float *>(c.take(sizeof(float) * (size_t)f.plan_s.ksplit1 * T * 2 * d->Fs));
-    f.deq_s = FfnWs{};
-    if (separate && f.plan_s.deq) {
-        const size_t b = 2 * (size_t)d->H * d->Fs;
-        f.deq_s.deq1 = c.take(b);
-        f.deq_s.deq3 = c.take(b);
-        f.deq_s.deq2 = c.take(b);
-    }
     f.bytes = c.used;
     return f;
 }
@@ -691,10 +655,9 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     if (counts_out) f.counts = counts_out;
 
     const int A = T * d->k, H = d->H, F = d->F, E = d->E;
-    const WType wt = f.plan.deq ? W_BF16 : wtype(d->w_dt);
+    const WType wt = wtype(d->w_dt);
     // separate shared-expert launches
-    const WType wts = (d->Fs > 0 && f.plan_s.deq) ? W_BF16 : wtype(d->Fs > 0 ? d->ws_dt : d->w_dt);
-    // expert weights as the GEMMs read them (tiled MXFP4: bf16 copies in the workspace)
+    const WType wts = wtype(d->Fs > 0 ? d->ws_dt : d->w_dt);
     const void *W1 = d->W1, *W3 = d->W3, *W2 = d->W2, *Ws1 = d->Ws1, *Ws3 = d->Ws3, *Ws2 = d->Ws2;
     const float *S1 = d->S1, *S3 = d->S3, *S2 = d->S2, *Ss1 = d->Ss1, *Ss3 = d->Ss3, *Ss2 = d->Ss2;
     const bool bf = d->act_dt == MOE_BF16;
@@ -704,25 +667,6 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     const int hw = d->F > d->Fs ? d->F : d->Fs;
 
     ExtraGroup ex{};
-    if (f.plan.deq) {
-        W1 = f.ffn.deq1;
-        W3 = f.ffn.deq3;
-        W2 = f.ffn.deq2;
-        S1 = S3 = S2 = nullptr;
-        if (f.combined) {  // the shared expert is group E of the decoded copies
-            const size_t off = 2 * (size_t)E * H * F;
-            Ws1 = static_cast<const char *>(W1) + off;
-            Ws3 = static_cast<const char *>(W3) + off;
-            Ws2 = static_cast<const char *>(W2) + off;
-            Ss1 = Ss3 = Ss2 = nullptr;
-        }
-    }
-    if (d->Fs > 0 && !f.combined && f.plan_s.deq) {
-        Ws1 = f.deq_s.deq1;
-        Ws3 = f.deq_s.deq3;
-        Ws2 = f.deq_s.deq2;
-        Ss1 = Ss3 = Ss2 = nullptr;
-    }
     if (f.combined) {
         ex.rows = T;
         ex.W1 = Ws1;
@@ -760,14 +704,6 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     // W8A8: the token rows are quantised once (per-row scales, so the gather
     // in the GEMM's loads picks the same codes as quantising gathered rows)
     if (p.a8) MOE_TRY(launch_quant_rows(X, H, nullptr, 1, T, H, f.ffn.xq, f.ffn.xs, stream));
-    // tiled MXFP4: decode the weights the GEMMs will read (every expert)
-    if (p.deq) {
-        MOE_TRY(decode_mxfp4(f.ffn, 0, E, H, F, d->W1, d->W3, d->W2, d->S1, d->S3, d->S2, stream));
-        if (f.combined)
-            MOE_TRY(decode_mxfp4(f.ffn, E, 1, H, F, d->Ws1, d->Ws3, d->Ws2, d->Ss1, d->Ss3, d->Ss2, stream));
-    }
-    if (d->Fs > 0 && !f.combined && f.plan_s.deq)
-        MOE_TRY(decode_mxfp4(f.deq_s, 0, 1, H, d->Fs, d->Ws1, d->Ws3, d->Ws2, d->Ss1, d->Ss3, d->Ss2, stream));
     MOE_TRY(mark(MOE_EV_SCHEDULE));
     GemmProblem g1 = gate_up_problem(X, f.row_src, d->k, &f.ffn, E, max_tiles, M, H, F, W1, W3, S1, S3, ex, A,
                                      f.ffn.h);

@@ -82,8 +82,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *lds, int *total)
 // W_F32_XBF16: fp32 weights against bf16 token rows (the higher-precision
 // router gate; row-streaming kernel, fp32 output only).
 // W_MXFP4: E2M1 codes packed two K-consecutive values a byte ([K/2][N]) with
-// one E8M0 scale per 32 K rows of a column ([K/32][N] bytes; row-streaming
-// kernel only).
+// one E8M0 scale per 32 K rows of a column ([K/32][N] bytes), decoded to bf16
+// inside the row-streaming and the tiled kernels.
 enum WType { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_F32_XBF16 = 3, W_MXFP4 = 4 };
 
 // Row-streaming grouped GEMM (small rows per group).
@@ -159,10 +159,6 @@ bool tiled_a8_supports(int N, int K);
 // s = amax / 448 (1 when amax is 0), q = E4M3(x / s) rounded to nearest even
 // and saturated. Output row r reads X[row_src[r] / gk] (X[r] if row_src is
 // NULL; row stride ldx elements) -> Q [R][C], S [R][C/128].
-// MXFP4 codes [G][K/2][N] with E8M0 scales [G][K/32][N] -> bf16 [G][K][N]
-// (K % 32 == 0, N % 8 == 0)
-hipError_t launch_mxfp4_to_bf16(const void *codes, const void *scales, int G, int K, int N, void *out,
-                                hipStream_t s);
 hipError_t launch_quant_rows(const void *X, long long ldx, const int32_t *row_src, int gk, int R, int C,
                              uint8_t *Q, float *S, hipStream_t s);
 

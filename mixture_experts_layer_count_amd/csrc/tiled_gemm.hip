@@ -12,19 +12,22 @@ int tiled_gemm_bm(WType wt, long long rows, int groups) {
 }
 
 bool tiled_gemm_supports(WType wt, int N, int K) {
-    if (wt == W_F32 || wt == W_MXFP4) return false;  // MXFP4 reaches these kernels decoded to bf16
+    if (wt == W_F32 || wt == W_F32_XBF16) return false;
     if (N % 8 || K % tiled::kBK || N < 16 || K < tiled::kBK) return false;
+    if (wt == W_MXFP4 && N % 16) return false;  // 16-column byte chunks
     if (wt == W_FP8 && (N % 128 || K % 128)) return false;
     return true;
 }
 
 hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16, int bm,
                              hipStream_t s) {
-    // an extra group needs its own weights (and scales for fp8)
-    if (p.extra_group >= 0 && (!p.Bx0 || (swiglu && !p.Bx1) || (wt == W_FP8 && (!p.Sx0 || (swiglu && !p.Sx1)))))
+    // an extra group needs its own weights (and scales for fp8 and MXFP4)
+    const bool sc = wt == W_FP8 || wt == W_MXFP4;
+    if (p.extra_group >= 0 && (!p.Bx0 || (swiglu && !p.Bx1) || (sc && (!p.Sx0 || (swiglu && !p.Sx1)))))
         return hipErrorInvalidValue;
+    if (sc && (!p.S0 || (swiglu && !p.S1))) return hipErrorInvalidValue;
     if (!out_bf16 || p.ksplit != 1 || !tiled_gemm_supports(wt, p.N, p.K)) return hipErrorInvalidValue;
-    if (!(bm == 128 || (bm == 256 && wt == W_BF16))) return hipErrorInvalidValue;
+    if (!(bm == 128 || (bm == 256 && (wt == W_BF16 || wt == W_MXFP4)))) return hipErrorInvalidValue;
     return bm == 256 ? launch_tiled_bm256(p, wt, swiglu, s) : launch_tiled_bm128(p, wt, swiglu, s);
 }
 

@@ -80,16 +80,25 @@ constexpr int kRingBudget = 144 * 1024;
 template <int WT, int BM, int WR = 2>
 struct Ring {
     static constexpr int threads = 128 * WR;
+    static constexpr int waves = 2 * WR;
     static constexpr bool fp8 = WT == W_FP8;
+    static constexpr bool mx = WT == W_MXFP4;
     static constexpr int a_bytes = BM * kBK * 2;        // 64-byte bf16 rows
-    static constexpr int b_row = fp8 ? 256 : 512;       // one K row of 256 B-columns
-    static constexpr int b_bytes = kBK * b_row;
-    static constexpr int s_bytes = fp8 ? 2 * WR * 256 : 0;  // per-wavefront block-scale copies
+    // one K row of 256 B-columns (bf16 512 B, fp8 256 B); MXFP4: one row of
+    // bytes, each holding two K rows of its column (256 B)
+    static constexpr int b_row = (fp8 || mx) ? 256 : 512;
+    static constexpr int b_bytes = (mx ? kBK / 2 : kBK) * b_row;
+    // fp8: per-wavefront block-scale copies; MXFP4: the step's E8M0 scale row
+    // (one byte per B-column)
+    static constexpr int s_bytes = fp8 ? 2 * WR * 256 : mx ? 256 : 0;
     static constexpr int stage = a_bytes + b_bytes + s_bytes;
     static constexpr int S = (kRingBudget / stage) < 8 ? (kRingBudget / stage) : 8;
     static constexpr int nA = a_bytes / (threads * 16);  // 16-byte copies per thread per tile
-    static constexpr int nB = b_bytes / (threads * 16);
-    static constexpr int per_tile = nA + nB + (fp8 ? 1 : 0);  // vector-memory ops per tile
+    // MXFP4: the B tile is four 1 KB copies; with 8 wavefronts, wavefronts
+    // 0..3 copy it and 4..7 the scale row (one copy each); with 4, each
+    // copies 1 KB of B and then the scale row
+    static constexpr int nB = mx ? 1 : b_bytes / (threads * 16);
+    static constexpr int per_tile = nA + nB + ((fp8 || (mx && waves < 8)) ? 1 : 0);  // vector-memory ops per tile
     static constexpr int mi = BM / (16 * WR);              // 16-row MFMA blocks per wavefront
     static constexpr int ring = S * stage;
 };
@@ -113,6 +122,17 @@ __device__ __forceinline__ int aswz_chunk(int lane) { return (lane & 3) ^ ((lane
 // chunk swizzles of the B tile (16-byte chunks of one K row)
 __device__ __forceinline__ int bswz16(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 __device__ __forceinline__ int bswz8(int k) { return k & 15; }
+// MXFP4 B tile (16 byte rows of 256 B per step): chunk swizzle by byte row.
+// A transposing read pairs two column chunks whose indices differ by 8
+// (gate/up: W1 and W3 halves) or by 4 (down); the swizzle keeps the 8 rows
+// read by each 32-lane half of a wavefront in distinct 16-byte bank groups
+// for that pairing (down: byte-row bits 2 and 3 swapped, so no two rows of a
+// half differ by 4 in the swizzle).
+template <bool SWIGLU>
+__device__ __forceinline__ int mxswz(int kb) {
+    if constexpr (SWIGLU) return kb & 15;
+    else return (kb & 3) | ((kb & 4) << 1) | ((kb & 8) >> 1);
+}
 
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
 template <int N>
@@ -198,11 +218,13 @@ __device__ __forceinline__ bool pick_tile(const GemmProblem &p, int nN, int bm, 
 
 // One fragment set: the A operands of the wavefront's row blocks, the B
 // operands of its 8 column blocks and (fp8) its two block scales.
-template <int MI, bool FP8>
+// RW: transposed reads per block (bf16: 2 x 4 values; fp8: 8 values; MXFP4:
+// raw[p] holds 8 K values of blocks p and p + 4, raw[4] the 8 blocks' scales)
+template <int MI, int RW>
 struct Frags {
     bf16x8 a[MI];
     bf16x8 b[8];                // B operands, formed by land()
-    u32x2 raw[8][FP8 ? 1 : 2];  // transposed reads: 8 fp8, or 2 x 4 bf16, per block
+    u32x2 raw[8][RW];
     float s0, s1;
 };
 
@@ -215,6 +237,9 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     typedef Ring<WT, BM, WR> R;
     constexpr int kT = R::threads;
     constexpr bool FP8 = R::fp8;
+    constexpr bool MX = R::mx;
+    static_assert(!(F32OUT && MX), "fp32 output takes bf16 weights");
+    constexpr int RW = (FP8 || MX) ? 1 : 2;
     constexpr int S = R::S;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<WT, SWIGLU, BM, WR>()];
 
@@ -259,16 +284,39 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     // B: copy q of wavefront w fills K rows of the B tile; each lane fetches
     // the chunk that the swizzle places at its LDS position. Columns past N
     // copy a valid chunk (their results are never stored).
-    typedef typename std::conditional<FP8, uint8_t, uint16_t>::type WE;
+    typedef typename std::conditional<FP8 || MX, uint8_t, uint16_t>::type WE;
     const WE *b_src[R::nB];
     const void *B0 = extra ? p.Bx0 : p.B0;
     const void *B1 = extra ? p.Bx1 : p.B1;
     const long long gofs = extra ? 0 : (long long)g * p.b_stride;
+    // MXFP4 scale row copy: lane -> 4 bytes at 4 lane of the 256-byte row
+    // (16-column chunk lane / 4), unswizzled
+    const uint8_t *mx_s_src = nullptr;
+    if constexpr (MX) {
+        const uint8_t *S0 = reinterpret_cast<const uint8_t *>(extra ? p.Sx0 : p.S0);
+        const uint8_t *S1 = reinterpret_cast<const uint8_t *>(extra ? p.Sx1 : p.S1);
+        const long long sofs = extra ? 0 : (long long)g * p.s_stride;
+        const int c = lane >> 2;
+        const uint8_t *sb;
+        int col;
+        if (SWIGLU) { sb = (c >> 3) ? S1 : S0; col = n0 + 16 * (c & 7); }
+        else { sb = S0; col = n0 + 16 * c; }
+        if (col > p.N - 16) col = p.N - 16;
+        mx_s_src = sb + sofs + col + 4 * (lane & 3);
+    }
 #pragma unroll
     for (int q = 0; q < R::nB; ++q) {
         int k, col;
         const void *base;
-        if constexpr (FP8) {
+        if constexpr (MX) {
+            // byte rows 4 (w % 4) .. +3 of the step: lane -> row lane / 16,
+            // physical chunk lane % 16 holding the chunk the swizzle puts there
+            k = 4 * (w & 3) + (lane >> 4);
+            const int c = (lane & 15) ^ mxswz<SWIGLU>(k);
+            if (SWIGLU) { base = (c >> 3) ? B1 : B0; col = n0 + 16 * (c & 7); }
+            else { base = B0; col = n0 + 16 * c; }
+            if (col > p.N - 16) col = p.N - 16;
+        } else if constexpr (FP8) {
             k = 4 * (w * R::nB + q) + (lane >> 4);
             const int c = (lane & 15) ^ bswz8(k);  // 16 columns per chunk
             if (SWIGLU) { base = (c >> 3) ? B1 : B0; col = n0 + 16 * (c & 7); }
@@ -298,7 +346,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     }
 
     // ---- global -> LDS copies of one K tile: item q of NC ----
-    constexpr int NC = R::nA + R::nB + (FP8 ? 1 : 0);
+    constexpr int NC = R::per_tile;
     auto copy = [&](int q, int kt, int stage) {
         uint8_t *st = lds + stage * R::stage;
         const int k0 = kbase + kt * kBK;
@@ -306,23 +354,48 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
             copy16(a_src[q] + k0, st + (w * R::nA + q) * 1024);
         } else if (q < R::nA + R::nB) {
             const int qb = q - R::nA;
-            copy16(b_src[qb] + (long long)k0 * p.N, st + R::a_bytes + (w * R::nB + qb) * 1024);
+            if constexpr (MX) {
+                // a step is 16 byte rows of B and one row of scales
+                if (R::waves >= 8 && w >= 4) copy4(mx_s_src + (long long)(k0 >> 5) * p.N, st + R::a_bytes + R::b_bytes);
+                else copy16(b_src[0] + (long long)(k0 >> 1) * p.N, st + R::a_bytes + (w & 3) * 1024);
+            } else {
+                copy16(b_src[qb] + (long long)k0 * p.N, st + R::a_bytes + (w * R::nB + qb) * 1024);
+            }
         } else if constexpr (FP8) {
             copy4(s_src + (long long)(k0 >> 7) * (p.N >> 7), st + R::a_bytes + R::b_bytes + w * 256);
+        } else if constexpr (MX) {
+            copy4(mx_s_src + (long long)(k0 >> 5) * p.N, st + R::a_bytes + R::b_bytes);
         }
     };
 
     // ---- fragment reads of one K tile: item r of NR (B blocks, then A row
     // blocks, then the fp8 scales); LDS byte offsets are fixed per lane ----
-    constexpr int NBR = FP8 ? 8 : 16;
+    constexpr int NBR = MX ? 5 : FP8 ? 8 : 16;
     constexpr int NR = NBR + R::mi + (FP8 ? 1 : 0);
     const int a_off = (wr * (BM / WR) + (lane & 15)) * 64 + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
     const int i16 = lane & 15, gq = lane >> 4;
-    auto read = [&](Frags<R::mi, FP8> &f, int r, int stage) {
+    // MXFP4: chunk of the wavefront's column block j in the 256-byte rows
+    auto mx_chunk = [&](int j) { return SWIGLU ? 8 * (j >> 2) + 4 * wc + (j & 3) : 8 * wc + j; };
+    auto read = [&](Frags<R::mi, RW> &f, int r, int stage) {
         const uint8_t *st = lds + stage * R::stage;
         if (r < NBR) {
             const uint32_t bs = lds_addr(st + R::a_bytes);
-            if constexpr (FP8) {
+            if constexpr (MX) {
+                // r < 4: rows 0..3 of the transposed 8 x 16-byte block are byte
+                // rows 4 gq .. +3 of block r's chunk, rows 4..7 the same byte
+                // rows of block r + 4; lane l of a 16-lane group then holds 8 K
+                // values (K 8 gq .. +7) of column l of both blocks. r == 4: the
+                // scale row, row j = block j's chunk: lane l gets the 8 blocks'
+                // scales of its column
+                const int row = i16 >> 1, h = i16 & 1;
+                if (r < 4) {
+                    const int kb = 4 * gq + (row & 3);
+                    const int c = mx_chunk(row < 4 ? r : r + 4);
+                    f.raw[r][0] = ds_tr8(bs + kb * 256 + 16 * (c ^ mxswz<SWIGLU>(kb)) + 8 * h);
+                } else {
+                    f.raw[4][0] = ds_tr8(bs + R::b_bytes + 16 * mx_chunk(row) + 8 * h);
+                }
+            } else if constexpr (FP8) {
                 const int j = r;
                 const int nb = SWIGLU ? 128 * (j >> 2) + 64 * wc + 16 * (j & 3) : 128 * wc + 16 * j;
                 const int k = 8 * gq + (i16 >> 1);
@@ -347,25 +420,46 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     // completes this wavefront's reads of f, hands the transposed reads to
     // the compiler and forms the B operands (fp8: exact E4M3 -> bf16, scale
     // 1; K order kept, byte e of a read being K row e)
-    auto land = [&](Frags<R::mi, FP8> &f) {
+    auto land = [&](Frags<R::mi, RW> &f) {
         wait_lds();
+        if constexpr (MX) {
+            // E2M1 pairs -> bf16 times the column's E8M0 scale (the conversion
+            // takes the scale's exponent field: 2^(code - 127), exact)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+            for (int q = 0; q < 5; ++q) fence(f.raw[q][0]);
 #pragma unroll
-            for (int h = 0; h < (FP8 ? 1 : 2); ++h) fence(f.raw[j][h]);
-            u32x4 v;
-            if constexpr (FP8) {
-                v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][0], 1.0f, false));
-                v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][0], 1.0f, true));
-                v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][1], 1.0f, false));
-                v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][1], 1.0f, true));
-            } else {
-                v[0] = f.raw[j][0][0];
-                v[1] = f.raw[j][0][1];
-                v[2] = f.raw[j][1][0];
-                v[3] = f.raw[j][1][1];
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t word = f.raw[q][0][hh];
+                    const float s = __uint_as_float(((f.raw[4][0][hh] >> (8 * q)) & 0xffu) << 23);
+                    u32x4 v;
+                    v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 0));
+                    v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 1));
+                    v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 2));
+                    v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 3));
+                    f.b[q + 4 * hh] = __builtin_bit_cast(bf16x8, v);
+                }
             }
-            f.b[j] = __builtin_bit_cast(bf16x8, v);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+#pragma unroll
+                for (int h = 0; h < RW; ++h) fence(f.raw[j][h]);
+                u32x4 v;
+                if constexpr (FP8) {
+                    v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][0], 1.0f, false));
+                    v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][0], 1.0f, true));
+                    v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][1], 1.0f, false));
+                    v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.raw[j][0][1], 1.0f, true));
+                } else {
+                    v[0] = f.raw[j][0][0];
+                    v[1] = f.raw[j][0][1];
+                    v[2] = f.raw[j][RW - 1][0];
+                    v[3] = f.raw[j][RW - 1][1];
+                }
+                f.b[j] = __builtin_bit_cast(bf16x8, v);
+            }
         }
     };
 
@@ -381,7 +475,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
 
     // the 8 MFMAs of row block m, kept together as one scheduling group
     // (row blocks m >= ACT, past the group's end, issue none)
-    auto mma_rows = [&](const Frags<R::mi, FP8> &f, int m, auto act) {
+    auto mma_rows = [&](const Frags<R::mi, RW> &f, int m, auto act) {
         constexpr int ACT = decltype(act)::value;
         __builtin_amdgcn_sched_barrier(0);
         if (m < ACT) {
@@ -394,7 +488,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
         __builtin_amdgcn_sched_barrier(0);
     };
     // fp8: add the closed 128-deep K block, times its block scales
-    auto promote = [&](const Frags<R::mi, FP8> &f) {
+    auto promote = [&](const Frags<R::mi, RW> &f) {
         if constexpr (FP8) {
 #pragma unroll
             for (int m = 0; m < R::mi; ++m)
@@ -419,7 +513,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     // tile into stages nobody reads, keeping the counts fixed; the read after
     // the last tile is discarded.
     const int nk = F32OUT ? (min(p.K, kbase + p.kchunk) - kbase) / kBK : p.K / kBK;
-    Frags<R::mi, FP8> fa, fb;
+    Frags<R::mi, RW> fa, fb;
 #pragma unroll
     for (int t = 0; t < S; ++t)
 #pragma unroll

@@ -15,7 +15,9 @@ import mixture_experts_layer_count_amd as moe
 import oracle
 from synth import CONFIGS, MINI_CONFIGS, LayerConfig
 from synth.worked import load_fixture, worked_example_layer
-from _gpu import cover_tokens, rel_err, say, screened_layer, tol_for
+from _gpu import TOL, cover_tokens, rel_err, say, screened_layer, tol_for
+
+TOL_BF16 = TOL["bf16"]
 
 # host threads for the oracle's per-expert work (model-sized layers)
 ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -278,16 +280,99 @@ def test_fp8_block_scales_spread(name, path):
     _check_forward(cfg, d, moe.MoELayer(d, cfg.k, path=path), mirror=path == "tiled_a8")
 
 
+def _mx_layer_extremes(cfg, d):
+    """E8M0 extremes in one layer: a K block of W1 and W3 with scale code 254
+    (2^127; its E2M1 codes limited to magnitudes <= 1.5 so the decoded bf16
+    weights stay finite) facing token values scaled by 2^-124, and a K block
+    with scale code 0 (2^-127) facing token values scaled by 2^126 (so that
+    block's products are of order 1, and decoding 2^-127 as zero would show);
+    W2 has a block of code 0 too."""
+    g = torch.Generator(device="cpu").manual_seed(cfg.seed + 4242)
+    hi, lo = 3, 5  # K blocks (32 rows each) of H
+    X = d["X"].float().cpu()
+    mag = X.abs().clamp(0.25, 1.9) * torch.where(X < 0, -1.0, 1.0)
+    X[:, 32 * hi:32 * hi + 32] = mag[:, 32 * hi:32 * hi + 32] * 2.0 ** -124
+    X[:, 32 * lo:32 * lo + 32] = mag[:, 32 * lo:32 * lo + 32] * 2.0 ** 126
+    d = dict(d)
+    d["X"] = X.to(torch.bfloat16).cuda()
+    for key in ("W1", "W3"):
+        W = d[key].clone()
+        S = d["S" + key[1:]].clone()
+        rows = slice(16 * hi, 16 * hi + 16)  # byte rows of K block hi
+        codes = torch.randint(0, 256, tuple(W[:, rows].shape), generator=g, dtype=torch.uint8).cuda()
+        W[:, rows] = codes & 0xBB  # both nibbles: sign kept, magnitude index <= 3 (0, 0.5, 1, 1.5)
+        S[:, hi] = 254
+        S[:, lo] = 0
+        d[key], d["S" + key[1:]] = W, S
+    S2 = d["S2"].clone()
+    S2[:, 2] = 0
+    d["S2"] = S2
+    return d
+
+
+@pytest.mark.parametrize("path", ["gemv", "tiled"])
+def test_mxfp4_scale_extremes(path):
+    cfg = MINI_CONFIGS["mini_mxfp4_decode"]
+    say(f"[mxfp4 E8M0 extremes] path={path}")
+    d = _mx_layer_extremes(cfg, screened_layer(cfg))
+    L = oracle.Layer(d, cfg.k)
+    _, idx, _ = oracle.route(L.X(), L.Wg(), L.gate_bias(), cfg.k)
+    counts, offsets, row_src, _ = oracle.permute(idx, cfg.E)
+    Xp = L.X()[row_src // cfg.k]
+    ref = oracle.grouped_ffn(Xp, offsets, L.expert)
+    # the code-0 block alone moves the output well beyond the bar
+    d0 = dict(d)
+    d0["X"] = d["X"].clone()
+    d0["X"][:, 160:192] = 0
+    ref0 = oracle.grouped_ffn(oracle.Layer(d0, cfg.k).X()[row_src // cfg.k], offsets, L.expert)
+    assert rel_err(ref0, ref) > 5 * TOL_BF16
+    Yp = moe.grouped_ffn(d["X"], _to_dev_i32(offsets), d["W1"], d["W3"], d["W2"], d["S1"], d["S3"], d["S2"],
+                         row_src=_to_dev_i32(row_src), k=cfg.k, path=path)
+    torch.cuda.synchronize()
+    err = rel_err(Yp, ref)
+    say(f"    max rel err {err:.3e} (tol {TOL_BF16})")
+    assert torch.isfinite(Yp.float()).all()
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("path", ["gemv", "tiled"])
+def test_mxfp4_nan_scale(path):
+    """E8M0 code 255 is NaN: the outputs that depend on it are not finite,
+    and every other output is unchanged."""
+    cfg = MINI_CONFIGS["mini_mxfp4_decode"]
+    say(f"[mxfp4 E8M0 NaN] path={path}")
+    d = dict(screened_layer(cfg))
+    S1 = d["S1"].clone()
+    S1[2, 4, 7] = 255  # expert 2, K block 4, column 7 of W1
+    d["S1"] = S1
+    L = oracle.Layer(d, cfg.k)
+    _, idx, _ = oracle.route(L.X(), L.Wg(), L.gate_bias(), cfg.k)
+    counts, offsets, row_src, _ = oracle.permute(idx, cfg.E)
+    ref = oracle.grouped_ffn(L.X()[row_src // cfg.k], offsets, L.expert)
+    assert counts[2] > 0
+    Yp = moe.grouped_ffn(d["X"], _to_dev_i32(offsets), d["W1"], d["W3"], d["W2"], d["S1"], d["S3"], d["S2"],
+                         row_src=_to_dev_i32(row_src), k=cfg.k, path=path)
+    torch.cuda.synchronize()
+    got = Yp.float().cpu().numpy()
+    bad = ~np.isfinite(ref)
+    assert bad[offsets[2]:offsets[3]].all() and not bad[:offsets[2]].any() and not bad[offsets[3]:].any()
+    np.testing.assert_array_equal(~np.isfinite(got), bad)
+    assert rel_err(got[~bad.any(axis=1)], ref[~bad.any(axis=1)]) <= TOL_BF16
+
+
 # Group sizes on both sides of every tile height (128, 160, 256 rows), with
 # empty groups; the rows are pre-permuted token rows drawn by the generator.
 EDGE_SIZES = {
     "mini_fp8_prefill": [0, 1, 159, 160, 161, 0, 320, 7, 128, 129, 255, 256, 257, 0, 33, 2],
     "mini_bf16_prefill": [1, 255, 256, 257, 0, 513, 129, 127],  # 1538 rows: 256-row tiles
     "mini_fp8_wide": [0, 1, 159, 160, 161, 0, 320, 7, 128, 129, 255, 256, 257, 0, 33, 2],
+    "mini_mxfp4_prefill": [1, 255, 256, 257, 0, 513, 129, 127],  # 1538 rows: 256-row tiles
+    "mini_mxfp4_shared": [0, 1, 127, 128, 129, 0, 40, 7, 3, 64, 2, 0, 33, 2, 5, 1],  # 128-row tiles
 }
 EDGE_CASES = [("mini_fp8_prefill", "tiled_a8"), ("mini_fp8_wide", "tiled_a8"), ("mini_fp8_prefill", "tiled"),
               ("mini_fp8_prefill", "gemv"),
-              ("mini_bf16_prefill", "tiled"), ("mini_bf16_prefill", "gemv")]
+              ("mini_bf16_prefill", "tiled"), ("mini_bf16_prefill", "gemv"),
+              ("mini_mxfp4_prefill", "tiled"), ("mini_mxfp4_shared", "tiled"), ("mini_mxfp4_prefill", "gemv")]
 
 
 @pytest.mark.parametrize("name,path", EDGE_CASES)
