@@ -89,9 +89,9 @@ typedef enum {
 } moe_dtype;
 
 /* Expert-FFN kernel choice. AUTO picks the row-streaming (batched GEMV) path
- * when the experts average fewer than 15 rows (decode) and the LDS-tiled
- * grouped GEMM otherwise (prefill); for FP8 weights the tiled choice is
- * TILED_A8. All give results within the same tolerance of the exact layer;
+ * when the experts average fewer than 15 rows (48 for MXFP4 weights) and the
+ * LDS-tiled grouped GEMM otherwise (prefill); for FP8 weights the tiled choice
+ * is TILED_A8. All give results within the same tolerance of the exact layer;
  * the forced values exist for testing and comparison.
  *  GEMV, TILED: activations stay in act_dt; FP8 weights are decoded exactly
  *    and each 128-deep K block is scaled (W8A16).

@@ -95,9 +95,9 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path, 
     } else {
         // the tiled kernels win from about 12-25 rows per group (measured by
         // token-count sweeps of the Mixtral-, Qwen3- and DeepSeek-shaped
-        // layers; MXFP4 weights, decoded inside both kernels, cross over at
-        // about the same rows per group)
-        const long long min_rows = 15;
+        // layers); with MXFP4 weights the row-streaming kernel reads a quarter
+        // of bf16's bytes, and the sweeps put the crossover at 32-64 rows
+        const long long min_rows = w_dt == MOE_MXFP4 ? 48 : 15;
         p.tiled = can_tile && (long long)M >= min_rows * G;
         p.a8 = p.tiled && can_a8;
     }
