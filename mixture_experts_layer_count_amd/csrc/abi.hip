@@ -167,8 +167,9 @@ size_t ffn_ws_carve(Carver &c, FfnWs &w, const FfnPlan &p, int rows, int groups,
     w.part1 = p.ksplit1 > 1 ? static_cast<float *>(c.take(sizeof(float) * (size_t)p.ksplit1 * rows * 2 * hw))
                             : nullptr;
     if (p.a8) {
+        // codes per input row; scales per GEMM row, transposed [H/128][rows]
         w.xq = static_cast<uint8_t *>(c.take((size_t)xrows * H));
-        w.xs = static_cast<float *>(c.take(sizeof(float) * (size_t)xrows * (H / 128)));
+        w.xs = static_cast<float *>(c.take(sizeof(float) * (size_t)rows * (H / 128)));
         w.hq = static_cast<uint8_t *>(c.take((size_t)rows * hw));
         w.hs = static_cast<float *>(c.take(sizeof(float) * (size_t)rows * (hw / 128)));
     }
@@ -283,12 +284,13 @@ hipError_t run_gate_up_rows(const FfnPlan &p, GemmProblem g, const FfnWs &w, int
     return launch_swiglu_splits(w.part1, g.c_split_stride, p.ksplit1, rows, F, act_dt, h, s);
 }
 
-// W8A8 operands: A holds E4M3 codes of rows of `width` values with scales As.
-void set_a8(GemmProblem &g, const uint8_t *q, const float *sc, int width) {
+// W8A8 operands: A holds E4M3 codes of rows of `width` values; As their
+// scales, transposed, one per GEMM row of `rows` and 128 columns.
+void set_a8(GemmProblem &g, const uint8_t *q, const float *sc, int width, int rows) {
     g.A = q;
     g.lda = width;
     g.As = sc;
-    g.as_ld = width / 128;
+    g.as_ld = rows;
 }
 
 }  // namespace
@@ -489,15 +491,18 @@ moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M
     MOE_TRY(launch_build_tiles(offsets, G, 0, p.bm, w.tiles, w.n_tiles, w.group_tile_start, stream));
     if (p.a8) {
         // E4M3 input rows (gathered here), gate/up writing E4M3 h, down
-        MOE_TRY(launch_quant_rows(Xin, H, row_src, k, M, H, w.xq, w.xs, stream));
+        ScaleLayout sl;  // the gathered rows' scales, transposed
+        sl.ld = M;
+        MOE_TRY(launch_quant_rows(Xin, H, row_src, k, M, H, w.xq, w.xs, stream, &sl));
         GemmProblem g1 = gate_up_problem(nullptr, nullptr, 1, &w, G, max_tiles, M, H, F, W1, W3, S1, S3, none, M,
                                          w.h);
-        set_a8(g1, w.xq, w.xs, H);
+        set_a8(g1, w.xq, w.xs, H, M);
         g1.Cq = w.hq;
         g1.Cqs = w.hs;
+        g1.cqs_ld = M;
         MOE_TRY(run_gemm(p, g1, wt, true, true, stream));
         GemmProblem g2 = down_problem(nullptr, &w, G, max_tiles, M, H, F, W2, S2, none, M, Yp, 0, 1, F);
-        set_a8(g2, w.hq, w.hs, F);
+        set_a8(g2, w.hq, w.hs, F, M);
         MOE_TRY(run_gemm(p, g2, wt, false, true, stream));
         return MOE_OK;
     }
@@ -703,14 +708,24 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
                                    f.ffn.group_tile_start, stream));
     // W8A8: the token rows are quantised once (per-row scales, so the gather
     // in the GEMM's loads picks the same codes as quantising gathered rows)
-    if (p.a8) MOE_TRY(launch_quant_rows(X, H, nullptr, 1, T, H, f.ffn.xq, f.ffn.xs, stream));
+    if (p.a8) {
+        // the scales go, transposed, to the rows of each token's assignments
+        // (and of its shared-expert row), where the GEMM's tiles read them
+        ScaleLayout sl;
+        sl.ld = M;
+        sl.scatter = f.assign_row;
+        sl.k = d->k;
+        sl.extra0 = ex.rows > 0 ? A : -1;
+        MOE_TRY(launch_quant_rows(X, H, nullptr, 1, T, H, f.ffn.xq, f.ffn.xs, stream, &sl));
+    }
     MOE_TRY(mark(MOE_EV_SCHEDULE));
     GemmProblem g1 = gate_up_problem(X, f.row_src, d->k, &f.ffn, E, max_tiles, M, H, F, W1, W3, S1, S3, ex, A,
                                      f.ffn.h);
     if (p.a8) {
-        set_a8(g1, f.ffn.xq, f.ffn.xs, H);
+        set_a8(g1, f.ffn.xq, f.ffn.xs, H, M);
         g1.Cq = f.ffn.hq;  // h leaves the gate/up GEMM as E4M3 codes
         g1.Cqs = f.ffn.hs;
+        g1.cqs_ld = M;
     }
     if (p.tiled) MOE_TRY(run_gemm(p, g1, wt, true, bf, stream));
     else MOE_TRY(run_gate_up_rows(p, g1, f.ffn, M, F, wt, d->act_dt, stream));
@@ -737,7 +752,7 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     if (p.tiled) {
         GemmProblem g2 = down_problem(f.ffn.h, &f.ffn, E, max_tiles, M, H, F, W2, S2, ex, A, f.ffn.part, 0, 1,
                                       F);
-        if (p.a8) set_a8(g2, f.ffn.hq, f.ffn.hs, F);
+        if (p.a8) set_a8(g2, f.ffn.hq, f.ffn.hs, F, M);
         MOE_TRY(run_gemm(p, g2, wt, false, bf, stream));
         MOE_TRY(mark(MOE_EV_DOWN));
         void *Sp = static_cast<char *>(f.ffn.part) + hb * (size_t)A * H;

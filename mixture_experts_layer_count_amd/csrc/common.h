@@ -125,15 +125,17 @@ struct GemmProblem {
     long long c_split_stride;
     int ksplit;
     int kchunk;               // K elements per split (multiple of 32, or 128 for fp8)
-    // fp8 activations (W8A8 tiled path): A holds E4M3 codes and As their
-    // scales, [row][as_ld] with one scale per 128 K, rows mapped as A's
+    // fp8 activations (W8A8 tiled path): A holds E4M3 codes (rows mapped
+    // through row_src as for bf16) and As their scales, one per GEMM row r
+    // and 128 K, transposed: As[kb * as_ld + r], as_ld >= M
     const float *As = nullptr;
-    int as_ld = 0;
+    long long as_ld = 0;
     // W8A8 gate/up: when Cq is set, h is written as E4M3 codes (Cq, ldc bytes
-    // a row) with one fp32 scale per row and 128 columns (Cqs, ldc / 128 a
-    // row) instead of bf16 to C
+    // a row) with one fp32 scale per row and 128 columns, transposed:
+    // Cqs[(column / 128) * cqs_ld + row], instead of bf16 to C
     uint8_t *Cq = nullptr;
     float *Cqs = nullptr;
+    long long cqs_ld = 0;
 };
 
 hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,
@@ -167,8 +169,17 @@ bool tiled_a8_supports(int N, int K);
 // s = amax / 448 (1 when amax is 0), q = E4M3(x / s) rounded to nearest even
 // and saturated. Output row r reads X[row_src[r] / gk] (X[r] if row_src is
 // NULL; row stride ldx elements) -> Q [R][C], S [R][C/128].
+// Scale output layout (NULL: row-major S[R][C/128]): transposed,
+// S[g * ld + row]; with `scatter`, input row r's scales go to rows
+// scatter[r * k + j] (j < k) and, when extra0 >= 0, extra0 + r.
+struct ScaleLayout {
+    long long ld = 0;
+    const int32_t *scatter = nullptr;
+    int k = 0;
+    int extra0 = -1;
+};
 hipError_t launch_quant_rows(const void *X, long long ldx, const int32_t *row_src, int gk, int R, int C,
-                             uint8_t *Q, float *S, hipStream_t s);
+                             uint8_t *Q, float *S, hipStream_t s, const ScaleLayout *sl = nullptr);
 
 // Tile list (group, row0, row_end, 0) for G groups of rows given by offsets
 // plus, when extra_rows > 0, group G = rows [offsets[G], offsets[G] +

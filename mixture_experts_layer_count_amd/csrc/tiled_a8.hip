@@ -188,8 +188,12 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     int sc_off = 0, sc_du = 0, sc_max = 0;
     const int sc_slot = min(w, R::nsa);
     if (w < R::nsa) {
-        sc_src = p.As + src_row(row0 + 64 * w + lane) * p.as_ld;
-        sc_step = 1;
+        // 64 consecutive GEMM rows of the transposed scales (rows past the
+        // tile's end read row0's: never used)
+        int r = row0 + 64 * w + lane;
+        if (r >= row_end) r = row0;
+        sc_src = p.As + r;
+        sc_step = p.as_ld;
     } else {
         const float *S0 = extra ? p.Sx0 : p.S0;
         const float *S1 = extra ? p.Sx1 : p.S1;
@@ -447,7 +451,7 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
                 uint8_t *dst = p.Cq + (long long)row * p.ldc + n0 + 32 * part;
                 *reinterpret_cast<u32x4 *>(dst) = u32x4{qw[0], qw[1], qw[2], qw[3]};
                 *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{qw[4], qw[5], qw[6], qw[7]};
-                if (part == 0) p.Cqs[(long long)row * (p.ldc >> 7) + (n0 >> 7)] = sc;
+                if (part == 0) p.Cqs[(long long)(n0 >> 7) * p.cqs_ld + row] = sc;
             }
             }
             return;
@@ -507,7 +511,8 @@ hipError_t launch_tiled_a8(const GemmProblem &p, bool swiglu, int bm, hipStream_
     if (p.Cq && (!swiglu || !p.Cqs || p.ldc % 128 || tiled::OutA8<true, tiled::kA8WC>::width != 128))
         return hipErrorInvalidValue;
     if (p.extra_group >= 0 && (!p.Bx0 || !p.Sx0 || (swiglu && (!p.Bx1 || !p.Sx1)))) return hipErrorInvalidValue;
-    if (!p.As || p.as_ld < p.K / 128 || p.ksplit != 1 || !tiled_a8_supports(p.N, p.K) || !p.S0 ||
+    if (p.Cq && p.cqs_ld < p.M) return hipErrorInvalidValue;
+    if (!p.As || p.as_ld < p.M || p.ksplit != 1 || !tiled_a8_supports(p.N, p.K) || !p.S0 ||
         (swiglu && (!p.B1 || !p.S1)))
         return hipErrorInvalidValue;
     if (bm == 160)
