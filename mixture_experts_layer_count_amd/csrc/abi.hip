@@ -68,6 +68,7 @@ moe_status check_ffn_dims(int H, int F, moe_dtype w_dt) {
 struct FfnPlan {
     bool tiled;
     bool a8;      // tiled with E4M3 activations (W8A8)
+    bool tail;    // tiled with the tail split (bf16 and MXFP4 weights)
     int bm;
     int ksplit1;  // split-K of gate/up (row-streaming path; 1: none)
     int kchunk1;
@@ -102,6 +103,7 @@ FfnPlan plan_ffn(int M, int G, int H, int F, moe_dtype w_dt, moe_ffn_path path, 
         p.a8 = p.tiled && can_a8;
     }
     p.bm = p.a8 ? tiled_a8_bm(M, G) : p.tiled ? tiled_gemm_bm(wt, M, G) : kGemvBM;
+    p.tail = p.tiled && !p.a8 && (w_dt == MOE_BF16 || w_dt == MOE_MXFP4);
     p.ksplit1 = 1;
     p.kchunk1 = H;
     p.ksplit2 = 1;
@@ -142,6 +144,8 @@ struct FfnWs {
     float *part1;  // gate/up split-K partials [ksplit1][rows][2 hw] (g then u), or null
     uint8_t *xq, *hq;  // W8A8: E4M3 codes of the expert inputs [xrows][H] and of h [rows][hw]
     float *xs, *hs;    // and their per-row 128-column scales
+    float *tail_part;  // tail split: partial sums and counters (or null)
+    int32_t *tail_cnt;
 };
 
 // Weights of the optional extra group: the always-on shared expert run in
@@ -173,6 +177,10 @@ size_t ffn_ws_carve(Carver &c, FfnWs &w, const FfnPlan &p, int rows, int groups,
         w.hq = static_cast<uint8_t *>(c.take((size_t)rows * hw));
         w.hs = static_cast<float *>(c.take(sizeof(float) * (size_t)rows * (hw / 128)));
     }
+    if (p.tail) {
+        w.tail_part = static_cast<float *>(c.take(tiled_tail_bytes(p.bm)));
+        w.tail_cnt = static_cast<int32_t *>(c.take(sizeof(int32_t) * tiled_tail_counters));
+    }
     return c.used;
 }
 
@@ -185,6 +193,8 @@ GemmProblem base_problem(const FfnWs *ws, int G, int max_tiles, const ExtraGroup
     g.max_tiles = max_tiles;
     g.extra_group = ex.rows > 0 ? G : -1;
     g.extra_row0 = extra_row0;
+    g.tail_part = ws ? ws->tail_part : nullptr;
+    g.tail_cnt = ws ? ws->tail_cnt : nullptr;
     return g;
 }
 
@@ -203,6 +213,8 @@ GemmProblem gate_up_problem(const void *X, const int32_t *row_src, int gk, const
     g.K = H;
     g.B0 = W1;
     g.B1 = W3;
+    g.tail_part = nullptr;  // the tail split is for down projections
+    g.tail_cnt = nullptr;
     g.b_stride = (long long)H * F;
     g.S0 = S1;
     g.S1 = S3;
@@ -488,7 +500,8 @@ moe_status moe_grouped_ffn(const void *Xin, const int32_t *row_src, int k, int M
     const int max_tiles = (int)max_tiles_for(M, G, p.bm);
     const ExtraGroup none{};
 
-    MOE_TRY(launch_build_tiles(offsets, G, 0, p.bm, w.tiles, w.n_tiles, w.group_tile_start, stream));
+    MOE_TRY(launch_build_tiles(offsets, G, 0, p.bm, w.tiles, w.n_tiles, w.group_tile_start, stream, w.tail_cnt,
+                               w.tail_cnt ? tiled_tail_counters : 0));
     if (p.a8) {
         // E4M3 input rows (gathered here), gate/up writing E4M3 h, down
         ScaleLayout sl;  // the gathered rows' scales, transposed
@@ -698,6 +711,8 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     tr.group_tile_start = f.ffn.group_tile_start;
     tr.extra_rows = ex.rows;
     tr.bm = p.bm;
+    tr.zero = f.ffn.tail_cnt;
+    tr.n_zero = f.ffn.tail_cnt ? tiled_tail_counters : 0;
     bool tiles_built = false;
     MOE_TRY(launch_permute(f.idx, A, E, f.counts, f.offsets, f.row_src, f.assign_row, f.perm_ws, stream, &tr,
                            &tiles_built));
@@ -705,7 +720,7 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     // 3. expert FFN; with `combined` the shared expert is group E of the same launches
     if (!tiles_built)
         MOE_TRY(launch_build_tiles(f.offsets, E, ex.rows, p.bm, f.ffn.tiles, f.ffn.n_tiles,
-                                   f.ffn.group_tile_start, stream));
+                                   f.ffn.group_tile_start, stream, tr.zero, tr.n_zero));
     // W8A8: the token rows are quantised once (per-row scales, so the gather
     // in the GEMM's loads picks the same codes as quantising gathered rows)
     if (p.a8) {

@@ -136,6 +136,13 @@ struct GemmProblem {
     uint8_t *Cq = nullptr;
     float *Cqs = nullptr;
     long long cqs_ld = 0;
+    // tail split (LDS-tiled plain GEMM with a tile list, bf16 and MXFP4 weights):
+    // the items of each XCD's last, partial round are split over K; the parts
+    // leave fp32 partial sums in tail_part (tiled_tail_bytes(bm) bytes) and
+    // count themselves in tail_cnt (tiled_tail_counters ints, zero at launch
+    // and left zero). NULL: no split.
+    float *tail_part = nullptr;
+    int32_t *tail_cnt = nullptr;
 };
 
 hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,
@@ -157,10 +164,15 @@ hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool o
                              hipStream_t s);
 int tiled_gemm_bm(WType wt, long long rows, int groups);  // rows per tile for this row distribution
 bool tiled_gemm_supports(WType wt, int N, int K);
+// tail-split scratch of the tiled kernel: partial sums for tiles of bm rows,
+// and the number of counters
+size_t tiled_tail_bytes(int bm);
+constexpr int tiled_tail_counters = 256;
 
 // W8A8 variant of the LDS-tiled grouped GEMM (fp8 weights and fp8
-// activations with per-row 128-column scales, p.As): 128-row tiles built with
-// bm = 128; output bf16. Returns hipErrorInvalidValue for unsupported shapes.
+// activations with per-row 128-column scales, p.As transposed by GEMM row):
+// tiles of bm = 128 or 160 rows; output bf16, or E4M3 h with transposed
+// scales (gate/up). Returns hipErrorInvalidValue for unsupported shapes.
 hipError_t launch_tiled_a8(const GemmProblem &p, bool swiglu, int bm, hipStream_t s);
 int tiled_a8_bm(long long rows, int groups);  // rows per W8A8 tile (128 or 160)
 bool tiled_a8_supports(int N, int K);
@@ -186,7 +198,8 @@ hipError_t launch_quant_rows(const void *X, long long ldx, const int32_t *row_sr
 // extra_rows); bm rows per tile. Also the first tile index of every group,
 // [groups + 1] (optional).
 hipError_t launch_build_tiles(const int32_t *offsets, int G, int extra_rows, int bm, int32_t *tiles,
-                              int32_t *n_tiles, int32_t *group_tile_start, hipStream_t s);
+                              int32_t *n_tiles, int32_t *group_tile_start, hipStream_t s,
+                              int32_t *zero = nullptr, int n_zero = 0);
 
 // Router top-k. logits[t,e] = sum_s part[s][t][e] (s ascending) + bias[e] is
 // written to `logits`, then the k best are selected. part may alias logits
@@ -200,6 +213,8 @@ hipError_t launch_topk(const float *part, int nsplit, long long split_stride, co
 struct TileRequest {
     int32_t *tiles = nullptr, *n_tiles = nullptr, *group_tile_start = nullptr;
     int extra_rows = 0, bm = 0;
+    int32_t *zero = nullptr;  // n_zero ints cleared with the list (tail-split counters)
+    int n_zero = 0;
 };
 
 // Permutation (count / scan / scatter) and optional row gather. With `tr`,

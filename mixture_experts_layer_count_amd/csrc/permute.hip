@@ -37,6 +37,7 @@ __device__ __forceinline__ int ceil_log2(int E) {
 // guarantees E + 1 <= 1024 groups. Called by the whole block.
 __device__ __forceinline__ void emit_tiles(const TileRequest &tr, int E, int lo, int hi, int *scan_lds) {
     const int tid = threadIdx.x;
+    for (int i = tid; i < tr.n_zero; i += blockDim.x) tr.zero[i] = 0;
     const int NG = E + (tr.extra_rows > 0 ? 1 : 0);
     const int n = tid < NG ? (hi - lo + tr.bm - 1) / tr.bm : 0;
     int nt = 0;

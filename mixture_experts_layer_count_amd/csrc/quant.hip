@@ -65,15 +65,17 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t *X, long
     }
     if (!ok) return;
     *reinterpret_cast<u32x2 *>(Q + r * C + 128 * gc + 8 * sub) = u32x2{w[0], w[1]};
-    if (sub != 0) return;
-    if (s_ld == 0) {
-        S[r * gpr + gc] = s;
-    } else if (scatter) {
-        for (int j = 0; j < sk; ++j) S[gc * s_ld + scatter[r * sk + j]] = s;
-        if (extra0 >= 0) S[gc * s_ld + extra0 + r] = s;
-    } else {
-        S[gc * s_ld + r] = s;
+    if (scatter) {
+        // lane j < sk writes the copy of assignment j, lane sk the shared row's
+        for (int j = sub; j <= sk; j += 16) {
+            if (j < sk) S[gc * s_ld + scatter[r * sk + j]] = s;
+            else if (extra0 >= 0) S[gc * s_ld + extra0 + r] = s;
+        }
+        return;
     }
+    if (sub != 0) return;
+    if (s_ld == 0) S[r * gpr + gc] = s;
+    else S[gc * s_ld + r] = s;
 }
 
 }  // namespace

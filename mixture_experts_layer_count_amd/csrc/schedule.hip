@@ -13,8 +13,10 @@ namespace {
 
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *offsets, int G, int extra_rows,
                                                            int bm, int32_t *tiles, int32_t *n_tiles,
-                                                           int32_t *group_tile_start) {
+                                                           int32_t *group_tile_start, int32_t *zero,
+                                                           int n_zero) {
     __shared__ int scan_lds[16];
+    for (int i = threadIdx.x; i < n_zero; i += 1024) zero[i] = 0;
     const int NG = G + (extra_rows > 0 ? 1 : 0);
     int carry = 0;
     // groups in rounds of 1024; each thread emits its group's tiles
@@ -48,10 +50,11 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *offset
 }  // namespace
 
 hipError_t launch_build_tiles(const int32_t *offsets, int G, int extra_rows, int bm, int32_t *tiles,
-                              int32_t *n_tiles, int32_t *group_tile_start, hipStream_t s) {
-    if (G < 1 || bm < 1 || extra_rows < 0) return hipErrorInvalidValue;
+                              int32_t *n_tiles, int32_t *group_tile_start, hipStream_t s, int32_t *zero,
+                              int n_zero) {
+    if (G < 1 || bm < 1 || extra_rows < 0 || n_zero < 0 || (n_zero > 0 && !zero)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, G, extra_rows, bm, tiles,
-                       n_tiles, group_tile_start);
+                       n_tiles, group_tile_start, zero, n_zero);
     return hipGetLastError();
 }
 

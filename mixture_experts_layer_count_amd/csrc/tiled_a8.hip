@@ -39,12 +39,13 @@
 //    c ^ swz(k), so that the 16 rows that two 16-lane groups of a
 //    ds_read_b64_tr_b8 read land in distinct banks; an operand is four
 //    transposing reads (8 K rows each) of the lane's column.
-//  * the activation scales of the tile's rows ride along with each stage
-//    (gathered through row_src like the rows), and so do the weight block
-//    scales: one 4-byte copy per wavefront and stage (slots of 64 rows' scales,
-//    then one slot for the two weight scales that every further wavefront
-//    fills with the same copy), which keeps every wavefront's count of copies
-//    per stage equal.
+//  * the activation scales of the tile's rows ride along with each stage, and
+//    so do the weight block scales: one 4-byte copy per wavefront and stage
+//    (slots of 64 rows' scales, then one slot for the two weight scales that
+//    every further wavefront fills with the same copy), which keeps every
+//    wavefront's count of copies per stage equal. The activation scales are
+//    stored transposed and by GEMM row (As[k block][row], written there by
+//    the quantiser), so a slot's 64 rows are one or two cache lines.
 #include "tiled_gemm_kernel.h"
 
 namespace moe {

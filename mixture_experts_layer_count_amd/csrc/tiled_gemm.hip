@@ -11,6 +11,10 @@ int tiled_gemm_bm(WType wt, long long rows, int groups) {
     return (groups > 0 && rows >= 192LL * groups) ? 256 : 128;
 }
 
+static_assert(tiled::kTailSlots == tiled_tail_counters, "one counter per tail slot");
+// one partial tile (bm rows x 256 B-columns, fp32) per tail slot
+size_t tiled_tail_bytes(int bm) { return sizeof(float) * (size_t)tiled::kTailSlots * bm * 256; }
+
 bool tiled_gemm_supports(WType wt, int N, int K) {
     if (wt == W_F32 || wt == W_F32_XBF16) return false;
     if (N % 8 || K % tiled::kBK || N < 16 || K < tiled::kBK) return false;
@@ -28,6 +32,8 @@ hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool o
     if (sc && (!p.S0 || (swiglu && !p.S1))) return hipErrorInvalidValue;
     if (!out_bf16 || p.ksplit != 1 || !tiled_gemm_supports(wt, p.N, p.K)) return hipErrorInvalidValue;
     if (!(bm == 128 || (bm == 256 && (wt == W_BF16 || wt == W_MXFP4)))) return hipErrorInvalidValue;
+    // the tail split: plain GEMMs with bf16 or MXFP4 weights
+    if (p.tail_part && (wt == W_FP8 || swiglu || !p.tail_cnt || !p.tiles)) return hipErrorInvalidValue;
     return bm == 256 ? launch_tiled_bm256(p, wt, swiglu, s) : launch_tiled_bm128(p, wt, swiglu, s);
 }
 

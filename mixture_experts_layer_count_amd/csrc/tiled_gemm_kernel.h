@@ -186,6 +186,7 @@ __device__ __forceinline__ void fence(u32x2 &v) { asm volatile("" : "+v"(v)); }
 // surplus workgroups. Work order: for each group, for each band of gn column
 // tiles, the group's row tiles x the band's column tiles (column fastest).
 // XCD x (workgroup id mod 8) takes the contiguous run [x*per, (x+1)*per).
+__device__ __forceinline__ void tile_of(const GemmProblem &p, int nN, int n_tiles, int id, int &mt, int &nt);
 __device__ __forceinline__ bool pick_tile(const GemmProblem &p, int nN, int bm, int &mt, int &nt) {
     const int n_tiles = p.tiles ? *p.n_tiles : (p.M + bm - 1) / bm;
     const int n_work = n_tiles * nN;
@@ -194,10 +195,62 @@ __device__ __forceinline__ bool pick_tile(const GemmProblem &p, int nN, int bm, 
     if (slot >= per) return false;
     const int id = (blockIdx.x % kXcds) * per + slot;
     if (id >= n_work) return false;
+    tile_of(p, nN, n_tiles, id, mt, nt);
+    return true;
+}
+
+// Tail split. An XCD runs its n items on kBlocksPerXcd CUs; when n is not a
+// multiple of that, the last round holds only tail = n % 32 items and most of
+// the XCD idles through it (the Mixtral-shaped down projection has 2.25
+// rounds: a third of its time at a quarter of the chip). The tail items are
+// then split over K into parts = min(kTailSplit, 32 / tail) parts, one
+// workgroup each, dispatched after the XCD's full rounds (only when the
+// fullest XCDs' last round is at most half full). Part q of item i
+// is workgroup slot full + i parts + q; tail_slot = (XCD, i) names its
+// counter, part_slot = (XCD, i parts + q) its partial buffer.
+constexpr int kTailSplit = 4;
+constexpr int kTailSlots = kXcds * kBlocksPerXcd;  // partial buffers (and counters)
+struct Unit {
+    int mt, nt;
+    int part = 0, parts = 1;
+    int tail_slot = 0, part_slot = 0;
+};
+__device__ __forceinline__ bool pick_unit(const GemmProblem &p, int nN, int bm, int nk, Unit &u) {
+    const int n_tiles = p.tiles ? *p.n_tiles : (p.M + bm - 1) / bm;
+    const int n_work = n_tiles * nN;
+    const int per = (n_work + kXcds - 1) / kXcds;
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int first = xcd * per;
+    const int n = min(per, n_work - first);  // this XCD's items
+    if (n <= 0) return false;
+    const int tail = n % kBlocksPerXcd;
+    const int full = n - tail;
+    // the launch ends with the XCDs that hold `per` items: split only when
+    // their last round is at most half full (else splitting any XCD's tail
+    // only adds partial traffic), and never past one round of parts
+    const int tail_max = per % kBlocksPerXcd;
+    const int split = tail_max == 0 ? 1 : min(kTailSplit, kBlocksPerXcd / tail_max);
+    int item = slot;
+    if (slot >= full) {
+        if (tail == 0) return false;
+        const int parts = split < 2 ? 1 : min(min(split, kBlocksPerXcd / tail), nk);
+        const int v = slot - full;
+        if (v >= tail * parts) return false;
+        item = full + v / parts;
+        u.part = v % parts;
+        u.parts = parts;
+        u.tail_slot = xcd * kBlocksPerXcd + v / parts;
+        u.part_slot = xcd * kBlocksPerXcd + v;
+    }
+    tile_of(p, nN, n_tiles, first + item, u.mt, u.nt);
+    return true;
+}
+
+__device__ __forceinline__ void tile_of(const GemmProblem &p, int nN, int n_tiles, int id, int &mt, int &nt) {
     if (!p.tiles || !p.group_tile_start) {
         mt = id % n_tiles;
         nt = id / n_tiles;
-        return true;
+        return;
     }
     // group holding id: a group's items are [start * nN, next start * nN), so
     // tile id / nN belongs to it, and the tile's record names the group (two
@@ -213,7 +266,6 @@ __device__ __forceinline__ bool pick_tile(const GemmProblem &p, int nN, int bm, 
     const int width = min(gn, nN - band * gn);
     nt = band * gn + q % width;
     mt = t0 + q / width;
-    return true;
 }
 
 // One fragment set: the A operands of the wavefront's row blocks, the B
@@ -243,10 +295,25 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     constexpr int S = R::S;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<WT, SWIGLU, BM, WR>()];
 
-    int mt, nt;
-    if (!pick_tile(p, nN, BM, mt, nt)) return;
+    // K steps of the problem (F32OUT: of this split)
     const int split = F32OUT ? (int)blockIdx.y : 0;
-    const int kbase = F32OUT ? split * p.kchunk : 0;  // first K of this split
+    const int nk_all = F32OUT ? (min(p.K, split * p.kchunk + p.kchunk) - split * p.kchunk) / kBK : p.K / kBK;
+    // the tail split: down projections with bf16 or MXFP4 weights (fp8
+    // weights close 128-deep scale blocks every 4 steps; the gate/up shapes
+    // measured end their launches with well-filled rounds, and carrying the
+    // split code cost them 2-3 %)
+    constexpr bool TAIL = !F32OUT && !FP8 && !SWIGLU;
+    Unit u;
+    if (TAIL && p.tail_part) {
+        if (!pick_unit(p, nN, BM, nk_all, u)) return;
+    } else if (!pick_tile(p, nN, BM, u.mt, u.nt)) {
+        return;
+    }
+    const int mt = u.mt, nt = u.nt;
+    // this workgroup's K steps: [k_first, k_first + nk) (a tail part: its share)
+    const int k_first = nk_all * u.part / u.parts;
+    const int nk = nk_all * (u.part + 1) / u.parts - k_first;
+    const int kbase = (F32OUT ? split * p.kchunk : 0) + k_first * kBK;  // first K of this workgroup
     int g, row0, row_end;
     if (p.tiles) {
         g = p.tiles[4 * mt];
@@ -512,7 +579,6 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     // busy while they issue. Past the last tile the copies repeat the last
     // tile into stages nobody reads, keeping the counts fixed; the read after
     // the last tile is discarded.
-    const int nk = F32OUT ? (min(p.K, kbase + p.kchunk) - kbase) / kBK : p.K / kBK;
     Frags<R::mi, RW> fa, fb;
 #pragma unroll
     for (int t = 0; t < S; ++t)
@@ -572,6 +638,67 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
             }
         return;
     }
+    if (TAIL && u.parts > 1) {
+        // tail part: publish this part's fp32 sums ([accumulator][thread]
+        // 16-byte vectors, coalesced); the last part to finish adds the
+        // parts in part order, all read back from memory, so the sums are the
+        // same whichever part is last, and stores the tile. Its counter is
+        // left at zero.
+        wait_vm<0>();  // the discarded copies land before the LDS is released
+        constexpr int NGR = R::mi * 8;
+        f32x4 *buf = reinterpret_cast<f32x4 *>(p.tail_part);
+        f32x4 *mine = buf + (long long)u.part_slot * NGR * kT;
+#pragma unroll
+        for (int m = 0; m < R::mi; ++m)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mine[(m * 8 + j) * kT + tid] = acc[m][j];
+        // Every wavefront's stores complete, then one thread makes them
+        // visible beyond this XCD's L2 (an agent-scope release: an L2
+        // writeback, so one per workgroup, not one per wavefront) and counts
+        // the part; the last part's one acquire (L1 and L2 invalidate) serves
+        // the whole workgroup, which shares the CU's L1, after the barrier.
+        wait_vm<0>();
+        __syncthreads();
+        // the flag lives in the (now idle) ring: a separate __shared__
+        // variable makes the compiler drain the copies before every LDS read
+        // of the K loop
+        int *tail_last = reinterpret_cast<int *>(lds);
+        if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const bool last = __hip_atomic_fetch_add(p.tail_cnt + u.tail_slot, 1, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT) == u.parts - 1;
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            *tail_last = last;
+        }
+        __syncthreads();
+        if (!*tail_last) return;
+        const f32x4 *part0 = buf + (long long)(u.part_slot - u.part) * NGR * kT;
+        // P parts: the loads of GB accumulators' partials are issued together
+        auto gather = [&](auto pc) {
+            constexpr int P = decltype(pc)::value;
+            constexpr int GB = 2;
+#pragma unroll
+            for (int g0 = 0; g0 < NGR; g0 += GB) {
+                f32x4 v[P][GB];
+#pragma unroll
+                for (int q = 0; q < P; ++q)
+#pragma unroll
+                    for (int i = 0; i < GB; ++i) v[q][i] = part0[((long long)q * NGR + g0 + i) * kT + tid];
+#pragma unroll
+                for (int i = 0; i < GB; ++i) {
+                    f32x4 sum = v[0][i];
+#pragma unroll
+                    for (int q = 1; q < P; ++q) sum += v[q][i];
+                    acc[(g0 + i) >> 3][(g0 + i) & 7] = sum;
+                }
+            }
+        };
+        static_assert(kTailSplit == 4, "part counts 2..4");
+        if (u.parts == 2) gather(std::integral_constant<int, 2>{});
+        else if (u.parts == 3) gather(std::integral_constant<int, 3>{});
+        else gather(std::integral_constant<int, 4>{});
+        if (tid == 0) __hip_atomic_store(p.tail_cnt + u.tail_slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     // ---- epilogue: stage the bf16 tile in LDS, then 16-byte row stores ----
     constexpr int LD = Out<SWIGLU>::ld;
     __syncthreads();  // every wavefront is done with the ring
@@ -611,9 +738,14 @@ inline hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
     const int W = Out<SWIGLU>::width;
     const int nN = (p.N + W - 1) / W;
     const long long mt_cap = p.tiles ? p.max_tiles : (p.M + BM - 1) / BM;
-    long long blocks = mt_cap * nN;
-    blocks = (blocks + kXcds - 1) / kXcds * kXcds;
-    if (blocks <= 0) return hipSuccess;
+    long long per = (mt_cap * nN + kXcds - 1) / kXcds;  // items per XCD, worst case
+    if (per <= 0) return hipSuccess;
+    if (!F32OUT && !SWIGLU && WT != W_FP8 && p.tail_part) {
+        // tail parts: at most kBlocksPerXcd more workgroups per XCD
+        if (!p.tail_cnt || !p.tiles) return hipErrorInvalidValue;
+        per += kBlocksPerXcd;
+    }
+    const long long blocks = per * kXcds;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((tiled_gemm_kernel<WT, SWIGLU, BM, WR, F32OUT>),
                        dim3((unsigned)blocks, F32OUT ? (unsigned)p.ksplit : 1u), dim3(128 * WR), 0, s, p, nN);
