@@ -10,16 +10,20 @@
 // A-tile load and SwiGLU into the gate/up epilogue.
 //
 // Tile: BM rows (256, or 128 when experts hold few rows, always 128 for fp8
-// weights) x 256 B-columns x 32 deep. Wavefronts form a WR x 2 grid, each
-// owning BM/WR rows x 128 B-columns: WR = 2 (4 wavefronts, one per SIMD) for
-// 128-row tiles, WR = 4 (8 wavefronts, two per SIMD, 64 rows each) for
-// 256-row tiles.
+// weights) x 256 B-columns x 32 deep. Wavefronts form a WR x WC grid, each
+// owning BM/WR rows x 256/WC B-columns: 2 x 2 (4 wavefronts, one per SIMD)
+// for 128-row tiles; for 256-row tiles 8 wavefronts, two per SIMD: 2 x 4
+// (128 rows x 64 B-columns each) with bf16 weights, 4 x 2 with MXFP4.
+// The B operands are read with transposing 8-byte reads, about half the LDS
+// bandwidth of the A operands' 16-byte reads, so with bf16 the taller 2 x 4
+// wavefront tiles (twice the A reads, half the B reads of 4 x 2) take less
+// LDS time for the same MFMAs.
 //  * gate/up (SWIGLU): B-columns 0..127 are W1[:, n0:n0+128] and 128..255 are
 //    W3[:, n0:n0+128]; wavefront column wc holds the W1 and W3 accumulators of
-//    output columns n0 + 64 wc .. +63, so h = silu(g) * u is formed in
-//    registers.
+//    output columns n0 + (128/WC) wc .. +128/WC-1, so h = silu(g) * u is
+//    formed in registers.
 //  * down (PLAIN): B-columns are W2[:, n0:n0+256]; wavefront column wc owns
-//    n0 + 128 wc .. +127.
+//    n0 + (256/WC) wc .. +256/WC-1.
 // MI355X mapping:
 //  * operands go global -> LDS with global_load_lds_dwordx4 (no register
 //    staging) into a ring of S stages (S = 4..8, as many as fit in 144 KB), so
@@ -75,12 +79,12 @@ constexpr int kXcds = 8;
 constexpr int kBlocksPerXcd = 32;  // one workgroup per CU (LDS-bound)
 constexpr int kRingBudget = 144 * 1024;
 
-// WR: wavefront rows (2: 4 wavefronts, one per SIMD; 4: 8 wavefronts, two
-// per SIMD, each half the rows and registers)
-template <int WT, int BM, int WR = 2>
+// WR x WC wavefronts: WR rows of BM/WR tile rows, WC columns of 256/WC
+// B-columns (2 x 2: one wavefront per SIMD; 4 x 2 or 2 x 4: two per SIMD)
+template <int WT, int BM, int WR = 2, int WC = 2>
 struct Ring {
-    static constexpr int threads = 128 * WR;
-    static constexpr int waves = 2 * WR;
+    static constexpr int threads = 64 * WR * WC;
+    static constexpr int waves = WR * WC;
     static constexpr bool fp8 = WT == W_FP8;
     static constexpr bool mx = WT == W_MXFP4;
     static constexpr int a_bytes = BM * kBK * 2;        // 64-byte bf16 rows
@@ -90,7 +94,7 @@ struct Ring {
     static constexpr int b_bytes = (mx ? kBK / 2 : kBK) * b_row;
     // fp8: per-wavefront block-scale copies; MXFP4: the step's E8M0 scale row
     // (one byte per B-column)
-    static constexpr int s_bytes = fp8 ? 2 * WR * 256 : mx ? 256 : 0;
+    static constexpr int s_bytes = fp8 ? waves * 256 : mx ? 256 : 0;
     static constexpr int stage = a_bytes + b_bytes + s_bytes;
     static constexpr int S = (kRingBudget / stage) < 8 ? (kRingBudget / stage) : 8;
     static constexpr int nA = a_bytes / (threads * 16);  // 16-byte copies per thread per tile
@@ -100,7 +104,10 @@ struct Ring {
     static constexpr int nB = mx ? 1 : b_bytes / (threads * 16);
     static constexpr int per_tile = nA + nB + ((fp8 || (mx && waves < 8)) ? 1 : 0);  // vector-memory ops per tile
     static constexpr int mi = BM / (16 * WR);              // 16-row MFMA blocks per wavefront
+    static constexpr int nb = 16 / WC;                     // 16-column B blocks per wavefront
     static constexpr int ring = S * stage;
+    // fp8 block scales and the MXFP4 read pairing assume two wavefront columns
+    static_assert(WC == 2 || (!fp8 && !mx), "wavefront grid");
 };
 
 template <bool SWIGLU>
@@ -109,9 +116,10 @@ struct Out {
     static constexpr int ld = width + 8;              // LDS staging row stride (elements)
 };
 
-template <int WT, bool SWIGLU, int BM, int WR>
+template <int WT, bool SWIGLU, int BM, int WR, int WC>
 constexpr int lds_bytes() {
-    return Ring<WT, BM, WR>::ring > BM * Out<SWIGLU>::ld * 2 ? Ring<WT, BM, WR>::ring : BM * Out<SWIGLU>::ld * 2;
+    return Ring<WT, BM, WR, WC>::ring > BM * Out<SWIGLU>::ld * 2 ? Ring<WT, BM, WR, WC>::ring
+                                                                  : BM * Out<SWIGLU>::ld * 2;
 }
 
 // A tile: 64-byte rows, 16-byte chunk c of row r stored at c ^ ((r >> 2) & 3),
@@ -268,32 +276,33 @@ __device__ __forceinline__ void tile_of(const GemmProblem &p, int nN, int n_tile
     mt = t0 + q / width;
 }
 
-// One fragment set: the A operands of the wavefront's row blocks, the B
-// operands of its 8 column blocks and (fp8) its two block scales.
+// One fragment set: the A operands of the wavefront's MI row blocks, the B
+// operands of its NB column blocks and (fp8) its two block scales.
 // RW: transposed reads per block (bf16: 2 x 4 values; fp8: 8 values; MXFP4:
 // raw[p] holds 8 K values of blocks p and p + 4, raw[4] the 8 blocks' scales)
-template <int MI, int RW>
+template <int MI, int NB, int RW>
 struct Frags {
     bf16x8 a[MI];
-    bf16x8 b[8];                // B operands, formed by land()
-    u32x2 raw[8][RW];
+    bf16x8 b[NB];               // B operands, formed by land()
+    u32x2 raw[NB][RW];
     float s0, s1;
 };
 
 // F32OUT (plain GEMM only): fp32 output straight from the accumulators, and
 // split-K: blockIdx.y = split s multiplies K range [s kchunk, (s+1) kchunk)
 // into C + s c_split_stride (every split must be non-empty).
-template <int WT, bool SWIGLU, int BM, int WR, bool F32OUT = false>
-__global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, int nN) {
+template <int WT, bool SWIGLU, int BM, int WR, bool F32OUT = false, int WC = 2>
+__global__ __launch_bounds__(64 * WR * WC, 1) void tiled_gemm_kernel(GemmProblem p, int nN) {
     static_assert(!(F32OUT && SWIGLU), "fp32 output is for the plain GEMM");
-    typedef Ring<WT, BM, WR> R;
+    typedef Ring<WT, BM, WR, WC> R;
+    constexpr int NB = R::nb;
     constexpr int kT = R::threads;
     constexpr bool FP8 = R::fp8;
     constexpr bool MX = R::mx;
     static_assert(!(F32OUT && MX), "fp32 output takes bf16 weights");
     constexpr int RW = (FP8 || MX) ? 1 : 2;
     constexpr int S = R::S;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<WT, SWIGLU, BM, WR>()];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<WT, SWIGLU, BM, WR, WC>()];
 
     // K steps of the problem (F32OUT: of this split)
     const int split = F32OUT ? (int)blockIdx.y : 0;
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     const bool extra = g == p.extra_group;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), wr = w >> 1, wc = w & 1;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), wr = w / WC, wc = w % WC;
     // 16-row blocks of this wavefront that hold rows of the group; a
     // wavefront with none (in a short last tile of an expert) skips its MFMAs
     // (its accumulators stay zero and are never stored)
@@ -437,13 +446,18 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
 
     // ---- fragment reads of one K tile: item r of NR (B blocks, then A row
     // blocks, then the fp8 scales); LDS byte offsets are fixed per lane ----
-    constexpr int NBR = MX ? 5 : FP8 ? 8 : 16;
+    constexpr int NBR = MX ? 5 : FP8 ? NB : 2 * NB;
+    // B-column of the wavefront's column block j: gate/up, blocks 0..NB/2-1
+    // of W1 and the same columns of W3; down, 256/WC consecutive columns
+    auto b_col = [&](int j) {
+        return SWIGLU ? 128 * (j / (NB / 2)) + (128 / WC) * wc + 16 * (j % (NB / 2)) : (256 / WC) * wc + 16 * j;
+    };
     constexpr int NR = NBR + R::mi + (FP8 ? 1 : 0);
     const int a_off = (wr * (BM / WR) + (lane & 15)) * 64 + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
     const int i16 = lane & 15, gq = lane >> 4;
     // MXFP4: chunk of the wavefront's column block j in the 256-byte rows
     auto mx_chunk = [&](int j) { return SWIGLU ? 8 * (j >> 2) + 4 * wc + (j & 3) : 8 * wc + j; };
-    auto read = [&](Frags<R::mi, RW> &f, int r, int stage) {
+    auto read = [&](Frags<R::mi, NB, RW> &f, int r, int stage) {
         const uint8_t *st = lds + stage * R::stage;
         if (r < NBR) {
             const uint32_t bs = lds_addr(st + R::a_bytes);
@@ -464,12 +478,12 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
                 }
             } else if constexpr (FP8) {
                 const int j = r;
-                const int nb = SWIGLU ? 128 * (j >> 2) + 64 * wc + 16 * (j & 3) : 128 * wc + 16 * j;
+                const int nb = b_col(j);
                 const int k = 8 * gq + (i16 >> 1);
                 f.raw[j][0] = ds_tr8(bs + k * 256 + 16 * ((nb >> 4) ^ bswz8(k)) + 8 * (i16 & 1));
             } else {
                 const int j = r >> 1, kh = r & 1;
-                const int nb = SWIGLU ? 128 * (j >> 2) + 64 * wc + 16 * (j & 3) : 128 * wc + 16 * j;
+                const int nb = b_col(j);
                 const int k = 8 * gq + 4 * kh + (i16 >> 2);
                 const int n = nb + 4 * (i16 & 3);
                 f.raw[j][kh] = ds_tr16(bs + k * 512 + 16 * ((n >> 3) ^ bswz16(k)) + 2 * (n & 7));
@@ -487,7 +501,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     // completes this wavefront's reads of f, hands the transposed reads to
     // the compiler and forms the B operands (fp8: exact E4M3 -> bf16, scale
     // 1; K order kept, byte e of a read being K row e)
-    auto land = [&](Frags<R::mi, RW> &f) {
+    auto land = [&](Frags<R::mi, NB, RW> &f) {
         wait_lds();
         if constexpr (MX) {
             // E2M1 pairs -> bf16 times the column's E8M0 scale (the conversion
@@ -510,7 +524,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < NB; ++j) {
 #pragma unroll
                 for (int h = 0; h < RW; ++h) fence(f.raw[j][h]);
                 u32x4 v;
@@ -530,24 +544,24 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
         }
     };
 
-    f32x4 acc[R::mi][8];
-    f32x4 part[FP8 ? R::mi : 1][8];  // fp8: the current 128-deep K block
+    f32x4 acc[R::mi][NB];
+    f32x4 part[FP8 ? R::mi : 1][NB];  // fp8: the current 128-deep K block
 #pragma unroll
     for (int m = 0; m < R::mi; ++m)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NB; ++j) {
             acc[m][j] = f32x4{};
             if constexpr (FP8) part[m][j] = f32x4{};
         }
 
-    // the 8 MFMAs of row block m, kept together as one scheduling group
+    // the NB MFMAs of row block m, kept together as one scheduling group
     // (row blocks m >= ACT, past the group's end, issue none)
-    auto mma_rows = [&](const Frags<R::mi, RW> &f, int m, auto act) {
+    auto mma_rows = [&](const Frags<R::mi, NB, RW> &f, int m, auto act) {
         constexpr int ACT = decltype(act)::value;
         __builtin_amdgcn_sched_barrier(0);
         if (m < ACT) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < NB; ++j) {
                 if constexpr (FP8) part[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[m], f.b[j], part[m][j], 0, 0, 0);
                 else acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
             }
@@ -555,13 +569,13 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
         __builtin_amdgcn_sched_barrier(0);
     };
     // fp8: add the closed 128-deep K block, times its block scales
-    auto promote = [&](const Frags<R::mi, RW> &f) {
+    auto promote = [&](const Frags<R::mi, NB, RW> &f) {
         if constexpr (FP8) {
 #pragma unroll
             for (int m = 0; m < R::mi; ++m)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float s = (SWIGLU && j >= 4) ? f.s1 : f.s0;
+                for (int j = 0; j < NB; ++j) {
+                    const float s = (SWIGLU && j >= NB / 2) ? f.s1 : f.s0;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[m][j][i] += part[m][j][i] * s;
                     part[m][j] = f32x4{};
@@ -579,7 +593,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     // busy while they issue. Past the last tile the copies repeat the last
     // tile into stages nobody reads, keeping the counts fixed; the read after
     // the last tile is discarded.
-    Frags<R::mi, RW> fa, fb;
+    Frags<R::mi, NB, RW> fa, fb;
 #pragma unroll
     for (int t = 0; t < S; ++t)
 #pragma unroll
@@ -617,6 +631,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
         }
     };
     if (nblk == 0) kloop(std::integral_constant<int, 0>{});
+    else if (R::mi >= 8 && nblk <= R::mi / 2) kloop(std::integral_constant<int, R::mi / 2>{});
     else kloop(std::integral_constant<int, R::mi>{});
 
     if constexpr (F32OUT) {
@@ -631,8 +646,8 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
                 const int row = row0 + wr * (BM / WR) + m * 16 + 4 * (lane >> 4) + i;
                 if (row >= row_end) continue;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int col = n0 + 128 * wc + 16 * j + i16;
+                for (int j = 0; j < NB; ++j) {
+                    const int col = n0 + (256 / WC) * wc + 16 * j + i16;
                     if (col < p.N) Cf[(long long)row * p.ldc + col] = acc[m][j][i];
                 }
             }
@@ -645,13 +660,13 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
         // same whichever part is last, and stores the tile. Its counter is
         // left at zero.
         wait_vm<0>();  // the discarded copies land before the LDS is released
-        constexpr int NGR = R::mi * 8;
+        constexpr int NGR = R::mi * NB;
         f32x4 *buf = reinterpret_cast<f32x4 *>(p.tail_part);
         f32x4 *mine = buf + (long long)u.part_slot * NGR * kT;
 #pragma unroll
         for (int m = 0; m < R::mi; ++m)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) mine[(m * 8 + j) * kT + tid] = acc[m][j];
+            for (int j = 0; j < NB; ++j) mine[(m * NB + j) * kT + tid] = acc[m][j];
         // Every wavefront's stores complete, then one thread makes them
         // visible beyond this XCD's L2 (an agent-scope release: an L2
         // writeback, so one per workgroup, not one per wavefront) and counts
@@ -689,7 +704,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
                     f32x4 sum = v[0][i];
 #pragma unroll
                     for (int q = 1; q < P; ++q) sum += v[q][i];
-                    acc[(g0 + i) >> 3][(g0 + i) & 7] = sum;
+                    acc[(g0 + i) / NB][(g0 + i) % NB] = sum;
                 }
             }
         };
@@ -710,14 +725,14 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
             const int r = wr * (BM / WR) + m * 16 + 4 * (lane >> 4) + i;
             if (SWIGLU) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float v = silu_f32(acc[m][j][i]) * acc[m][j + 4][i];
-                    Cs[r * LD + 64 * wc + 16 * j + i16] = __builtin_bit_cast(uint16_t, (__bf16)v);
+                for (int j = 0; j < NB / 2; ++j) {
+                    const float v = silu_f32(acc[m][j][i]) * acc[m][j + NB / 2][i];
+                    Cs[r * LD + (128 / WC) * wc + 16 * j + i16] = __builtin_bit_cast(uint16_t, (__bf16)v);
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    Cs[r * LD + 128 * wc + 16 * j + i16] = __builtin_bit_cast(uint16_t, (__bf16)acc[m][j][i]);
+                for (int j = 0; j < NB; ++j)
+                    Cs[r * LD + (256 / WC) * wc + 16 * j + i16] = __builtin_bit_cast(uint16_t, (__bf16)acc[m][j][i]);
             }
         }
     __syncthreads();
@@ -733,7 +748,7 @@ __global__ __launch_bounds__(128 * WR, 1) void tiled_gemm_kernel(GemmProblem p, 
     }
 }
 
-template <int WT, bool SWIGLU, int BM, int WR = 2, bool F32OUT = false>
+template <int WT, bool SWIGLU, int BM, int WR = 2, bool F32OUT = false, int WC = 2>
 inline hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
     const int W = Out<SWIGLU>::width;
     const int nN = (p.N + W - 1) / W;
@@ -747,14 +762,14 @@ inline hipError_t launch_t(const GemmProblem &p, hipStream_t s) {
     }
     const long long blocks = per * kXcds;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((tiled_gemm_kernel<WT, SWIGLU, BM, WR, F32OUT>),
-                       dim3((unsigned)blocks, F32OUT ? (unsigned)p.ksplit : 1u), dim3(128 * WR), 0, s, p, nN);
+    hipLaunchKernelGGL((tiled_gemm_kernel<WT, SWIGLU, BM, WR, F32OUT, WC>),
+                       dim3((unsigned)blocks, F32OUT ? (unsigned)p.ksplit : 1u), dim3(64 * WR * WC), 0, s, p, nN);
     return hipGetLastError();
 }
 
-template <int WT, int BM, int WR = 2>
+template <int WT, int BM, int WR = 2, int WC = 2>
 inline hipError_t launch_bm(const GemmProblem &p, bool swiglu, hipStream_t s) {
-    return swiglu ? launch_t<WT, true, BM, WR>(p, s) : launch_t<WT, false, BM, WR>(p, s);
+    return swiglu ? launch_t<WT, true, BM, WR, false, WC>(p, s) : launch_t<WT, false, BM, WR, false, WC>(p, s);
 }
 
 }  // namespace tiled
