@@ -255,6 +255,27 @@ def summarize_trace(args) -> int:
     return 0
 
 
+def summarize_counter(args) -> int:
+    """Markdown table of one rocprofv3 counter (a derived one such as
+    MfmaUtil, or a raw one) per libmoe GEMM kernel: its mean per dispatch,
+    from a `--pmc <counter> -f csv` output directory."""
+    means = _pmc_means(args.summarize_counter, args.counter)
+    rows = [(re.sub(r"\(moe::GemmProblem.*$", "", n.replace("(anonymous namespace)::", "")).strip(), v, c)
+            for n, (v, c) in means.items() if "_gemm_kernel" in n or "tiled_a8" in n]
+    if not rows:
+        raise SystemExit(f"no GEMM kernel rows for {args.counter} under {args.summarize_counter}")
+    print(f"# {args.counter} of the expert GEMM kernels: {args.workload}\n")
+    print("Commands, from the repository root R:\n\n```\n" + "\n".join(args.commands) + "\n```\n")
+    print(f"| kernel | dispatches | {args.counter} (mean per dispatch) |\n|---|---:|---:|")
+    for name, v, c in sorted(rows):
+        print(f"| `{name}` | {c} | {v:.2f} |")
+    if args.counter == "MfmaUtil":
+        print("\nMfmaUtil is rocprofv3's derived counter: the summed SQ_VALU_MFMA_BUSY_CYCLES over "
+              "GRBM_GUI_ACTIVE times the SIMD count, in percent (matrix-core busy cycles, whatever the "
+              "clock).")
+    return 0
+
+
 SWEEP_T = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192]
 
 
@@ -570,11 +591,16 @@ def main() -> int:
                     help="time the layer with its experts spread over G ranks on this GPU (loopback all-to-all)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 kernel-trace run (no GPU)")
+    ap.add_argument("--summarize-counter", metavar="DIR",
+                    help="print a markdown table of --counter per GEMM kernel from a rocprofv3 --pmc run (no GPU)")
+    ap.add_argument("--counter", default="MfmaUtil")
     args = ap.parse_args()
     if args.record_traffic:
         return record_traffic(args)
     if args.summarize_trace:
         return summarize_trace(args)
+    if args.summarize_counter:
+        return summarize_counter(args)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the MoE layer here runs on a "
