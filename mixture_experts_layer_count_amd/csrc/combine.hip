@@ -11,7 +11,9 @@
 // token row for bf16 rows (two 16-byte loads per row; 128-thread blocks when
 // a row needs no more), else 8 or, when H is not a multiple of 8, 4; the rows
 // and weights of up to 8 contributions are fetched before their row loads are
-// issued together.
+// issued together. bf16 rows are widened only when used (86 registers a lane
+// instead of 168 for 16 columns, so five wavefronts a SIMD instead of three);
+// split partials (nsplit > 1) come as fp32 only.
 #include "common.h"
 
 namespace moe {
@@ -43,21 +45,30 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t *p, f32x4 v) {
     *reinterpret_cast<u32x2 *>(p) = o;
 }
 
-// V = 4, 8 or 16 consecutive columns per thread (4-column quarters)
+// V = 4, 8 or 16 consecutive columns per thread (4-column quarters). bf16
+// rows of 8 or 16 columns stay packed until they are used: half the
+// registers of widened values, so more rows are in flight per SIMD.
 template <typename InT, int V>
 struct Vec {
-    f32x4 h[V / 4];
+    static constexpr bool packed = (V == 8 || V == 16) && sizeof(InT) == 2;
+    u32x4 raw[packed ? V / 8 : 1];
+    f32x4 h[packed ? 1 : V / 4];
+    __device__ __forceinline__ f32x4 quarter(int i) const {
+        if constexpr (packed) {
+            const u32x4 &v = raw[i >> 1];
+            return (i & 1) ? f32x4{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])}
+                           : f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
+        } else {
+            return h[i];
+        }
+    }
 };
 template <typename InT, int V>
 __device__ __forceinline__ Vec<InT, V> loadv(const InT *p) {
     Vec<InT, V> r;
-    if constexpr ((V == 8 || V == 16) && sizeof(InT) == 2) {
+    if constexpr (Vec<InT, V>::packed) {
 #pragma unroll
-        for (int q = 0; q < V / 8; ++q) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(p + 8 * q);
-            r.h[2 * q] = f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
-            r.h[2 * q + 1] = f32x4{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
-        }
+        for (int q = 0; q < V / 8; ++q) r.raw[q] = *reinterpret_cast<const u32x4 *>(p + 8 * q);
     } else {
 #pragma unroll
         for (int i = 0; i < V / 4; ++i) r.h[i] = load4<InT>(p + 4 * i);
@@ -90,14 +101,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const InT *Yp, const InT *
             }
         }
         Vec<InT, V> y[8];
+        f32x4 ys[8][Vec<InT, V>::packed ? 1 : V / 4];  // split sums (fp32 partials only)
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             if (j0 + u < k) {
                 y[u] = loadv<InT, V>(Yp + row[u] * H + col);
-                for (int s = 1; s < nsplit; ++s) {
-                    const Vec<InT, V> z = loadv<InT, V>(Yp + s * split_stride + row[u] * H + col);
+                if constexpr (!Vec<InT, V>::packed) {
 #pragma unroll
-                    for (int i = 0; i < V / 4; ++i) y[u].h[i] += z.h[i];
+                    for (int i = 0; i < V / 4; ++i) ys[u][i] = y[u].h[i];
+                    for (int s = 1; s < nsplit; ++s) {
+                        const Vec<InT, V> z = loadv<InT, V>(Yp + s * split_stride + row[u] * H + col);
+#pragma unroll
+                        for (int i = 0; i < V / 4; ++i) ys[u][i] += z.h[i];
+                    }
                 }
             }
         }
@@ -105,21 +121,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const InT *Yp, const InT *
         for (int u = 0; u < 8; ++u) {
             if (j0 + u < k) {
 #pragma unroll
-                for (int i = 0; i < V / 4; ++i)
+                for (int i = 0; i < V / 4; ++i) {
+                    f32x4 v;
+                    if constexpr (Vec<InT, V>::packed) v = y[u].quarter(i);
+                    else v = ys[u][i];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[i][c] = fmaf(wj[u], y[u].h[i][c], acc[i][c]);
+                    for (int c = 0; c < 4; ++c) acc[i][c] = fmaf(wj[u], v[c], acc[i][c]);
+                }
             }
         }
     }
     if (S) {
-        Vec<InT, V> y = loadv<InT, V>(S + (long long)t * H + col);
-        for (int s = 1; s < nsplit_s; ++s) {
-            const Vec<InT, V> z = loadv<InT, V>(S + s * split_stride + (long long)t * H + col);
+        const Vec<InT, V> y = loadv<InT, V>(S + (long long)t * H + col);
 #pragma unroll
-            for (int i = 0; i < V / 4; ++i) y.h[i] += z.h[i];
+        for (int i = 0; i < V / 4; ++i) {
+            f32x4 v = y.quarter(i);
+            if constexpr (!Vec<InT, V>::packed)
+                for (int s = 1; s < nsplit_s; ++s) v += load4<InT>(S + s * split_stride + (long long)t * H + col + 4 * i);
+            acc[i] += v;
         }
-#pragma unroll
-        for (int i = 0; i < V / 4; ++i) acc[i] += y.h[i];
     }
 #pragma unroll
     for (int i = 0; i < V / 4; ++i) store4<OutT>(Y + (long long)t * H + col + 4 * i, acc[i]);
@@ -181,6 +201,8 @@ hipError_t launch_combine(const void *Yp, const void *S, long long split_stride,
                           int k, int H, moe_dtype out_dt, void *Y, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     if (H % 4 || nsplit < 1 || nsplit_s < 1 || T > 65535) return hipErrorInvalidValue;
+    // split partials are fp32 (bf16 rows come whole from the tiled kernels)
+    if (in_dt == MOE_BF16 && (nsplit != 1 || nsplit_s != 1)) return hipErrorInvalidValue;
     // 16 bf16 columns a thread (two 16-byte loads per row) when H allows
     const bool v16 = H % 16 == 0 && in_dt == MOE_BF16;
     const bool v8 = H % 8 == 0;
