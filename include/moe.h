@@ -355,6 +355,28 @@ moe_status moe_forward_noalloc(const moe_layer_desc *desc, const void *X, int T,
                                float *logits_out, int32_t *topk_idx_out, float *topk_w_out,
                                int32_t *counts_out, hipEvent_t const *events);
 
+/* ---------------------------------------------------------------------------
+ * Bounds-checked debug build (libmoe_debug.so: every source compiled with
+ * -DMOE_BOUNDS_CHECK). Its kernels check the indices they address memory
+ * with -- tile records, gathered and permuted rows, combine rows, scale rows,
+ * tail-split slots, exchange rows -- and on a failed check record a bit
+ * (below) instead of trapping, and keep the access in bounds (results are
+ * then wrong, but nothing faults). Same arguments and results as the release
+ * library otherwise.
+ * moe_debug_bounds(): waits for the current device, returns the union of the
+ * bits recorded since the previous call and clears them; ~0u if a HIP call
+ * failed. The release library returns 0 and touches no device.
+ * ------------------------------------------------------------------------- */
+#define MOE_BOUNDS_TILE 1u          /* tile record: group, first or end row */
+#define MOE_BOUNDS_A_ROW 2u         /* gathered input row of a GEMM */
+#define MOE_BOUNDS_SCALE_ROW 4u     /* activation-scale row of the W8A8 GEMM */
+#define MOE_BOUNDS_TAIL_SLOT 8u     /* tail-split partial slot or counter */
+#define MOE_BOUNDS_PERM_ROW 16u     /* permuted row of an assignment */
+#define MOE_BOUNDS_COMBINE_ROW 32u  /* Yp row read by combine */
+#define MOE_BOUNDS_QUANT_ROW 64u    /* scale row written by the quantiser */
+#define MOE_BOUNDS_EP_ROW 128u      /* row of an expert-parallel exchange */
+unsigned moe_debug_bounds(void);
+
 #ifdef __cplusplus
 }
 #endif

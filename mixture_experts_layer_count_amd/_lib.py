@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
  MOE_ERR_SCRATCH_LIMIT) = range(6)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 PATHS = {"auto": 0, "gemv": 1, "tiled": 2, "tiled_a8": 3}
+# bits of moe_debug_bounds() (the bounds-checked build)
+(MOE_BOUNDS_TILE, MOE_BOUNDS_A_ROW, MOE_BOUNDS_SCALE_ROW, MOE_BOUNDS_TAIL_SLOT, MOE_BOUNDS_PERM_ROW,
+ MOE_BOUNDS_COMBINE_ROW, MOE_BOUNDS_QUANT_ROW, MOE_BOUNDS_EP_ROW) = (1 << i for i in range(8))
 
 # Every function include/moe.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -44,6 +47,7 @@ SIGNATURES = {
                              _I, _P]),
     "moe_ep_local_experts": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "moe_forward_noalloc": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_debug_bounds": (ctypes.c_uint, []),
 }
 
 
@@ -61,21 +65,47 @@ class LayerDesc(ctypes.Structure):
     ]
 
 
+# the bounds-checked debug build of the same sources (-DMOE_BOUNDS_CHECK)
+DEBUG_LIB_PATH = os.path.join(PKG, "libmoe_debug.so")
+
 _lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """A handle on a built libmoe (release or debug) with every signature set."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m mixture_experts_layer_count_amd.build`")
+    h = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(h, name)
+        fn.restype = res
+        fn.argtypes = args
+    return h
 
 
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_count_amd.build`")
-        h = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(h, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = h
+        _lib = load(LIB_PATH)
     return _lib
+
+
+class use_library:
+    """Context manager: route every call of this binding to another libmoe
+    handle (the bounds-checked build) inside the block."""
+
+    def __init__(self, handle: ctypes.CDLL):
+        self.handle, self.saved = handle, None
+
+    def __enter__(self):
+        global _lib
+        self.saved, _lib = lib(), self.handle
+        return self.handle
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
 
 
 class MoEError(RuntimeError):

@@ -209,6 +209,7 @@ GemmProblem gate_up_problem(const void *X, const int32_t *row_src, int gk, const
     g.gk = gk;
     g.lda = H;
     g.M = M;
+    g.a_rows = row_src ? 0 : M;  // gathered: the caller knows X's rows
     g.N = F;
     g.K = H;
     g.B0 = W1;
@@ -241,6 +242,7 @@ GemmProblem down_problem(const void *h, const FfnWs *ws, int G, int max_tiles, i
     g.gk = 1;
     g.lda = F;
     g.M = M;
+    g.a_rows = M;
     g.N = H;
     g.K = F;
     g.B0 = W2;
@@ -308,6 +310,17 @@ void set_a8(GemmProblem &g, const uint8_t *q, const float *sc, int width, int ro
 }  // namespace
 
 extern "C" {
+
+unsigned moe_debug_bounds(void) {
+#ifdef MOE_BOUNDS_CHECK
+    if (hipDeviceSynchronize() != hipSuccess) return ~0u;
+    return bounds_take_tiled128() | bounds_take_tiled256() | bounds_take_tiledf32() | bounds_take_a8() |
+           bounds_take_stream() | bounds_take_permute() | bounds_take_combine() | bounds_take_quant() |
+           bounds_take_ep();
+#else
+    return 0u;
+#endif
+}
 
 const char *moe_status_string(moe_status s) {
     switch (s) {
@@ -453,7 +466,8 @@ moe_status moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *co
     const size_t need = permute_ws_bytes(T * k, E);
     if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     MOE_TRY(launch_permute(topk_idx, T * k, E, counts, offsets, row_src, assign_row, ws, stream));
-    if (Xp) MOE_TRY(launch_gather_rows(X, (int)dt_size(x_dt), H, row_src, k, T * k, Xp, stream));
+    // rows past offsets[E] (assignments of experts outside [0, E)) stay unset
+    if (Xp) MOE_TRY(launch_gather_rows(X, (int)dt_size(x_dt), H, row_src, k, T * k, Xp, stream, offsets + E));
     return MOE_OK;
 }
 
@@ -554,7 +568,8 @@ moe_status moe_combine(const void *Yp, const int32_t *assign_row, const float *t
     if (H % 4 || T > 65535) return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
     if (!Yp || !assign_row || !topk_w || !Y) return MOE_ERR_INVALID_ARG;
-    return hip_status(launch_combine(Yp, S, 0, 1, 1, act_dt, assign_row, topk_w, T, k, H, act_dt, Y, stream));
+    return hip_status(
+        launch_combine(Yp, S, 0, 1, 1, act_dt, assign_row, topk_w, T, k, H, act_dt, Y, stream, (long long)T * k));
 }
 
 // ---------------------------------------------------------------------------
@@ -736,6 +751,7 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     MOE_TRY(mark(MOE_EV_SCHEDULE));
     GemmProblem g1 = gate_up_problem(X, f.row_src, d->k, &f.ffn, E, max_tiles, M, H, F, W1, W3, S1, S3, ex, A,
                                      f.ffn.h);
+    g1.a_rows = T;  // token rows (bf16) or their E4M3 codes
     if (p.a8) {
         set_a8(g1, f.ffn.xq, f.ffn.xs, H, M);
         g1.Cq = f.ffn.hq;  // h leaves the gate/up GEMM as E4M3 codes
@@ -798,7 +814,7 @@ moe_status moe_forward(const moe_layer_desc *d, const void *X, int T, void *Y, v
     MOE_TRY(mark(MOE_EV_SHARED_DOWN));
     // 4. combine
     MOE_TRY(launch_combine(f.ffn.part, S, split_stride, nsplit, nsplit_s, yp_dt, f.assign_row, f.w, T, d->k, H,
-                           d->act_dt, Y, stream));
+                           d->act_dt, Y, stream, A));
     MOE_TRY(mark(MOE_EV_COMBINE));
     return MOE_OK;
 }

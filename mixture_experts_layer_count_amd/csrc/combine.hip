@@ -17,6 +17,8 @@
 #include "common.h"
 
 namespace moe {
+
+MOE_BOUNDS_FILE(combine)
 namespace {
 
 template <typename InT>
@@ -80,7 +82,7 @@ template <typename InT, typename OutT, int V>
 __global__ __launch_bounds__(256) void combine_kernel(const InT *Yp, const InT *S,
                                                       long long split_stride, int nsplit, int nsplit_s,
                                                       const int32_t *assign_row, const float *w,
-                                                      int T, int k, int H, OutT *Y) {
+                                                      int T, int k, int H, OutT *Y, long long yp_rows) {
     const int t = blockIdx.y;
     const int col = (blockIdx.x * blockDim.x + threadIdx.x) * V;
     if (t >= T || col >= H) return;
@@ -97,6 +99,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const InT *Yp, const InT *
             if (j0 + u < k) {
                 const long long a = (long long)t * k + j0 + u;
                 row[u] = assign_row[a];
+                if (MOE_BOUNDS_FAIL(row[u] >= 0 && (yp_rows <= 0 || row[u] < yp_rows), BOUNDS_COMBINE_ROW))
+                    row[u] = 0;
                 wj[u] = w[a];
             }
         }
@@ -198,7 +202,7 @@ hipError_t launch_swiglu_splits(const float *part, long long split_stride, int n
 
 hipError_t launch_combine(const void *Yp, const void *S, long long split_stride, int nsplit, int nsplit_s,
                           moe_dtype in_dt, const int32_t *assign_row, const float *w, int T,
-                          int k, int H, moe_dtype out_dt, void *Y, hipStream_t s) {
+                          int k, int H, moe_dtype out_dt, void *Y, hipStream_t s, long long yp_rows) {
     if (T <= 0) return hipSuccess;
     if (H % 4 || nsplit < 1 || nsplit_s < 1 || T > 65535) return hipErrorInvalidValue;
     // split partials are fp32 (bf16 rows come whole from the tiled kernels)
@@ -214,13 +218,13 @@ hipError_t launch_combine(const void *Yp, const void *S, long long split_stride,
     do {                                                                                                  \
         if (v16)                                                                                          \
             hipLaunchKernelGGL((combine_kernel<IT, OT, 16>), grid, block, 0, s, (const IT *)Yp,            \
-                               (const IT *)S, split_stride, nsplit, nsplit_s, assign_row, w, T, k, H, (OT *)Y); \
+                               (const IT *)S, split_stride, nsplit, nsplit_s, assign_row, w, T, k, H, (OT *)Y, yp_rows); \
         else if (v8)                                                                                      \
             hipLaunchKernelGGL((combine_kernel<IT, OT, 8>), grid, block, 0, s, (const IT *)Yp,             \
-                               (const IT *)S, split_stride, nsplit, nsplit_s, assign_row, w, T, k, H, (OT *)Y);    \
+                               (const IT *)S, split_stride, nsplit, nsplit_s, assign_row, w, T, k, H, (OT *)Y, yp_rows);    \
         else                                                                                              \
             hipLaunchKernelGGL((combine_kernel<IT, OT, 4>), grid, block, 0, s, (const IT *)Yp,             \
-                               (const IT *)S, split_stride, nsplit, nsplit_s, assign_row, w, T, k, H, (OT *)Y);    \
+                               (const IT *)S, split_stride, nsplit, nsplit_s, assign_row, w, T, k, H, (OT *)Y, yp_rows);    \
     } while (0)
     if (in_dt == MOE_F32 && out_dt == MOE_F32) MOE_COMBINE(float, float);
     else if (in_dt == MOE_F32 && out_dt == MOE_BF16) MOE_COMBINE(float, uint16_t);

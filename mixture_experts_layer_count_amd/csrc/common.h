@@ -10,6 +10,54 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
+// Bounds-checked debug build (-DMOE_BOUNDS_CHECK, libmoe_debug.so). Kernels
+// check the indices they address memory with; a failed check sets its bit in
+// a flag of the source file (atomicOr, no trap) and the access is clamped in
+// bounds. moe_debug_bounds() returns the union of every file's flags and
+// clears them. In the release build the checks compile to nothing.
+// ---------------------------------------------------------------------------
+enum BoundsBit : unsigned {
+    BOUNDS_TILE = 1u,        // tile record: group, first and end row
+    BOUNDS_A_ROW = 2u,       // gathered input row of a GEMM
+    BOUNDS_SCALE_ROW = 4u,   // activation-scale row of the W8A8 GEMM
+    BOUNDS_TAIL_SLOT = 8u,   // tail-split partial slot or counter
+    BOUNDS_PERM_ROW = 16u,   // permuted row of an assignment
+    BOUNDS_COMBINE_ROW = 32u,  // Yp row read by combine
+    BOUNDS_QUANT_ROW = 64u,  // scale row written by the quantiser
+    BOUNDS_EP_ROW = 128u,    // row of an expert-parallel exchange
+};
+#ifdef MOE_BOUNDS_CHECK
+namespace {
+__device__ unsigned bounds_flag;  // this source file's failed checks
+}
+#define MOE_BOUNDS_FILE(tag)                                                        \
+    unsigned bounds_take_##tag() {                                                  \
+        unsigned v = 0;                                                             \
+        if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(bounds_flag), sizeof(v)) != hipSuccess) \
+            return ~0u;                                                             \
+        const unsigned z = 0;                                                       \
+        if (hipMemcpyToSymbol(HIP_SYMBOL(bounds_flag), &z, sizeof(z)) != hipSuccess)  \
+            return ~0u;                                                             \
+        return v;                                                                   \
+    }
+// true when cond fails (the caller then clamps the index)
+#define MOE_BOUNDS_FAIL(cond, bit) (!(cond) ? (atomicOr(&bounds_flag, (unsigned)(bit)), true) : false)
+#else
+#define MOE_BOUNDS_FILE(tag) \
+    unsigned bounds_take_##tag() { return 0u; }
+#define MOE_BOUNDS_FAIL(cond, bit) false
+#endif
+unsigned bounds_take_tiled128();
+unsigned bounds_take_tiled256();
+unsigned bounds_take_tiledf32();
+unsigned bounds_take_a8();
+unsigned bounds_take_stream();
+unsigned bounds_take_permute();
+unsigned bounds_take_combine();
+unsigned bounds_take_quant();
+unsigned bounds_take_ep();
+
+// ---------------------------------------------------------------------------
 // Vector types for MFMA operands and wide loads
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -143,6 +191,8 @@ struct GemmProblem {
     // and left zero). NULL: no split.
     float *tail_part = nullptr;
     int32_t *tail_cnt = nullptr;
+    // rows of A (the bounds-checked build's checks only; 0: not known)
+    long long a_rows = 0;
 };
 
 hipError_t launch_stream_gemm(const GemmProblem &p, WType wt, bool swiglu, bool out_bf16,
@@ -224,15 +274,16 @@ size_t permute_ws_bytes(int A, int E);
 hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int32_t *offsets,
                           int32_t *row_src, int32_t *assign_row, void *ws, hipStream_t s,
                           const TileRequest *tr = nullptr, bool *tiles_built = nullptr);
+// Xp[r] = X[row_src[r] / gk] for r < A, or r < *n_rows when n_rows is given
 hipError_t launch_gather_rows(const void *X, int elem_bytes, int H, const int32_t *row_src,
-                              int gk, int A, void *Xp, hipStream_t s);
+                              int gk, int A, void *Xp, hipStream_t s, const int32_t *n_rows = nullptr);
 
 // Combine: Y[t] = sum_j w[t,j] * sum_{s<nsplit} Yp_s[assign_row[t*k+j]]
 //               (+ sum_{s<nsplit_s} S_s[t]).
 // in_dt/out_dt: MOE_F32 or MOE_BF16.
 hipError_t launch_combine(const void *Yp, const void *S, long long split_stride, int nsplit, int nsplit_s,
                           moe_dtype in_dt, const int32_t *assign_row, const float *w, int T,
-                          int k, int H, moe_dtype out_dt, void *Y, hipStream_t s);
+                          int k, int H, moe_dtype out_dt, void *Y, hipStream_t s, long long yp_rows = 0);
 
 // Sum fp32 split partials [nsplit][M][N] into out [M][N] (f32 or bf16).
 hipError_t launch_reduce_splits(const float *part, long long split_stride, int nsplit, int M,

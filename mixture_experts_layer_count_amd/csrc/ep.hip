@@ -31,6 +31,8 @@
 #include "common.h"
 
 namespace moe {
+
+MOE_BOUNDS_FILE(ep)
 namespace {
 
 // key[a] = owner rank of the assignment's expert (-1: expert out of range,
@@ -91,10 +93,14 @@ __global__ __launch_bounds__(256) void ep_exchange_kernel(int G, const uint8_t *
     const uint4 *src_base = reinterpret_cast<const uint4 *>(in + s * in_stride);
     uint4 *dst_base = reinterpret_cast<uint4 *>(out + d * out_stride);
     const int32_t *gth = gather ? gather + s * gather_stride : nullptr;
+    // rows a rank holds (the bounds-checked build's checks; 0: not known)
+    const long long in_rows = in_stride / (16LL * row_vecs), out_rows = out_stride / (16LL * row_vecs);
     for (int v = threadIdx.x; v < nr * row_vecs; v += 256) {
         const int i = v / row_vecs, c = v - i * row_vecs;
         const long long j = lo + r0 + i;
-        const long long sr = gth ? gth[j] : j;
+        long long sr = gth ? gth[j] : j;
+        if (MOE_BOUNDS_FAIL(sr >= 0 && (in_rows <= 0 || sr < in_rows), BOUNDS_EP_ROW)) sr = 0;
+        if (MOE_BOUNDS_FAIL(out_rows <= 0 || dst0 + i < out_rows, BOUNDS_EP_ROW)) continue;
         dst_base[(long long)(dst0 + i) * row_vecs + c] = src_base[sr * row_vecs + c];
     }
 }

@@ -21,6 +21,8 @@
 #include "common.h"
 
 namespace moe {
+
+MOE_BOUNDS_FILE(permute)
 namespace {
 
 constexpr int kChunk = 1024;
@@ -115,8 +117,10 @@ __global__ __launch_bounds__(kChunk) void permute_rank_kernel(
         __syncthreads();
         if (e >= 0) {
             const int row = off_lds[e] + r_in_chunk;
-            row_src[row] = a;
-            assign_row[a] = row;
+            if (!MOE_BOUNDS_FAIL(row >= 0 && row < A, BOUNDS_PERM_ROW)) {
+                row_src[row] = a;
+                assign_row[a] = row;
+            }
         }
         if (tr.tiles) {
             // the extra group's rows follow the routed ones
@@ -203,16 +207,22 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t *idx
     const int e = idx[a];
     if (e < 0 || e >= E) return;
     const int row = chunk_base[(long long)(a / kChunk) * E + e] + rank[a];
+    if (MOE_BOUNDS_FAIL(row >= 0 && row < A, BOUNDS_PERM_ROW)) return;
     row_src[row] = a;
     assign_row[a] = row;
 }
 
-// Xp[r] = X[row_src[r] / gk]; one block per row, 16-byte vectors.
+// Xp[r] = X[row_src[r] / gk] for the rows the permutation wrote (r <
+// *n_rows when given: assignments of experts outside [0, E) get no row); one
+// block per row, 16-byte vectors.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *X, int row_vecs,
                                                           const int32_t *row_src, int gk,
+                                                          const int32_t *n_rows, long long x_rows,
                                                           uint4 *Xp) {
     const int r = blockIdx.x;
-    const long long src = row_src[r] / gk;
+    if (n_rows && r >= *n_rows) return;
+    long long src = row_src[r] / gk;
+    if (MOE_BOUNDS_FAIL(src >= 0 && src < x_rows, BOUNDS_A_ROW)) src = 0;
     for (int i = threadIdx.x; i < row_vecs; i += 256)
         Xp[(long long)r * row_vecs + i] = X[src * row_vecs + i];
 }
@@ -269,13 +279,13 @@ hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int
 }
 
 hipError_t launch_gather_rows(const void *X, int elem_bytes, int H, const int32_t *row_src,
-                              int gk, int A, void *Xp, hipStream_t s) {
+                              int gk, int A, void *Xp, hipStream_t s, const int32_t *n_rows) {
     if (A <= 0) return hipSuccess;
     const long long row_bytes = (long long)H * elem_bytes;
-    if (row_bytes % 16) return hipErrorInvalidValue;
+    if (row_bytes % 16 || gk < 1) return hipErrorInvalidValue;
     hipLaunchKernelGGL(gather_rows_kernel, dim3(A), dim3(256), 0, s,
-                       reinterpret_cast<const uint4 *>(X), (int)(row_bytes / 16), row_src, gk,
-                       reinterpret_cast<uint4 *>(Xp));
+                       reinterpret_cast<const uint4 *>(X), (int)(row_bytes / 16), row_src, gk, n_rows,
+                       (long long)((A + gk - 1) / gk), reinterpret_cast<uint4 *>(Xp));
     return hipGetLastError();
 }
 

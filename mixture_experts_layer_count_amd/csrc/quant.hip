@@ -23,6 +23,8 @@
 #include "common.h"
 
 namespace moe {
+
+MOE_BOUNDS_FILE(quant)
 namespace {
 
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t *X, long long ldx, const int32_t *row_src,
@@ -68,8 +70,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t *X, long
     if (scatter) {
         // lane j < sk writes the copy of assignment j, lane sk the shared row's
         for (int j = sub; j <= sk; j += 16) {
-            if (j < sk) S[gc * s_ld + scatter[r * sk + j]] = s;
-            else if (extra0 >= 0) S[gc * s_ld + extra0 + r] = s;
+            const long long dst = j < sk ? (long long)scatter[r * sk + j] : extra0 >= 0 ? extra0 + r : -1;
+            if (j == sk && extra0 < 0) continue;
+            if (MOE_BOUNDS_FAIL(dst >= 0 && dst < s_ld, BOUNDS_QUANT_ROW)) continue;
+            S[gc * s_ld + dst] = s;
         }
         return;
     }

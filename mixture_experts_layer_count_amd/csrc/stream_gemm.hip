@@ -31,6 +31,8 @@
 #include "common.h"
 
 namespace moe {
+
+MOE_BOUNDS_FILE(stream)
 namespace {
 
 constexpr int kWaves = 4;   // wavefronts per block (at most)
@@ -280,6 +282,9 @@ __device__ __forceinline__ void stream_gemm_body(const GemmProblem &p, int n_sli
         g = p.tiles[4 * mt];
         row0 = p.tiles[4 * mt + 1];
         row_end = p.tiles[4 * mt + 2];
+        if (MOE_BOUNDS_FAIL(g >= 0 && g < p.n_groups && row0 >= 0 && row0 < row_end && row_end <= p.M,
+                            BOUNDS_TILE))
+            return;
     } else {
         g = 0;
         row0 = mt * kBM;
@@ -303,6 +308,7 @@ __device__ __forceinline__ void stream_gemm_body(const GemmProblem &p, int n_sli
     if (rok) {
         if (extra && p.row_src) arow = r - p.extra_row0;
         else arow = p.row_src ? (long long)(p.row_src[r] / p.gk) : (long long)r;
+        if (MOE_BOUNDS_FAIL(arow >= 0 && (p.a_rows <= 0 || arow < p.a_rows), BOUNDS_A_ROW)) arow = 0;
     }
     const AT *Ap = reinterpret_cast<const AT *>(p.A) + arow * p.lda + 8 * kg + kbeg;
 

@@ -49,6 +49,9 @@
 #include "tiled_gemm_kernel.h"
 
 namespace moe {
+
+MOE_BOUNDS_FILE(a8)
+
 namespace tiled {
 namespace {
 
@@ -118,9 +121,13 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     const int ntiles = MULTI ? min(per_wg, nN - ng * per_wg) : 1;
     int g, row0, row_end;
     if (p.tiles) {
+        if (MOE_BOUNDS_FAIL(mt < p.max_tiles, BOUNDS_TILE)) return;
         g = p.tiles[4 * mt];
         row0 = p.tiles[4 * mt + 1];
         row_end = p.tiles[4 * mt + 2];
+        if (MOE_BOUNDS_FAIL(g >= 0 && g < p.n_groups && row0 >= 0 && row0 < row_end && row_end <= p.M,
+                            BOUNDS_TILE))
+            return;
     } else {
         g = 0;
         row0 = mt * BM;
@@ -134,8 +141,11 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
 
     auto src_row = [&](int r) -> long long {
         if (r >= row_end) r = row0;  // padding rows read a valid row (never stored)
-        if (extra && p.row_src) return r - p.extra_row0;
-        return p.row_src ? (long long)(p.row_src[r] / p.gk) : (long long)r;
+        long long s;
+        if (extra && p.row_src) s = r - p.extra_row0;
+        else s = p.row_src ? (long long)(p.row_src[r] / p.gk) : (long long)r;
+        if (MOE_BOUNDS_FAIL(s >= 0 && (p.a_rows <= 0 || s < p.a_rows), BOUNDS_A_ROW)) s = 0;
+        return s;
     };
 
     // ---- copy sources ----
@@ -193,6 +203,7 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
         // tile's end read row0's: never used)
         int r = row0 + 64 * w + lane;
         if (r >= row_end) r = row0;
+        if (MOE_BOUNDS_FAIL(r >= 0 && r < p.as_ld, BOUNDS_SCALE_ROW)) r = 0;
         sc_src = p.As + r;
         sc_step = p.as_ld;
     } else {

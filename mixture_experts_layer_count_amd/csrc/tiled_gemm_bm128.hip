@@ -7,6 +7,8 @@
 
 namespace moe {
 
+MOE_BOUNDS_FILE(tiled128)
+
 hipError_t launch_tiled_bm128(const GemmProblem &p, WType wt, bool swiglu, hipStream_t s) {
     switch (wt) {
     case W_BF16: return tiled::launch_bm<W_BF16, 128>(p, swiglu, s);

@@ -11,6 +11,8 @@
 
 namespace moe {
 
+MOE_BOUNDS_FILE(tiled256)
+
 hipError_t launch_tiled_bm256(const GemmProblem &p, WType wt, bool swiglu, hipStream_t s) {
     if (wt == W_BF16) return tiled::launch_bm<W_BF16, 256, 2, 4>(p, swiglu, s);
     if (wt == W_MXFP4) return tiled::launch_bm<W_MXFP4, 256, 4>(p, swiglu, s);

@@ -10,6 +10,8 @@
 
 namespace moe {
 
+MOE_BOUNDS_FILE(tiledf32)
+
 bool tiled_f32_supports(int M, int N, int K, int ksplit, int kchunk) {
     return M > 0 && N >= 16 && N % 8 == 0 && K % tiled::kBK == 0 && ksplit >= 1 && kchunk % tiled::kBK == 0 &&
            kchunk > 0 && (long long)(ksplit - 1) * kchunk < K;

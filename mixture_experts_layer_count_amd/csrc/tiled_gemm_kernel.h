@@ -325,9 +325,13 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void tiled_gemm_kernel(GemmProblem
     const int kbase = (F32OUT ? split * p.kchunk : 0) + k_first * kBK;  // first K of this workgroup
     int g, row0, row_end;
     if (p.tiles) {
+        if (MOE_BOUNDS_FAIL(mt < p.max_tiles, BOUNDS_TILE)) return;
         g = p.tiles[4 * mt];
         row0 = p.tiles[4 * mt + 1];
         row_end = p.tiles[4 * mt + 2];
+        if (MOE_BOUNDS_FAIL(g >= 0 && g < p.n_groups && row0 >= 0 && row0 < row_end && row_end <= p.M,
+                            BOUNDS_TILE))
+            return;
     } else {
         g = 0;
         row0 = mt * BM;
@@ -355,6 +359,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void tiled_gemm_kernel(GemmProblem
         long long src;
         if (extra && p.row_src) src = r - p.extra_row0;
         else src = p.row_src ? (long long)(p.row_src[r] / p.gk) : (long long)r;
+        if (MOE_BOUNDS_FAIL(src >= 0 && (p.a_rows <= 0 || src < p.a_rows), BOUNDS_A_ROW)) src = 0;
         a_src[q] = reinterpret_cast<const uint16_t *>(p.A) + src * p.lda + 8 * aswz_chunk(lane);
     }
     // B: copy q of wavefront w fills K rows of the B tile; each lane fetches
@@ -660,6 +665,9 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void tiled_gemm_kernel(GemmProblem
         // same whichever part is last, and stores the tile. Its counter is
         // left at zero.
         wait_vm<0>();  // the discarded copies land before the LDS is released
+        if (MOE_BOUNDS_FAIL(u.part_slot < kTailSlots && u.tail_slot < kTailSlots && u.part_slot >= u.part,
+                            BOUNDS_TAIL_SLOT))
+            return;
         constexpr int NGR = R::mi * NB;
         f32x4 *buf = reinterpret_cast<f32x4 *>(p.tail_part);
         f32x4 *mine = buf + (long long)u.part_slot * NGR * kT;

@@ -38,6 +38,18 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) == set(_lib.SIGNATURES), "binding signatures out of sync with moe.h"
 
 
+def test_debug_library_exports_every_declared_symbol():
+    # the bounds-checked build of the same sources exports the same ABI
+    dbg = _lib.load(_lib.DEBUG_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(dbg, name), f"libmoe_debug.so does not export {name}"
+
+
+def test_release_bounds_flags_are_zero():
+    # the release build records nothing and touches no device
+    assert moe.lib().moe_debug_bounds() == 0
+
+
 def test_status_strings():
     lib = moe.lib()
     for code in range(6):
