@@ -590,7 +590,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void tiled_gemm_kernel(GemmProblem
 
     // One K tile per step, with a fixed number of copies in flight. Step kt
     // multiplies tile kt (fragments already in registers) row block by row
-    // block; after the first block it waits for tile kt+1 (all but the S-2
+    // block; after the first one or two blocks it waits for tile kt+1 (all but the S-2
     // newest tiles' copies), publishes it with the barrier (which also means
     // every wavefront has finished reading the stage tile kt came from), and
     // spreads over the remaining blocks the copies of tile kt+S into that
@@ -617,16 +617,22 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void tiled_gemm_kernel(GemmProblem
         for (int kt = 0; kt < nk; ++kt) {
             const int nstage = stage + 1 == S ? 0 : stage + 1;
             const int src = min(kt + S, nk - 1);
-            mma_rows(fa, 0, act);
+            // PRE row blocks before the barrier: with 8 row blocks, two (more
+            // matrix-core work to absorb the wavefronts' skew at the barrier:
+            // 1 % on the Mixtral- and Qwen3-shaped prefill layers)
+            constexpr int PRE = R::mi >= 8 ? 2 : 1;
+            constexpr int SLOTS = R::mi - PRE;
+#pragma unroll
+            for (int m = 0; m < PRE; ++m) mma_rows(fa, m, act);
             wait_vm<(S - 2) * R::per_tile>();
             __builtin_amdgcn_s_barrier();
 #pragma unroll
-            for (int c = 0; c < R::mi - 1; ++c) {
+            for (int c = 0; c < SLOTS; ++c) {
 #pragma unroll
-                for (int q = c * NC / (R::mi - 1); q < (c + 1) * NC / (R::mi - 1); ++q) copy(q, src, stage);
+                for (int q = c * NC / SLOTS; q < (c + 1) * NC / SLOTS; ++q) copy(q, src, stage);
 #pragma unroll
-                for (int r = c * NR / (R::mi - 1); r < (c + 1) * NR / (R::mi - 1); ++r) read(fb, r, nstage);
-                mma_rows(fa, c + 1, act);
+                for (int r = c * NR / SLOTS; r < (c + 1) * NR / SLOTS; ++r) read(fb, r, nstage);
+                mma_rows(fa, c + PRE, act);
             }
             if constexpr (FP8)
                 if ((kt & 3) == 3) promote(fa);
