@@ -164,6 +164,9 @@ def cpu_model() -> str:
 
 
 GATE_UP_KERNEL = re.compile(r"(stream|tiled)_gemm_kernel<[^,]+, true|tiled_a8_kernel<true")
+# the routed down projection: the plain tiled kernel of 256- or 160-row tiles
+# (the 128-row fp32 form is the router's gate GEMM)
+DOWN_KERNEL = re.compile(r"tiled_gemm_kernel<[^,]+, false, 256|tiled_a8_kernel<false")
 
 
 def _pmc_means(run_dir: str, counter: str) -> dict:
@@ -197,9 +200,11 @@ def record_traffic(args) -> int:
     # kernel of that run (fill, copy) writes the whole buffer
     f_fetch = nbytes / (max(v for v, _ in cal_f.values()) * 1024.0)
     f_write = nbytes / (max(v for v, _ in cal_w.values()) * 1024.0)
-    names = [n for n in fetch if GATE_UP_KERNEL.search(n)]
+    which = getattr(args, "pmc_kernel", "gate_up")
+    pattern = GATE_UP_KERNEL if which == "gate_up" else DOWN_KERNEL
+    names = [n for n in fetch if pattern.search(n)]
     if len(names) != 1:
-        raise SystemExit(f"expected one gate/up kernel, found {names}")
+        raise SystemExit(f"expected one {which} kernel, found {names}")
     name = names[0]
     fk, nf = fetch[name]
     wk, nw = write[name]
@@ -212,12 +217,14 @@ def record_traffic(args) -> int:
         "hbm_bytes_per_launch": round(fk * 1024.0 * f_fetch + wk * 1024.0 * f_write),
         "commands": args.commands,
     }
-    out = os.path.join(PROFILE_DIR, f"gate_up_swiglu_{args.workload}_pmc.json")
+    stem = "gate_up_swiglu" if which == "gate_up" else "down"
+    out = os.path.join(PROFILE_DIR, f"{stem}_{args.workload}_pmc.json")
     with open(out, "w", encoding="utf-8") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
     with open(out[:-5] + ".md", "w", encoding="utf-8") as fh:
-        fh.write(f"# HBM traffic of the gate/up SwiGLU kernel: {args.workload}\n\n"
+        fh.write(f"# HBM traffic of the {'gate/up SwiGLU' if which == 'gate_up' else 'down projection'} kernel: "
+                 f"{args.workload}\n\n"
                  f"Kernel: `{name}` (sources hash {rec['kernel_source_hash']}).\n\n"
                  "| counter | KiB per dispatch | dispatches | scale | bytes per launch |\n|---|---:|---:|---:|---:|\n"
                  f"| FETCH_SIZE | {fk:.1f} | {nf} | {f_fetch:.4f} | {fk * 1024 * f_fetch:.4g} |\n"
@@ -583,6 +590,8 @@ def main() -> int:
     ap.add_argument("--pmc-write")
     ap.add_argument("--calib-fetch")
     ap.add_argument("--calib-write")
+    ap.add_argument("--pmc-kernel", choices=["gate_up", "down"], default="gate_up",
+                    help="which GEMM's record --record-traffic writes (bench.py reads the gate/up one)")
     ap.add_argument("--commands", nargs="*", default=[])
     ap.add_argument("--sweep", metavar="WORKLOAD",
                     help="token-count sweep of this workload's layer shape (T = 1 .. --sweep-max-t), every path")
