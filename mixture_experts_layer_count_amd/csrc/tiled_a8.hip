@@ -306,13 +306,33 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     // one row scale per lane, and 8-byte output writes
     auto mma_rows = [&](const Frag &f, float sa, int m) {
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (SWIGLU) {
+            // gate/up: the four MFMAs first, then the 16 scaled adds, so each
+            // result is read after the other MFMAs have issued (gate/up
+            // 1.77 -> 1.74 ms on the DeepSeek-shaped layer; the down
+            // projection measured 0.5 % slower this way and keeps the
+            // interleaved order)
+            f32x4 t[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const f32x4 t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[m], f32x4{0, 0, 0, 0},
-                                                                            0, 0, 0, 0, 0, 0);
-            const float sc = sa * ((SWIGLU && j >= 2) ? f.s1 : f.s0);
+            for (int j = 0; j < 4; ++j)
+                t[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[m], f32x4{0, 0, 0, 0}, 0, 0, 0,
+                                                                       0, 0, 0);
+            const float sc0 = sa * f.s0, sc1 = sa * f.s1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(t[i], sc, acc[m][j][i]);
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(t[j][i], j >= 2 ? sc1 : sc0, acc[m][j][i]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 18, 0);  // VALU
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[m], f32x4{0, 0, 0, 0},
+                                                                                0, 0, 0, 0, 0, 0);
+                const float sc = sa * f.s0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(t[i], sc, acc[m][j][i]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
