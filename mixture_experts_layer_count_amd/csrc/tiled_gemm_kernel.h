@@ -59,7 +59,10 @@
 //    beyond L2 about once. The real tile count is read on the device, so
 //    surplus workgroups of the worst-case grid exit without unbalancing the
 //    XCDs.
-//  * the epilogue stages the bf16 tile in LDS and writes 16-byte rows.
+//  * the weight fragment is the MFMA's first operand, so a lane's four
+//    results are four adjacent columns of one row: the epilogue stages the
+//    bf16 tile in LDS with 8-byte writes and stores 16-byte row pieces (fp32
+//    output: 16-byte stores straight from the accumulators).
 #pragma once
 
 #include <type_traits>
@@ -560,15 +563,19 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void tiled_gemm_kernel(GemmProblem
         }
 
     // the NB MFMAs of row block m, kept together as one scheduling group
-    // (row blocks m >= ACT, past the group's end, issue none)
+    // (row blocks m >= ACT, past the group's end, issue none). The weights
+    // are the first operand, so the MFMA forms the transposed 16 x 16 block:
+    // a lane's four results are one row (16 m + lane % 16 of the wavefront's
+    // rows) and four adjacent columns (4 (lane / 16) .. +3 of the block), which
+    // the epilogue stores as one 8-byte (bf16) or 16-byte (fp32) vector
     auto mma_rows = [&](const Frags<R::mi, NB, RW> &f, int m, auto act) {
         constexpr int ACT = decltype(act)::value;
         __builtin_amdgcn_sched_barrier(0);
         if (m < ACT) {
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                if constexpr (FP8) part[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[m], f.b[j], part[m][j], 0, 0, 0);
-                else acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
+                if constexpr (FP8) part[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[m], part[m][j], 0, 0, 0);
+                else acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[m], acc[m][j], 0, 0, 0);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -656,21 +663,20 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void tiled_gemm_kernel(GemmProblem
 
     if constexpr (F32OUT) {
         wait_vm<0>();  // the last (discarded) copies land before the LDS is released
-        // lane holds rows 4 (lane / 16) + i of each 16-row block, column
-        // lane % 16 of each 16-column block: 64-byte row segments
+        // lane holds row lane % 16 of each 16-row block and columns
+        // 4 (lane / 16) .. +3 of each 16-column block: 16-byte stores (N and
+        // ldc are multiples of 8)
         float *Cf = reinterpret_cast<float *>(p.C) + (long long)split * p.c_split_stride;
 #pragma unroll
-        for (int m = 0; m < R::mi; ++m)
+        for (int m = 0; m < R::mi; ++m) {
+            const int row = row0 + wr * (BM / WR) + m * 16 + i16;
+            if (row >= row_end) continue;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = row0 + wr * (BM / WR) + m * 16 + 4 * (lane >> 4) + i;
-                if (row >= row_end) continue;
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const int col = n0 + (256 / WC) * wc + 16 * j + i16;
-                    if (col < p.N) Cf[(long long)row * p.ldc + col] = acc[m][j][i];
-                }
+            for (int j = 0; j < NB; ++j) {
+                const int col = n0 + (256 / WC) * wc + 16 * j + 4 * gq;
+                if (col < p.N) *reinterpret_cast<f32x4 *>(Cf + (long long)row * p.ldc + col) = acc[m][j];
             }
+        }
         return;
     }
     if (TAIL && u.parts > 1) {
@@ -738,26 +744,32 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void tiled_gemm_kernel(GemmProblem
         if (tid == 0) __hip_atomic_store(p.tail_cnt + u.tail_slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // ---- epilogue: stage the bf16 tile in LDS, then 16-byte row stores ----
+    // A lane holds four adjacent columns of one row: one 8-byte LDS write
+    // each (the 16 rows of a 16-lane group land 4 banks apart, conflict-free).
+    // Stores of 8 bytes straight from the accumulators were slower (each
+    // covers 16 row pieces of 32 bytes: 4x the L2 write requests per byte).
     constexpr int LD = Out<SWIGLU>::ld;
     __syncthreads();  // every wavefront is done with the ring
     uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);
 #pragma unroll
-    for (int m = 0; m < R::mi; ++m)
+    for (int m = 0; m < R::mi; ++m) {
+        const int r = wr * (BM / WR) + m * 16 + i16;
+        if constexpr (SWIGLU) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wr * (BM / WR) + m * 16 + 4 * (lane >> 4) + i;
-            if (SWIGLU) {
+            for (int j = 0; j < NB / 2; ++j) {
+                float h[4];
 #pragma unroll
-                for (int j = 0; j < NB / 2; ++j) {
-                    const float v = silu_f32(acc[m][j][i]) * acc[m][j + NB / 2][i];
-                    Cs[r * LD + (128 / WC) * wc + 16 * j + i16] = __builtin_bit_cast(uint16_t, (__bf16)v);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    Cs[r * LD + (256 / WC) * wc + 16 * j + i16] = __builtin_bit_cast(uint16_t, (__bf16)acc[m][j][i]);
+                for (int i = 0; i < 4; ++i) h[i] = silu_f32(acc[m][j][i]) * acc[m][j + NB / 2][i];
+                *reinterpret_cast<u32x2 *>(Cs + r * LD + (128 / WC) * wc + 16 * j + 4 * gq) =
+                    u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                *reinterpret_cast<u32x2 *>(Cs + r * LD + (256 / WC) * wc + 16 * j + 4 * gq) =
+                    u32x2{pack_bf16x2(acc[m][j][0], acc[m][j][1]), pack_bf16x2(acc[m][j][2], acc[m][j][3])};
         }
+    }
     __syncthreads();
     constexpr int W = Out<SWIGLU>::width;
     constexpr int chunks_per_row = W / 8;
