@@ -316,7 +316,7 @@ unsigned moe_debug_bounds(void) {
     if (hipDeviceSynchronize() != hipSuccess) return ~0u;
     return bounds_take_tiled128() | bounds_take_tiled256() | bounds_take_tiledf32() | bounds_take_a8() |
            bounds_take_stream() | bounds_take_permute() | bounds_take_combine() | bounds_take_quant() |
-           bounds_take_ep();
+           bounds_take_ep() | bounds_take_persist();
 #else
     return 0u;
 #endif

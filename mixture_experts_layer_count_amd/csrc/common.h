@@ -56,6 +56,7 @@ unsigned bounds_take_permute();
 unsigned bounds_take_combine();
 unsigned bounds_take_quant();
 unsigned bounds_take_ep();
+unsigned bounds_take_persist();
 
 // ---------------------------------------------------------------------------
 // Vector types for MFMA operands and wide loads
@@ -214,6 +215,10 @@ hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool o
                              hipStream_t s);
 int tiled_gemm_bm(WType wt, long long rows, int groups);  // rows per tile for this row distribution
 bool tiled_gemm_supports(WType wt, int N, int K);
+// persistent form of the 256-row bf16 tiled GEMM (tiled_persist.hip): shapes
+// it takes, and its launcher (N a multiple of the tile width)
+bool tiled_persist_fits(const GemmProblem &p, WType wt, bool swiglu, int bm);
+hipError_t launch_tiled_persist(const GemmProblem &p, bool swiglu, hipStream_t s);
 // tail-split scratch of the tiled kernel: partial sums for tiles of bm rows,
 // and the number of counters
 size_t tiled_tail_bytes(int bm);

@@ -15,6 +15,9 @@ static_assert(tiled::kTailSlots == tiled_tail_counters, "one counter per tail sl
 // one partial tile (bm rows x 256 B-columns, fp32) per tail slot
 size_t tiled_tail_bytes(int bm) { return sizeof(float) * (size_t)tiled::kTailSlots * bm * 256; }
 
+// down projections with more K steps than this keep the tail split
+constexpr int kPersistMaxSplitSteps = 128;
+
 bool tiled_gemm_supports(WType wt, int N, int K) {
     if (wt == W_F32 || wt == W_F32_XBF16) return false;
     if (N % 8 || K % tiled::kBK || N < 16 || K < tiled::kBK) return false;
@@ -34,6 +37,11 @@ hipError_t launch_tiled_gemm(const GemmProblem &p, WType wt, bool swiglu, bool o
     if (!(bm == 128 || (bm == 256 && (wt == W_BF16 || wt == W_MXFP4)))) return hipErrorInvalidValue;
     // the tail split: plain GEMMs with bf16 or MXFP4 weights
     if (p.tail_part && (wt == W_FP8 || swiglu || !p.tail_cnt || !p.tiles)) return hipErrorInvalidValue;
+    // the persistent form where it fits, unless a down projection's long K
+    // makes the tail split (one item per workgroup) the better end of the
+    // launch
+    if (tiled_persist_fits(p, wt, swiglu, bm) && (!p.tail_part || p.K / tiled::kBK <= kPersistMaxSplitSteps))
+        return launch_tiled_persist(p, swiglu, s);
     return bm == 256 ? launch_tiled_bm256(p, wt, swiglu, s) : launch_tiled_bm128(p, wt, swiglu, s);
 }
 
