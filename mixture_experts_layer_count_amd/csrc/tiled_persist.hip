@@ -20,17 +20,23 @@
 //    decodes the workgroup's items into an LDS table once, at the start.
 //  * the last S steps of an item issue the copies of the next item's first
 //    S steps (its pointers are set between two copies of the K loop, so no
-//    pointer changes inside one); after the item's tile is stored, the next
-//    item's first fragments are read.
+//    pointer changes inside one); the last step reads the next item's first
+//    fragments.
 //  * each finished tile is stored row block by row block through a small
 //    LDS staging area per wavefront (8-byte writes, 16-byte row pieces read
 //    back and stored), with no workgroup barrier, while the next item's
 //    copies are in flight.
-//  * every row block is multiplied, also past a short tile's end: the copies
-//    of the K loop that skip them (as the one-item kernel has) made this
-//    kernel spill inside the loop. With SwiGLU the kernel spilled around the
-//    item boundaries and measured slower than the one-item kernel (Qwen3-
-//    shaped gate/up 0.40 -> 0.46 ms), so gate/up keeps that one.
+//  * every row block is multiplied, also past a short tile's end: copies of
+//    the K loop that skip them (as the one-item kernel has) made this kernel
+//    spill inside the loop. The same structure for gate/up (SwiGLU epilogue,
+//    the next tile's gathered row indices copied to LDS ahead of the pointer
+//    switch) measured neutral on the Mixtral shape and 4 % slower on the
+//    Qwen3 shape, whose many short last tiles the one-item kernel skips, so
+//    gate/up keeps the one-item kernel.
+//  * register pressure: offsets of the rare paths (item switch, epilogue)
+//    are recomputed from a re-read lane index, and Item holds only ints
+//    (a bool member made the compiler keep item copies in LDS, behind a full
+//    wait for the copy ring at every item).
 #include "tiled_gemm_kernel.h"
 
 namespace moe {
@@ -57,7 +63,7 @@ struct Persist {
 
 struct Item {
     int g, row0, row_end, n0;
-    bool extra;
+    int extra;  // the extra group's item
 };
 
 __global__ __launch_bounds__(512, 1) void tiled_persist_kernel(GemmProblem p, int nN) {
@@ -223,6 +229,7 @@ __global__ __launch_bounds__(512, 1) void tiled_persist_kernel(GemmProblem p, in
         if (last) wait_vm<0>();
 #pragma unroll
         for (int m = 0; m < MI; ++m) {
+            __builtin_amdgcn_sched_barrier(0);
             if (m < ACT) {
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
@@ -263,12 +270,9 @@ __global__ __launch_bounds__(512, 1) void tiled_persist_kernel(GemmProblem p, in
         if (has_next) nx = item_at(j + 1);
         auto kloop = [&](auto act) {
             // one K step: multiply step kt (f) while reading step kt + 1
-            // into g and copying step src (of the item whose sources are
-            // set). READ false: the item's last step, whose fragment reads
-            // of the next item wait until its tile is stored, so that they
-            // do not sit in registers through the epilogue.
-            auto step = [&](Frags<MI, NB, 2> &f, Frags<MI, NB, 2> &g, int src, auto read_next) {
-                constexpr bool READ = decltype(read_next)::value;
+            // into g (the item's last step: the next item's first) and
+            // copying step src of the item whose sources are set
+            auto step = [&](Frags<MI, NB, 2> &f, Frags<MI, NB, 2> &g, int src) {
                 const int nstage = stage + 1 == S ? 0 : stage + 1;
 #pragma unroll
                 for (int m = 0; m < 2; ++m) mma_rows(f, m, act);
@@ -278,44 +282,30 @@ __global__ __launch_bounds__(512, 1) void tiled_persist_kernel(GemmProblem p, in
                 for (int c = 0; c < MI - 2; ++c) {
 #pragma unroll
                     for (int q = c * NC / (MI - 2); q < (c + 1) * NC / (MI - 2); ++q) copy(q, src, stage);
-                    if constexpr (READ) {
 #pragma unroll
-                        for (int r = c * NR / (MI - 2); r < (c + 1) * NR / (MI - 2); ++r) read(g, r, nstage);
-                    }
+                    for (int r = c * NR / (MI - 2); r < (c + 1) * NR / (MI - 2); ++r) read(g, r, nstage);
                     mma_rows(f, c + 2, act);
                 }
-                if constexpr (READ) land(g);
+                land(g);
                 stage = nstage;
             };
             // steps [0, nk - S): copies of this item's steps S ..
             int kt = 0;
             for (; kt < nk - S; kt += 2) {
-                step(fa, fb, kt + S, std::true_type{});
-                step(fb, fa, kt + 1 + S, std::true_type{});
+                step(fa, fb, kt + S);
+                step(fb, fa, kt + 1 + S);
             }
             // steps [nk - S, nk): copies of the next item's first S steps, or
             // past the last item this item's last step again (into stages
             // nobody reads)
             if (has_next) set_sources(nx);
-            for (; kt < nk - 2; kt += 2) {
-                step(fa, fb, has_next ? kt + S - nk : nk - 1, std::true_type{});
-                step(fb, fa, has_next ? kt + 1 + S - nk : nk - 1, std::true_type{});
+            for (; kt < nk; kt += 2) {
+                step(fa, fb, has_next ? kt + S - nk : nk - 1);
+                step(fb, fa, has_next ? kt + 1 + S - nk : nk - 1);
             }
-            step(fa, fb, has_next ? kt + S - nk : nk - 1, std::true_type{});
-            step(fb, fa, has_next ? kt + 1 + S - nk : nk - 1, std::false_type{});
             tile_out(cur, !has_next, act);
         };
-        // every row block multiplied (the one-item kernel's copies of the K
-        // loop that skip the row blocks past a short tile's end made this
-        // kernel spill inside the K loop)
         kloop(std::integral_constant<int, MI>{});
-        if (has_next) {
-            // the next item's first fragments (its tile is in stage `stage`,
-            // published by the last step's barrier)
-#pragma unroll
-            for (int r = 0; r < NR; ++r) read(fa, r, stage);
-            land(fa);
-        }
         cur = nx;
     }
 }
