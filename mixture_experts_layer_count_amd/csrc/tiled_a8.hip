@@ -137,7 +137,7 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     const bool extra = g == p.extra_group;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6, wr = w / WC, wc = w % WC;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), wr = w / WC, wc = w % WC;
 
     auto src_row = [&](int r) -> long long {
         if (r >= row_end) r = row0;  // padding rows read a valid row (never stored)
@@ -257,14 +257,29 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     constexpr int NR = 16 + MI + 1;
     const int i16 = lane & 15, gq = lane >> 4;
     const int a_row = wr * (BM / 2) + i16;  // + 16 m
+    // B read addresses: K row k = 32 gq + 8 t + (lane % 16) / 2 of column
+    // block j. Its chunk swizzle depends only on gq and lane % 16 (8 t adds
+    // neither low bits nor a carry into bit 5), so t moves the address by
+    // 8 t rows exactly: one lane base per column block, and t in the
+    // instruction's offset field
+    uint32_t b_base[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int nb = SWIGLU ? (R::BN / 2) * (j >> 1) + 32 * wc + 16 * (j & 1) : 64 * wc + 16 * j;
+        const int k = 32 * gq + (i16 >> 1);
+        b_base[j] = R::a_bytes + k * R::BN + 16 * ((nb >> 4) ^ bswz_a8<WC>(k)) + 8 * (i16 & 1);
+    }
     auto read = [&](Frag &f, int r, int stage) {
         const uint8_t *st = lds + stage * R::stage;
         if (r < 16) {
             const int j = r >> 2, t = r & 3;
-            const int nb = SWIGLU ? (R::BN / 2) * (j >> 1) + 32 * wc + 16 * (j & 1) : 64 * wc + 16 * j;
-            const int k = 32 * gq + 8 * t + (i16 >> 1);
-            raw[j][t] = ds_tr8(lds_addr(st + R::a_bytes) + k * R::BN + 16 * ((nb >> 4) ^ bswz_a8<WC>(k)) +
-                               8 * (i16 & 1));
+            const uint32_t addr = lds_addr(st) + b_base[j];
+            switch (t) {
+            case 0: raw[j][0] = ds_tr8_at<0>(addr); break;
+            case 1: raw[j][1] = ds_tr8_at<8 * R::BN>(addr); break;
+            case 2: raw[j][2] = ds_tr8_at<16 * R::BN>(addr); break;
+            default: raw[j][3] = ds_tr8_at<24 * R::BN>(addr); break;
+            }
         } else if (r < 16 + MI) {
             const int m = r - 16;
             const int row = a_row + 16 * m;

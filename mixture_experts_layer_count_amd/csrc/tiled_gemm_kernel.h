@@ -191,6 +191,14 @@ __device__ __forceinline__ u32x2 ds_tr8(uint32_t addr) {
     asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(addr));
     return r;
 }
+// the same with a constant byte offset in the instruction's offset field
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_tr8_at(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
 __device__ __forceinline__ void fence(u32x2 &v) { asm volatile("" : "+v"(v)); }
 
 // Map this workgroup to (row tile, column tile) of the work order; false for
