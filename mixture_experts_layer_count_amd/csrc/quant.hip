@@ -19,7 +19,13 @@
 // two cache lines instead of 64 (measured: 6 % of the DeepSeek-shaped gate/up).
 // For the token rows of a layer the transposed scales are written at the rows
 // the permutation gives each token's assignments (scatter[t*sk + j], j < sk,
-// the inverse map) and, with a shared expert, at extra0 + t.
+// the inverse map) and, with a shared expert, at extra0 + t. That launch is
+// ordered by group: a block takes 16 consecutive rows of one group, and the
+// groups g with g % 8 == x go to XCD x (block index % 8), so the 4-byte
+// scatter writes into group g's scale row all land in one XCD's L2 and merge
+// there into whole lines (in row order, every XCD wrote partial lines of
+// every scale row; the DeepSeek-shaped layer's quantisation went from 33.2
+// to 31.1 us).
 #include "common.h"
 
 namespace moe {
@@ -30,12 +36,29 @@ namespace {
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t *X, long long ldx, const int32_t *row_src,
                                                          int gk, int R, int C, uint8_t *Q, float *S, long long s_ld,
                                                          const int32_t *scatter, int sk, int extra0) {
-    const long long gid = ((long long)blockIdx.x * 256 + threadIdx.x) >> 4;
     const int sub = threadIdx.x & 15;
     const int gpr = C >> 7;  // groups per row
-    const bool ok = gid < (long long)R * gpr;
-    const long long r = ok ? gid / gpr : 0;
-    const int gc = ok ? (int)(gid - r * gpr) : 0;
+    bool ok;
+    long long r;
+    int gc;
+    if (scatter) {
+        // XCD x = block % 8 takes groups x, x + 8, ...; its block s covers
+        // rows 16 (s % chunks) .. +15 of group x + 8 (s / chunks)
+        const int chunks = (R + 15) >> 4;
+        const int x = blockIdx.x % 8, s = blockIdx.x / 8;
+        gc = x + 8 * (s / chunks);
+        r = 16LL * (s % chunks) + (threadIdx.x >> 4);
+        ok = gc < gpr && r < R;
+        if (!ok) {
+            gc = 0;
+            r = 0;
+        }
+    } else {
+        const long long gid = ((long long)blockIdx.x * 256 + threadIdx.x) >> 4;
+        ok = gid < (long long)R * gpr;
+        r = ok ? gid / gpr : 0;
+        gc = ok ? (int)(gid - r * gpr) : 0;
+    }
 
     u32x4 raw = {0, 0, 0, 0};
     if (ok) {
@@ -90,7 +113,9 @@ hipError_t launch_quant_rows(const void *X, long long ldx, const int32_t *row_sr
     if (sl && (sl->ld < 1 || (sl->scatter && sl->k < 1))) return hipErrorInvalidValue;
     if (R == 0) return hipSuccess;
     const long long threads = (long long)R * (C / 128) * 16;
-    const long long blocks = (threads + 255) / 256;
+    long long blocks = (threads + 255) / 256;
+    // group-ordered launch: 8 XCDs x ceil(groups / 8) x 16-row chunks
+    if (sl && sl->scatter) blocks = 8LL * ((C / 128 + 7) / 8) * ((R + 15) / 16);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                        reinterpret_cast<const uint16_t *>(X), ldx, row_src, gk, R, C, Q, S, sl ? sl->ld : 0LL,
