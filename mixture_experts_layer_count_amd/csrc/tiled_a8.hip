@@ -374,20 +374,32 @@ __global__ __launch_bounds__(128 * WC, 1) void tiled_a8_kernel(GemmProblem p, in
     // lane holds four adjacent columns of one row, so each store is 8 bytes
     // and one instruction covers 32 contiguous bytes of 16 rows (the four
     // stores of j fill the wavefront's 128-byte row segments)
+    // Lanes l and l ^ 16 hold columns 4 (lane / 16) .. +3 of the same row.
+    // For column blocks 2 jp and 2 jp + 1, the lane with even lane / 16 takes
+    // its partner's four columns of the first block and the odd one its
+    // partner's of the second (one 32-bit exchange per pair of values), so
+    // each lane stores 8 adjacent columns (16 bytes) and one store covers 64
+    // contiguous bytes of 16 rows: half the store instructions of 8-byte
+    // stores, each with twice the bytes per row.
     auto tile_out = [&](int u) {
         uint16_t *Cg = reinterpret_cast<uint16_t *>(p.C);
-        const int cbase = n0 + u * O::width + 64 * wc + 4 * gq;
+        const bool odd = gq & 1;
+        const int cbase = n0 + u * O::width + 64 * wc + 8 * (gq >> 1);
 #pragma unroll
         for (int m = 0; m < MI; ++m) {
             const int row = row0 + wr * (BM / 2) + 16 * m + i16;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = cbase + 16 * j;
-                if (row < row_end && col < p.N)
-                    *reinterpret_cast<u32x2 *>(Cg + (long long)row * p.ldc + col) =
-                        u32x2{pack_bf16x2(acc[m][j][0], acc[m][j][1]), pack_bf16x2(acc[m][j][2], acc[m][j][3])};
-                acc[m][j] = f32x4{};
+            for (int jp = 0; jp < 2; ++jp) {
+                const f32x4 &x0 = acc[m][2 * jp], &x1 = acc[m][2 * jp + 1];
+                const uint32_t a0 = pack_bf16x2(x0[0], x0[1]), a1 = pack_bf16x2(x0[2], x0[3]);
+                const uint32_t b0 = pack_bf16x2(x1[0], x1[1]), b1 = pack_bf16x2(x1[2], x1[3]);
+                const uint32_t r0 = __shfl_xor(odd ? a0 : b0, 16), r1 = __shfl_xor(odd ? a1 : b1, 16);
+                const u32x4 v = odd ? u32x4{r0, r1, b0, b1} : u32x4{a0, a1, r0, r1};
+                const int col = cbase + 16 * (2 * jp + (odd ? 1 : 0));
+                if (row < row_end && col < p.N) *reinterpret_cast<u32x4 *>(Cg + (long long)row * p.ldc + col) = v;
             }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{};
         }
     };
     // one K step: multiply step gs (in cur) while copying step gs + S and
