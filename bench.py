@@ -43,12 +43,15 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 # void once any of them changes)
 KERNEL_SOURCES = {"stream": ("stream_gemm.hip", "common.h"),
                   "tiled": ("tiled_gemm_kernel.h", "tiled_gemm_bm128.hip", "tiled_gemm_bm256.hip", "common.h"),
-                  "a8": ("tiled_a8.hip", "tiled_gemm_kernel.h", "common.h")}
+                  "a8": ("tiled_a8.hip", "tiled_gemm_kernel.h", "common.h"),
+                  "persist": ("tiled_persist.hip", "tiled_gemm_kernel.h", "common.h")}
 
 
 def kernel_family(name: str) -> str:
     """Source family of a gate/up kernel's (demangled) name."""
-    return "stream" if "stream_gemm" in name else ("a8" if "tiled_a8" in name else "tiled")
+    if "stream_gemm" in name:
+        return "stream"
+    return "a8" if "tiled_a8" in name else ("persist" if "tiled_persist" in name else "tiled")
 
 
 def kernel_source_hash(path: str) -> str:
@@ -164,9 +167,9 @@ def cpu_model() -> str:
 
 
 GATE_UP_KERNEL = re.compile(r"(stream|tiled)_gemm_kernel<[^,]+, true|tiled_a8_kernel<true")
-# the routed down projection: the plain tiled kernel of 256- or 160-row tiles
-# (the 128-row fp32 form is the router's gate GEMM)
-DOWN_KERNEL = re.compile(r"tiled_gemm_kernel<[^,]+, false, 256|tiled_a8_kernel<false")
+# the routed down projection: the plain tiled kernel of 256- or 160-row tiles,
+# or its persistent form (the 128-row fp32 form is the router's gate GEMM)
+DOWN_KERNEL = re.compile(r"tiled_gemm_kernel<[^,]+, false, 256|tiled_a8_kernel<false|tiled_persist_kernel")
 
 
 def _pmc_means(run_dir: str, counter: str) -> dict:
@@ -268,7 +271,7 @@ def summarize_counter(args) -> int:
     from a `--pmc <counter> -f csv` output directory."""
     means = _pmc_means(args.summarize_counter, args.counter)
     rows = [(re.sub(r"\(moe::GemmProblem.*$", "", n.replace("(anonymous namespace)::", "")).strip(), v, c)
-            for n, (v, c) in means.items() if "_gemm_kernel" in n or "tiled_a8" in n]
+            for n, (v, c) in means.items() if "_gemm_kernel" in n or "tiled_a8" in n or "tiled_persist" in n]
     if not rows:
         raise SystemExit(f"no GEMM kernel rows for {args.counter} under {args.summarize_counter}")
     print(f"# {args.counter} of the expert GEMM kernels: {args.workload}\n")
