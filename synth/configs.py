@@ -81,6 +81,10 @@ MINI_CONFIGS = {
         LayerConfig("mini_bf16_wide", T=300, H=256, F=192, E=64, k=8, seed=4),
         # enough rows per expert for 256-row tiles, ragged in rows, N and K
         LayerConfig("mini_bf16_tall", T=1536, H=640, F=416, E=8, k=2, zipf_s=1.1, seed=7),
+        # bf16 shared expert as wide as the routed experts (one more group of
+        # the routed launches), with 256-row tiles and whole 256-column down
+        # tiles: the persistent down projection's shared-expert rows
+        LayerConfig("mini_bf16_shared_prefill", T=800, H=512, F=384, E=8, k=2, Fs=384, seed=16),
         LayerConfig("mini_fp8_decode", T=20, H=384, F=256, E=16, k=4, Fs=256, w="fp8", seed=5),
         LayerConfig("mini_fp8_prefill", T=520, H=512, F=384, E=16, k=4, Fs=384, w="fp8", seed=6),
         # down projection over several 256-column tiles (H = 11 x 128: a
