@@ -650,7 +650,15 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void tiled_gemm_kernel(GemmProblem
 #pragma unroll
                 for (int q = c * NC / SLOTS; q < (c + 1) * NC / SLOTS; ++q) copy(q, src, stage);
 #pragma unroll
-                for (int r = c * NR / SLOTS; r < (c + 1) * NR / SLOTS; ++r) read(nxt, r, nstage);
+                for (int r = c * NR / SLOTS; r < (c + 1) * NR / SLOTS; ++r) {
+                    // the fragments of row blocks this wavefront does not
+                    // multiply (past the group's end) are not read, nor,
+                    // with none to multiply, the B fragments
+                    constexpr int ACT = decltype(act)::value;
+                    const bool a_rd = r >= NBR && r < NBR + R::mi;
+                    if ((a_rd && r - NBR >= ACT) || (ACT == 0 && r < NBR)) continue;
+                    read(nxt, r, nstage);
+                }
                 mma_rows(cur, c + PRE, act);
             }
             if constexpr (FP8)
