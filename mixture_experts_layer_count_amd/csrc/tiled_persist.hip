@@ -200,14 +200,11 @@ __global__ __launch_bounds__(512, 1) void tiled_persist_kernel(GemmProblem p, in
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[m][j] = f32x4{};
     // weights first: a lane's four results are one row, four adjacent columns
-    auto mma_rows = [&](const Frags<MI, NB, 2> &f, int m, auto act) {
-        constexpr int ACT = decltype(act)::value;
+    auto mma_rows = [&](const Frags<MI, NB, 2> &f, int m) {
         __builtin_amdgcn_sched_barrier(0);
-        if (m < ACT) {
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[m], acc[m][j], 0, 0, 0);
-        }
+        for (int j = 0; j < NB; ++j)
+            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[m], acc[m][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -216,8 +213,7 @@ __global__ __launch_bounds__(512, 1) void tiled_persist_kernel(GemmProblem p, in
     // back and next write need no barrier. The last item first lets the ring's
     // discarded copies land (the LDS must not be written once the workgroup
     // has ended). The accumulators are cleared for the next item.
-    auto tile_out = [&](const Item &it, bool last, auto act) {
-        constexpr int ACT = decltype(act)::value;
+    auto tile_out = [&](const Item &it, bool last) {
         uint16_t *stg = reinterpret_cast<uint16_t *>(lds + R::ring + w * P::stg_bytes);
         uint16_t *Cb = reinterpret_cast<uint16_t *>(p.C) + (long long)it.row0 * p.ldc + it.n0 + P::cols * wc;
         // the row stride, the tile's row count and the lane, re-read here so
@@ -230,19 +226,17 @@ __global__ __launch_bounds__(512, 1) void tiled_persist_kernel(GemmProblem p, in
 #pragma unroll
         for (int m = 0; m < MI; ++m) {
             __builtin_amdgcn_sched_barrier(0);
-            if (m < ACT) {
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    *reinterpret_cast<u32x2 *>(stg + l16 * P::sld + 16 * j + 4 * lq) =
-                        u32x2{pack_bf16x2(acc[m][j][0], acc[m][j][1]), pack_bf16x2(acc[m][j][2], acc[m][j][3])};
+            for (int j = 0; j < NB; ++j)
+                *reinterpret_cast<u32x2 *>(stg + l16 * P::sld + 16 * j + 4 * lq) =
+                    u32x2{pack_bf16x2(acc[m][j][0], acc[m][j][1]), pack_bf16x2(acc[m][j][2], acc[m][j][3])};
 #pragma unroll
-                for (int c = 0; c < 16 * P::pieces / 64; ++c) {
-                    const int piece = ln + 64 * c;
-                    const int r = piece / P::pieces, pc = piece % P::pieces;
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + r * P::sld + 8 * pc);
-                    const int lrow = wr * 128 + 16 * m + r;  // row within the tile
-                    if (lrow < rows) *reinterpret_cast<u32x4 *>(Cb + (lrow * ldc + 8 * pc)) = v;
-                }
+            for (int c = 0; c < 16 * P::pieces / 64; ++c) {
+                const int piece = ln + 64 * c;
+                const int r = piece / P::pieces, pc = piece % P::pieces;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + r * P::sld + 8 * pc);
+                const int lrow = wr * 128 + 16 * m + r;  // row within the tile
+                if (lrow < rows) *reinterpret_cast<u32x4 *>(Cb + (lrow * ldc + 8 * pc)) = v;
             }
 #pragma unroll
             for (int j = 0; j < NB; ++j) acc[m][j] = f32x4{};
@@ -268,44 +262,41 @@ __global__ __launch_bounds__(512, 1) void tiled_persist_kernel(GemmProblem p, in
         const bool has_next = j + 1 < count;
         Item nx = cur;
         if (has_next) nx = item_at(j + 1);
-        auto kloop = [&](auto act) {
-            // one K step: multiply step kt (f) while reading step kt + 1
-            // into g (the item's last step: the next item's first) and
-            // copying step src of the item whose sources are set
-            auto step = [&](Frags<MI, NB, 2> &f, Frags<MI, NB, 2> &g, int src) {
-                const int nstage = stage + 1 == S ? 0 : stage + 1;
+        // one K step: multiply step kt (f) while reading step kt + 1
+        // into g (the item's last step: the next item's first) and
+        // copying step src of the item whose sources are set
+        auto step = [&](Frags<MI, NB, 2> &f, Frags<MI, NB, 2> &g, int src) {
+            const int nstage = stage + 1 == S ? 0 : stage + 1;
 #pragma unroll
-                for (int m = 0; m < 2; ++m) mma_rows(f, m, act);
-                wait_vm<(S - 2) * NC>();
-                __builtin_amdgcn_s_barrier();
+            for (int m = 0; m < 2; ++m) mma_rows(f, m);
+            wait_vm<(S - 2) * NC>();
+            __builtin_amdgcn_s_barrier();
 #pragma unroll
-                for (int c = 0; c < MI - 2; ++c) {
+            for (int c = 0; c < MI - 2; ++c) {
 #pragma unroll
-                    for (int q = c * NC / (MI - 2); q < (c + 1) * NC / (MI - 2); ++q) copy(q, src, stage);
+                for (int q = c * NC / (MI - 2); q < (c + 1) * NC / (MI - 2); ++q) copy(q, src, stage);
 #pragma unroll
-                    for (int r = c * NR / (MI - 2); r < (c + 1) * NR / (MI - 2); ++r) read(g, r, nstage);
-                    mma_rows(f, c + 2, act);
-                }
-                land(g);
-                stage = nstage;
-            };
-            // steps [0, nk - S): copies of this item's steps S ..
-            int kt = 0;
-            for (; kt < nk - S; kt += 2) {
-                step(fa, fb, kt + S);
-                step(fb, fa, kt + 1 + S);
+                for (int r = c * NR / (MI - 2); r < (c + 1) * NR / (MI - 2); ++r) read(g, r, nstage);
+                mma_rows(f, c + 2);
             }
-            // steps [nk - S, nk): copies of the next item's first S steps, or
-            // past the last item this item's last step again (into stages
-            // nobody reads)
-            if (has_next) set_sources(nx);
-            for (; kt < nk; kt += 2) {
-                step(fa, fb, has_next ? kt + S - nk : nk - 1);
-                step(fb, fa, has_next ? kt + 1 + S - nk : nk - 1);
-            }
-            tile_out(cur, !has_next, act);
+            land(g);
+            stage = nstage;
         };
-        kloop(std::integral_constant<int, MI>{});
+        // steps [0, nk - S): copies of this item's steps S ..
+        int kt = 0;
+        for (; kt < nk - S; kt += 2) {
+            step(fa, fb, kt + S);
+            step(fb, fa, kt + 1 + S);
+        }
+        // steps [nk - S, nk): copies of the next item's first S steps, or
+        // past the last item this item's last step again (into stages
+        // nobody reads)
+        if (has_next) set_sources(nx);
+        for (; kt < nk; kt += 2) {
+            step(fa, fb, has_next ? kt + S - nk : nk - 1);
+            step(fb, fa, has_next ? kt + 1 + S - nk : nk - 1);
+        }
+        tile_out(cur, !has_next);
         cur = nx;
     }
 }
