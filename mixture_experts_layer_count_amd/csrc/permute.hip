@@ -131,10 +131,11 @@ __global__ __launch_bounds__(kChunk) void permute_rank_kernel(
 }
 
 // Per-chunk counts -> each chunk's first row in its expert block. The 1024
-// threads split into P = 1024 / E groups; thread (group s, expert e) owns a
-// contiguous run of chunks of expert e. Pass 1 sums the run (loads in
-// batches of 16, so their latencies overlap), the runs and the experts are
-// scanned in LDS, and pass 2 rewrites the run's counts as exclusive prefixes.
+// threads split into P = min(1024 / E, chunks) groups; thread (group s,
+// expert e) owns a contiguous run of chunks of expert e. Pass 1 sums the run
+// (loads in batches of 16, so their latencies overlap), the runs and the
+// experts are scanned in LDS, and pass 2 rewrites the run's counts as
+// exclusive prefixes (from the registers of pass 1 when the run is one batch).
 __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t *chunk_counts, int nchunks,
                                                             int E, int32_t *counts,
                                                             int32_t *offsets, TileRequest tr) {
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t *chunk_count
     __shared__ int expert_off[1024];
     __shared__ int scan_lds[16];
     const int tid = threadIdx.x;
-    const int P = 1024 / E;
+    const int P = min(1024 / E, nchunks);
     const int e = tid % E, sg = tid / E;
     const bool act = sg < P;
     const int per = (nchunks + P - 1) / P;
@@ -150,12 +151,17 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t *chunk_count
     const int c1 = act ? min(nchunks, c0 + per) : 0;
 
     int sum = 0;
+    int v0[16] = {};  // the first batch of the run
     for (int c = c0; c < c1; c += 16) {
         int v[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) v[u] = c + u < c1 ? chunk_counts[(long long)(c + u) * E + e] : 0;
 #pragma unroll
         for (int u = 0; u < 16; ++u) sum += v[u];
+        if (c == c0) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v0[u] = v[u];
+        }
     }
     run_sum[tid] = sum;
     __syncthreads();
@@ -173,14 +179,22 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t *chunk_count
     __syncthreads();
     if (act) {
         int run = expert_off[e] + before;
-        for (int c = c0; c < c1; c += 16) {
-            int v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = c + u < c1 ? chunk_counts[(long long)(c + u) * E + e] : 0;
+        if (per <= 16) {
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
-                if (c + u < c1) chunk_counts[(long long)(c + u) * E + e] = run;
-                run += v[u];
+                if (c0 + u < c1) chunk_counts[(long long)(c0 + u) * E + e] = run;
+                run += v0[u];
+            }
+        } else {
+            for (int c = c0; c < c1; c += 16) {
+                int v[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) v[u] = c + u < c1 ? chunk_counts[(long long)(c + u) * E + e] : 0;
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    if (c + u < c1) chunk_counts[(long long)(c + u) * E + e] = run;
+                    run += v[u];
+                }
             }
         }
         if (sg == 0) {
