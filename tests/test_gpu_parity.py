@@ -518,6 +518,18 @@ def test_forward_edge_cases(variant):
     _check_forward(cfg, d, moe.MoELayer(d, cfg.k))
 
 
+@pytest.mark.parametrize("variant", ["k16_shared", "k20", "k20_shared"])
+def test_forward_w8a8_many_picks(variant):
+    # the W8A8 forward quantises each token row once and writes its scales at
+    # the rows of all its picks (and the shared expert's row); 16 lanes share
+    # a row's picks, so 16 or more picks take a second pass over the lanes
+    kw = {"k16_shared": dict(E=32, k=16), "k20": dict(E=32, k=20, Fs=0), "k20_shared": dict(E=32, k=20)}[variant]
+    cfg = MINI_CONFIGS["mini_fp8_prefill"].with_(**kw)
+    say(f"[forward] W8A8 with {cfg.k} picks of {cfg.E}, shared expert width {cfg.Fs}")
+    d = screened_layer(cfg)
+    _check_forward(cfg, d, moe.MoELayer(d, cfg.k, path="tiled_a8"), mirror=True)
+
+
 def test_forward_empty_batch():
     cfg = MINI_CONFIGS["mini_bf16_decode"]
     d = screened_layer(cfg)
