@@ -571,9 +571,13 @@ def ep_bench(args) -> int:
 
 
 def dtype_label(cfg, a8: bool) -> str:
-    return {"f32": "f32", "bf16": "bf16",
-            "fp8": "fp8-e4m3 weights and activations (fp32 scales)" if a8 else "fp8-e4m3 weights, bf16 activations",
-            "mxfp4": "mxfp4 weights (e2m1 + e8m0 scales), bf16 activations"}[cfg.w]
+    """The type the expert GEMMs multiply in: E4M3 codes on the fp8 matrix
+    cores for W8A8; bf16 for bf16 weights and for fp8 or MXFP4 weights that
+    are decoded to bf16 beside bf16 activations; fp32 for the fp32 layer.
+    The weight and activation formats themselves are in `config`."""
+    if cfg.w == "f32":
+        return "f32"
+    return "fp8" if cfg.w == "fp8" and a8 else "bf16"
 
 
 def main() -> int:
