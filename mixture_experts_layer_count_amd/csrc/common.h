@@ -229,7 +229,7 @@ constexpr int tiled_tail_counters = 256;
 // tiles of bm = 128 or 160 rows; output bf16, or E4M3 h with transposed
 // scales (gate/up). Returns hipErrorInvalidValue for unsupported shapes.
 hipError_t launch_tiled_a8(const GemmProblem &p, bool swiglu, int bm, hipStream_t s);
-int tiled_a8_bm(long long rows, int groups);  // rows per W8A8 tile (128 or 160)
+int tiled_a8_bm(long long rows, int groups);  // rows per W8A8 tile (160)
 bool tiled_a8_supports(int N, int K);
 
 // E4M3 quantisation of bf16 rows: for each row and 128-column group,

@@ -64,7 +64,7 @@ constexpr int kA8WC = 4;
 constexpr int kA8BK = 128;   // K per step = one scale block
 constexpr int kA8Budget = 160 * 1024;
 
-// BM rows (128 or 160: 2 wavefront rows of BM/2) x BN B-columns
+// BM rows (160 as launched: 2 wavefront rows of BM/2) x BN B-columns
 template <int WC, int BM>
 struct RingA8 {
     static constexpr int threads = 128 * WC;        // 2 x WC wavefronts
@@ -574,11 +574,8 @@ hipError_t launch_tiled_a8(const GemmProblem &p, bool swiglu, int bm, hipStream_
     if (!p.As || p.as_ld < p.M || p.ksplit != 1 || !tiled_a8_supports(p.N, p.K) || !p.S0 ||
         (swiglu && (!p.B1 || !p.S1)))
         return hipErrorInvalidValue;
-    if (bm == 160)
-        return swiglu ? tiled::launch_a8<true, tiled::kA8WC, 160>(p, s) : tiled::launch_a8<false, tiled::kA8WC, 160>(p, s);
-    if (bm == 128)
-        return swiglu ? tiled::launch_a8<true, tiled::kA8WC, 128>(p, s) : tiled::launch_a8<false, tiled::kA8WC, 128>(p, s);
-    return hipErrorInvalidValue;
+    if (bm != 160) return hipErrorInvalidValue;
+    return swiglu ? tiled::launch_a8<true, tiled::kA8WC, 160>(p, s) : tiled::launch_a8<false, tiled::kA8WC, 160>(p, s);
 }
 
 }  // namespace moe
