@@ -79,6 +79,9 @@ def test_route_worked_example():
     # 512 tokens and more: the tiled router GEMM (128-row tiles, split over H),
     # with ragged rows, fewer experts than one 256-column tile, and K splits
     (600, 64, 4, 1024), (777, 40, 2, 512), (1100, 256, 8, 2048), (4096, 16, 2, 256),
+    # and fewer than 16 experts, where the row-streaming router runs at any
+    # token count (wide and narrow gates, ragged token counts)
+    (514, 8, 2, 4096), (1030, 12, 3, 800), (701, 4, 1, 224),
 ])
 def test_route_shapes(T, E, k, H):
     cfg = LayerConfig(f"route_{T}_{E}_{k}_{H}", T=T, H=H, F=32, E=E, k=k, w_std=0.2, seed=T + E)
@@ -94,16 +97,18 @@ def test_route_exact_ties():
     """Equal scores go to the lower expert index. Zero token rows (padding
     tokens) give all-equal logits: the k lowest experts, each with weight
     1/k. Duplicated gate columns give pairs of equal logits: the lower index
-    of a pair comes first wherever both are chosen. Both the row-streaming
-    router (few tokens) and the tiled one (512 tokens and more) run."""
-    for T in (200, 600):
-        cfg = LayerConfig(f"ties_{T}", T=T, H=256, F=32, E=64, k=6, seed=90 + T)
-        say(f"[route] exact ties T={T}")
+    of a pair comes first wherever both are chosen. The row-streaming router
+    (few tokens, or fewer than 16 experts) and the tiled one (512 tokens and
+    more) run."""
+    for T, E in ((200, 64), (600, 64), (600, 8)):
+        cfg = LayerConfig(f"ties_{T}_{E}", T=T, H=256, F=32, E=E, k=6, seed=90 + T + E)
+        say(f"[route] exact ties T={T} E={E}")
         d = screened_layer(cfg, experts=False)
         X = d["X"].clone()
         X[::3] = 0.0                                  # every third token is padding
         Wg = d["Wg"].clone()
-        pairs = [(3, 40), (10, 11), (17, 63), (0, 32)]  # same slice, next column, other slices
+        # same slice, next column, other slices (few experts: adjacent and apart)
+        pairs = [(3, 40), (10, 11), (17, 63), (0, 32)] if E == 64 else [(1, 2), (0, 6)]
         for a, b in pairs:
             Wg[:, b] = Wg[:, a]
         logits, idx, w = moe.route(X, Wg, cfg.k)
