@@ -1,8 +1,10 @@
 """Host arithmetic of bench.py, on the CPU: the algorithmic bytes and flops
 behind the roofline fractions, the W8A8 path choice, the percentile and the
-dtype label. Each expected value is written out here from the definitions
+dtype label, and the counter records behind `roofline.traffic`. Each expected value is written out here from the definitions
 of the kernels' work (weights of the touched experts, their block scales,
 token rows in and h out), not taken from bench.py."""
+import json
+
 import pytest
 
 import bench
@@ -74,3 +76,48 @@ def test_kernel_family_from_trace_names():
     assert bench.kernel_family("void moe::tiled::(anonymous namespace)::tiled_a8_kernel<true, 4, 160, false>") == "a8"
     assert bench.kernel_family("moe::tiled::(anonymous namespace)::tiled_persist_kernel") == "persist"
     assert bench.kernel_family("void moe::tiled::tiled_gemm_kernel<1, true, 256, 2, false, 4>") == "tiled"
+
+
+def _counter_csv(path, rows):
+    path.mkdir(parents=True, exist_ok=True)
+    lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+    lines += [f'{d},"{k}",{c},{v}' for d, k, c, v in rows]
+    (path / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+
+
+def test_counter_means_sum_rows_of_a_dispatch_then_average_dispatches(tmp_path):
+    a, b = "void tiled_a8_kernel<true, 4, 160, false>(x)", "void other_kernel(x)"
+    _counter_csv(tmp_path / "run", [
+        (1, a, "FETCH_SIZE", 10.0), (1, a, "FETCH_SIZE", 20.0),   # two rows of one dispatch
+        (2, a, "FETCH_SIZE", 40.0), (1, a, "WRITE_SIZE", 99.0),   # another dispatch; another counter
+        (3, b, "FETCH_SIZE", 5.0),
+    ])
+    got = bench._pmc_means(str(tmp_path / "run"), "FETCH_SIZE")
+    assert got == {a: (35.0, 2), b: (5.0, 1)}
+
+
+def test_traffic_record_scales_each_counter_by_the_copy_calibration(tmp_path, monkeypatch):
+    # a 1 GiB copy whose FETCH_SIZE reads half the bytes and whose WRITE_SIZE
+    # reads them all: scales 2 and 1; the gate/up kernel reads 3000 KiB and
+    # writes 500 KiB per dispatch
+    n = bench.COPY_CALIBRATION_BYTES
+    gu = "void moe::tiled::(anonymous namespace)::tiled_a8_kernel<true, 4, 160, false>(x)"
+    dn = "void moe::tiled::(anonymous namespace)::tiled_a8_kernel<false, 4, 160, true>(x)"
+    _counter_csv(tmp_path / "f", [(1, gu, "FETCH_SIZE", 3000.0), (2, dn, "FETCH_SIZE", 7.0)])
+    _counter_csv(tmp_path / "w", [(1, gu, "WRITE_SIZE", 500.0), (2, dn, "WRITE_SIZE", 7.0)])
+    _counter_csv(tmp_path / "cf", [(1, "copy", "FETCH_SIZE", n / 2048.0), (2, "fill", "FETCH_SIZE", 1.0)])
+    _counter_csv(tmp_path / "cw", [(1, "copy", "WRITE_SIZE", n / 1024.0), (2, "fill", "WRITE_SIZE", n / 1024.0)])
+    out = tmp_path / "profiles"
+    out.mkdir()
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(out))
+
+    class Args:
+        pmc_fetch, pmc_write = str(tmp_path / "f"), str(tmp_path / "w")
+        calib_fetch, calib_write = str(tmp_path / "cf"), str(tmp_path / "cw")
+        workload, commands, pmc_kernel = "dsv3_prefill", ["cmd"], "gate_up"
+
+    assert bench.record_traffic(Args) == 0
+    rec = json.loads((out / "gate_up_swiglu_dsv3_prefill_pmc.json").read_text())
+    assert rec["kernel"] == gu
+    assert (rec["fetch_scale"], rec["write_scale"]) == (2.0, 1.0)
+    assert rec["hbm_bytes_per_launch"] == 3000 * 1024 * 2 + 500 * 1024 * 1
