@@ -1,8 +1,9 @@
 """Host arithmetic of bench.py, on the CPU: the algorithmic bytes and flops
-behind the roofline fractions, the W8A8 path choice, the percentile and the
-dtype label, and the counter records behind `roofline.traffic`. Each expected value is written out here from the definitions
-of the kernels' work (weights of the touched experts, their block scales,
-token rows in and h out), not taken from bench.py."""
+behind the roofline fractions, the W8A8 path choice, the percentile, the
+dtype label and the counter records behind `roofline.traffic`. Each expected
+value is written out here from the definitions of the kernels' work (weights
+of the touched experts, their block scales, token rows in and h out), not
+taken from bench.py."""
 import json
 
 import pytest
